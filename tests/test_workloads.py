@@ -1,0 +1,82 @@
+"""The seeded generators: determinism, structure, and the geometry facts the
+pages state (tests/golden/geometry.json)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_243_amd import workloads as W
+from tests.helpers import S
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "geometry.json")
+
+
+def test_geometry_pins():
+    g = json.load(open(GOLDEN))
+    p = g["pages_for_context"]
+    assert -(-p["tokens"] // p["page_size"]) == p["pages"]
+    m = g["page_map_size"]
+    token_map = m["requests"] * m["context"] * m["entry_bytes"]
+    assert int(token_map / 1e6) == m["token_map_mb_rounded"]
+    assert int(token_map / m["page_size"] / 1e6) == m["page_map_mb_rounded"]
+    s = g["slot_formula"]
+    for page, off, slot in s["cases"]:
+        assert W._slots(np.array([page]), np.array([off]), s["page_size"])[0] == slot
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_generation_is_deterministic(cid):
+    a = W.generate(W.SMALL[cid])
+    b = W.generate(W.SMALL[cid])
+    for f in ("key_pool", "value_pool", "k_new", "v_new", "q", "block_table", "slot_mapping", "seq_lens"):
+        assert np.array_equal(S(getattr(a, f)).view(np.uint8), S(getattr(b, f)).view(np.uint8)), f
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_structure(cid):
+    w = W.generate(W.SMALL[cid])
+    cfg = w.cfg
+    ps = cfg.page_size
+    bt, lens, qsl, sm = S(w.block_table), S(w.seq_lens), S(w.query_start_loc), S(w.slot_mapping)
+    assert bt.shape == (cfg.batch, cfg.max_blocks)
+    assert qsl[0] == 0 and qsl[-1] == w.q.shape[0] == sm.shape[0]
+    assert np.all(np.diff(qsl) <= lens)
+    assert len(np.unique(sm)) == sm.shape[0]            # no duplicate slots
+    # new tokens land on the last n_b positions of each sequence
+    for b in range(cfg.batch):
+        n = qsl[b + 1] - qsl[b]
+        pos = np.arange(lens[b] - n, lens[b])
+        assert np.array_equal(sm[qsl[b]:qsl[b + 1]], bt[b, pos // ps] * ps + pos % ps)
+    # used pages are disjoint across sequences except the shared prefix, and
+    # padding entries name the poison page, which holds only NaN bytes
+    n_shared = cfg.shared_prefix_tokens // ps
+    private = np.concatenate([bt[b, n_shared:-(-lens[b] // ps)] for b in range(cfg.batch)])
+    assert len(np.unique(private)) == private.shape[0]
+    for b in range(cfg.batch):
+        assert (bt[b, -(-lens[b] // ps):] == w.poison_page).all()
+    poison = S(w.key_pool)[w.poison_page].view(np.uint8)
+    assert (poison == W.POISON_BYTE[cfg.kv_dtype]).all()
+    # no identity shortcuts: G > 1, K != V, block_table not the identity
+    assert cfg.hq > cfg.hkv
+    assert not torch.equal(w.k_new, w.v_new)
+    assert not np.array_equal(bt[0, :4], np.arange(4))
+
+
+def test_fp8_scales_make_codes_span_the_format():
+    w = W.generate(W.SMALL[5])
+    codes = S(w.k_new)
+    mag = codes & 0x7F
+    assert mag.max() >= 0x70  # near 448 for the per-head amax
+    assert w.k_scale.shape == (w.cfg.hkv,) and (w.k_scale > 0).all()
+    assert not (codes == 0x7F).any() and not (codes == 0xFF).any()
+
+
+def test_config1_session_shape():
+    kp, vp, bt, steps, full, scale = W.config1_session()
+    assert bt.shape == (1, 64) and sorted(S(bt)[0].tolist()) == list(range(64))
+    assert [s.q.shape[0] for s in steps] == [37] + [1] * 8
+    assert [int(s.seq_lens[0]) for s in steps] == [37] + list(range(38, 46))
+    pos = np.arange(45)
+    assert np.array_equal(S(full.slot_mapping), S(bt)[0][pos // 16] * 16 + pos % 16)
