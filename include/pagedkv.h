@@ -1,0 +1,202 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv.so: paged KV write and paged attention on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * The step these calls implement follows the I/O contract of the page "Add
+ * paged / block-table KV cache export (--features paged-cache)"
+ * (onnxruntime/mobius #395, table "ONNX I/O contract" and "How it works"):
+ * new K/V rows are scattered into per-layer page pools through slot_mapping,
+ * then causal attention runs over each sequence's pages, found through its
+ * block_table row and cut to nonpad_kv_seqlen (here: seq_lens).  That page
+ * fixes batch 1 and lists multi-sequence batches as future work; the batch
+ * form here takes the row-padded 2-D block table, seq_lens and
+ * query_start_loc of the vLLM-shaped metadata that the page "[Draft] kv paged
+ * kernels" (ROCm/maxtext #93, gpu_paged commit) accepts.
+ *
+ * Conventions shared by every call:
+ *  - Tensors are described by pkv_tensor: a device pointer to a dense,
+ *    row-major (C-contiguous) buffer, its element type and its shape.  The
+ *    library reads shapes only to validate them; it never copies a tensor.
+ *  - Index tensors (slot_mapping, block_table, seq_lens, query_start_loc) are
+ *    int64, as in the mobius I/O contract.
+ *  - Ownership: the caller owns every buffer, including the workspace.  The
+ *    library allocates no device memory and keeps no state beyond cached
+ *    device properties.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).
+ *  - Ordering: each call enqueues its kernels on `stream` and returns without
+ *    waiting.  A write followed by an attention call on the same stream
+ *    attends over exactly the rows the write stored (maxtext #93, gpu_paged
+ *    commit: prefill and decode read the pages the append wrote).
+ *  - Errors: argument problems the host can see are reported synchronously by
+ *    a negative status before anything is enqueued.  Bad index *values* in
+ *    device memory (slot or page ids out of range, duplicate slots, lengths
+ *    that exceed the block table) are not checked by the fast path; call
+ *    paged_validate_metadata to find them.
+ *  - Supported geometry: page_size 16; head_dim 64 or 128; Hq a multiple of
+ *    Hkv with Hq / Hkv <= 16.  Anything else is PKV_ERR_UNSUPPORTED; there is
+ *    no fallback path.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+typedef enum {
+  PKV_F32 = 0,
+  PKV_BF16 = 1,
+  PKV_FP8_E4M3FN = 2, /* OCP 8-bit E4M3FN codes (bias 7, max 448, 0x7F/0xFF NaN) */
+  PKV_I64 = 3
+} pkv_dtype;
+
+/* status codes */
+enum {
+  PKV_OK = 0,
+  PKV_ERR_NULL = -1,        /* a required pointer is NULL */
+  PKV_ERR_SHAPE = -2,       /* rank or size mismatch between arguments */
+  PKV_ERR_DTYPE = -3,       /* element type not allowed for this argument */
+  PKV_ERR_UNSUPPORTED = -4, /* geometry outside the supported set */
+  PKV_ERR_SCALE = -5,       /* non-finite scale, or fp8 pool without k/v scales */
+  PKV_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required */
+  PKV_ERR_HIP = -7,         /* the HIP runtime reported an error */
+  PKV_ERR_INDEX = -8        /* (validator only) an index value is out of range */
+};
+
+/* A dense row-major tensor in device memory. */
+typedef struct {
+  void* data;       /* device pointer (may be NULL only when the tensor has 0 elements) */
+  int32_t dtype;    /* pkv_dtype */
+  int32_t ndim;     /* 1..4 */
+  int64_t shape[4]; /* shape[0..ndim-1]; row-major, no padding */
+} pkv_tensor;
+
+/* Options of paged_attention. */
+typedef struct {
+  const float* k_scale;   /* [Hkv] fp32 device pointer: per-KV-head dequantisation scale of
+                             the key pool; required iff the pool dtype is PKV_FP8_E4M3FN,
+                             otherwise must be NULL */
+  const float* v_scale;   /* [Hkv] fp32 device pointer, same rule for the value pool */
+  void* workspace;        /* device scratch owned by the caller; may be NULL when
+                             paged_attention_workspace_size returns 0 */
+  size_t workspace_bytes; /* size of `workspace` */
+  int32_t max_query_len;  /* host-side upper bound of query_start_loc[b+1]-query_start_loc[b]
+                             over b (1 for pure decode); sizes the grid without a
+                             device->host copy.  A value below the true maximum is
+                             undefined behaviour; 0 means "T" (always safe). */
+  int32_t split_tokens;   /* decode only: KV positions per split-K partition; a multiple of
+                             the page size, or 0 for the library's choice */
+} pkv_attn_opts;
+
+/*
+ * paged_kv_write -- scatter new K/V rows into the page pools, in place.
+ *
+ * For every t with s = slot_mapping[t] >= 0, copies the Hkv*D elements of
+ * k[t] to key_pool[s / page_size][s % page_size] and of v[t] to
+ * value_pool[s / page_size][s % page_size], byte for byte (the pool keeps its
+ * element type; no conversion, NaN payloads survive).  Negative slots are
+ * skipped.  Everything else in the pools is left untouched.
+ * (mobius #395, PR summary and "ONNX I/O contract": slot = page_id *
+ * page_size + offset; the pools are written by ScatterND.)
+ *
+ *   k, v          [T_new, Hkv, D]                       pool dtype
+ *   slot_mapping  [T_new]                               PKV_I64
+ *   key_pool,     [num_pages, page_size, Hkv, D]        F32, BF16 or FP8_E4M3FN
+ *   value_pool    (same shape and dtype as key_pool)
+ *
+ * Duplicate non-negative slots within one call are a caller error (the
+ * surviving row is unspecified).  Returns PKV_OK or a negative status.
+ */
+int paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+                   pkv_tensor* key_pool, pkv_tensor* value_pool, void* stream);
+
+/*
+ * paged_attention -- causal GQA attention over paged KV.
+ *
+ * Sequence b owns query rows query_start_loc[b] .. query_start_loc[b+1]-1
+ * (n_b rows) and seq_lens[b] = L_b key positions (old context plus its n_b
+ * new tokens, i.e. nonpad_kv_seqlen after the write).  Key position p of b is
+ * row p % page_size of page block_table[b][p / page_size]; entries past
+ * ceil(L_b / page_size) are never read.  Query row i of b sits at position
+ * L_b - n_b + i and attends to positions 0 .. L_b - n_b + i.  Query head hq
+ * reads KV head hq / (Hq / Hkv).  For every row and head:
+ *     out = softmax_p(scale * <q, k_p>) . v_p
+ * with k and v dequantised as code * k_scale[h] / code * v_scale[h] for fp8
+ * pools.  `scale` is applied exactly as given; there is no implicit
+ * 1/sqrt(D) (maxtext #93: the caller passes the scale, 1.0 for a query that
+ * is already scaled).  Rows, tail slots and pages the sequence does not reach
+ * may hold any bytes, NaN included, without affecting the result.
+ * (mobius #395, "How it works" step 3: opset-24 Attention with is_causal=1
+ * and nonpad_kv_seqlen; the batch form is described in the file header.)
+ *
+ *   q, out           [T, Hq, D]             F32 or BF16 (same dtype)
+ *   key_pool,        [num_pages, page_size, Hkv, D]
+ *   value_pool         F32 (requires F32 q), BF16 or FP8_E4M3FN (require BF16 q)
+ *   block_table      [B, max_blocks]        PKV_I64
+ *   seq_lens         [B]                    PKV_I64
+ *   query_start_loc  [B+1]                  PKV_I64, non-decreasing, [0] = 0, [B] = T
+ *   scale            finite float
+ *   opts             see pkv_attn_opts; NULL is allowed when no fp8 scales and no
+ *                    workspace are needed
+ *
+ * Accumulation is fp32; bf16 outputs are rounded to nearest even.  Results
+ * are deterministic (no atomics): repeated calls give identical bits.
+ * Returns PKV_OK or a negative status.
+ */
+int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_tensor* value_pool,
+                    const pkv_tensor* block_table, const pkv_tensor* seq_lens,
+                    const pkv_tensor* query_start_loc, float scale, pkv_tensor* out,
+                    const pkv_attn_opts* opts, void* stream);
+
+/*
+ * paged_attention_workspace_size -- bytes of workspace paged_attention needs
+ * for these shapes and options (0 if none).  Depends only on shapes, dtypes,
+ * opts->max_query_len and opts->split_tokens.  Returns (size_t)-1 if the
+ * arguments are invalid (the same ones paged_attention would reject).
+ */
+size_t paged_attention_workspace_size(const pkv_tensor* q, const pkv_tensor* key_pool,
+                                      const pkv_tensor* block_table, const pkv_attn_opts* opts);
+
+/*
+ * paged_validate_metadata -- debug check of index values in device memory.
+ * Synchronises `stream`, copies the index tensors to the host and checks:
+ * every slot in [-1 .. num_pages*page_size), no duplicate non-negative slot,
+ * query_start_loc non-decreasing from 0 to T, n_b <= L_b, L_b <= max_blocks *
+ * page_size, and every block_table entry a sequence reaches in [0, num_pages).
+ * slot_mapping may be NULL (attention-only check).  Returns PKV_OK,
+ * PKV_ERR_INDEX on the first bad value (and, if `message` is non-NULL, writes
+ * a NUL-terminated description of at most `message_len` bytes), or another
+ * negative status for bad arguments.
+ */
+int paged_validate_metadata(const pkv_tensor* slot_mapping, const pkv_tensor* block_table,
+                            const pkv_tensor* seq_lens, const pkv_tensor* query_start_loc,
+                            int64_t num_pages, int64_t page_size, int64_t num_query_rows,
+                            void* stream, char* message, size_t message_len);
+
+/*
+ * pkv_check_metadata_host -- the checks of paged_validate_metadata on index
+ * arrays already in host memory (all int64, row-major: slots [n_slots] or NULL,
+ * block_table [B, max_blocks], seq_lens [B], query_start_loc [B+1]).  Same
+ * return values and message convention.
+ */
+int pkv_check_metadata_host(const int64_t* slots, int64_t n_slots, const int64_t* block_table,
+                            int64_t B, int64_t max_blocks, const int64_t* seq_lens,
+                            const int64_t* query_start_loc, int64_t num_pages, int64_t page_size,
+                            int64_t num_query_rows, char* message, size_t message_len);
+
+/* Human-readable name of a status code (static string). */
+const char* pkv_status_string(int status);
+
+/* Version of this ABI; bumped on any incompatible change. */
+int pkv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,55 @@
+// kernels.h -- internal launch interface between the C ABI layer and the
+// gfx950 kernels.  Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+enum KvType { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
+
+struct WriteParams {
+  const void* k;
+  const void* v;
+  const int64_t* slots;
+  void* key_pool;
+  void* value_pool;
+  int64_t n_tokens;
+  int64_t row_bytes;  // Hkv * D * element size; a multiple of 16
+};
+
+struct AttnParams {
+  const void* q;        // [T, Hq, D]
+  void* out;            // [T, Hq, D]
+  const void* key_pool;  // [num_pages, 16, Hkv, D]
+  const void* value_pool;
+  const int64_t* block_table;  // [B, max_blocks]
+  const int64_t* seq_lens;     // [B]
+  const int64_t* qsl;          // [B+1]
+  const float* k_scale;        // [Hkv] (fp8 only)
+  const float* v_scale;
+  int64_t T, B, max_blocks, num_pages;
+  int Hq, Hkv, D, G;
+  float scale;
+  int kv_type;         // KvType
+  int max_query_len;   // grid sizing hint (>= true max n_b)
+  // decode split-K
+  int split_tokens;    // positions per partition (multiple of 16)
+  int n_splits;        // partitions per sequence the grid covers
+  float* ws_o;         // [B, n_splits, Hq, D] unnormalised partial outputs
+  float* ws_ml;        // [B, n_splits, Hq, 2] (running max in log2 units, sum)
+  // prefill work list
+  int32_t* ws_plan;    // prefill tile schedule
+};
+
+hipError_t launch_write(const WriteParams& p, hipStream_t stream);
+hipError_t launch_decode(const AttnParams& p, hipStream_t stream);
+hipError_t launch_prefill(const AttnParams& p, hipStream_t stream);
+hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream);
+
+// workspace helpers shared by the ABI layer and the launchers
+size_t decode_workspace_bytes(int64_t B, int Hq, int D, int n_splits);
+size_t prefill_workspace_bytes(const AttnParams& p);
+int prefill_tokens_per_tile(int G);
+
+}  // namespace pkv

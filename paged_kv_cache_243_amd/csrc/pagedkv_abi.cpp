@@ -1,0 +1,362 @@
+// pagedkv_abi.cpp -- the C ABI of libpagedkv.so: argument validation, workspace
+// sizing and dispatch onto the gfx950 kernels.  Declarations and the contract of
+// every entry point are in include/pagedkv.h.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "kernels.h"
+#include "pagedkv.h"
+
+using pkv::AttnParams;
+using pkv::WriteParams;
+
+namespace {
+
+constexpr int kPageSize = 16;
+constexpr int kMaxGroup = 16;
+constexpr int kMaxSplitTokens = 4096;
+
+int64_t numel(const pkv_tensor* t) {
+  int64_t n = 1;
+  for (int i = 0; i < t->ndim; ++i) n *= t->shape[i];
+  return n;
+}
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    case PKV_FP8_E4M3FN: return 1;
+    case PKV_I64: return 8;
+    default: return 0;
+  }
+}
+
+// rank, non-negative sizes, non-NULL data when non-empty, alignment
+int check_tensor(const pkv_tensor* t, int ndim, size_t align) {
+  if (t == nullptr) return PKV_ERR_NULL;
+  if (t->ndim != ndim) return PKV_ERR_SHAPE;
+  for (int i = 0; i < ndim; ++i)
+    if (t->shape[i] < 0) return PKV_ERR_SHAPE;
+  if (elem_bytes(t->dtype) == 0) return PKV_ERR_DTYPE;
+  if (numel(t) > 0) {
+    if (t->data == nullptr) return PKV_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(t->data) % align != 0) return PKV_ERR_UNSUPPORTED;
+  }
+  return PKV_OK;
+}
+
+bool same_shape(const pkv_tensor* a, const pkv_tensor* b) {
+  if (a->ndim != b->ndim) return false;
+  for (int i = 0; i < a->ndim; ++i)
+    if (a->shape[i] != b->shape[i]) return false;
+  return true;
+}
+
+#define PKV_TRY(expr)            \
+  do {                           \
+    int _st = (expr);            \
+    if (_st != PKV_OK) return _st; \
+  } while (0)
+
+// Library choice of the decode partition: aim at ~2048 partitions for the
+// largest lengths the block table allows, clamped to [256, 2048] positions.
+int default_split_tokens(int64_t B, int64_t Hkv, int64_t max_len) {
+  const int64_t target_parts = 2048;
+  const int64_t work = B * Hkv * std::max<int64_t>(max_len / 2, 1);
+  int64_t s = (work + target_parts - 1) / target_parts;
+  s = (s + 63) / 64 * 64;
+  return (int)std::min<int64_t>(std::max<int64_t>(s, 256), 2048);
+}
+
+struct AttnPlan {
+  AttnParams p;
+  enum { kNone, kF32, kDecode, kPrefill } kernel;
+  size_t workspace;
+};
+
+// Validates the attention arguments and fills the launch plan (no HIP calls).
+int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_tensor* value_pool,
+                   const pkv_tensor* block_table, const pkv_tensor* seq_lens,
+                   const pkv_tensor* query_start_loc, float scale, const pkv_tensor* out,
+                   const pkv_attn_opts* opts, bool check_runtime_args, AttnPlan& plan) {
+  PKV_TRY(check_tensor(q, 3, 16));
+  PKV_TRY(check_tensor(key_pool, 4, 16));
+  if (value_pool) PKV_TRY(check_tensor(value_pool, 4, 16));
+  PKV_TRY(check_tensor(block_table, 2, 8));
+  if (check_runtime_args) {
+    PKV_TRY(check_tensor(seq_lens, 1, 8));
+    PKV_TRY(check_tensor(query_start_loc, 1, 8));
+    PKV_TRY(check_tensor(out, 3, 16));
+    if (value_pool == nullptr) return PKV_ERR_NULL;
+  }
+  const int64_t T = q->shape[0], Hq = q->shape[1], D = q->shape[2];
+  const int64_t num_pages = key_pool->shape[0], ps = key_pool->shape[1];
+  const int64_t Hkv = key_pool->shape[2];
+  const int64_t B = block_table->shape[0], max_blocks = block_table->shape[1];
+
+  // element types
+  if (q->dtype != PKV_F32 && q->dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  const int kv = key_pool->dtype;
+  if (kv != PKV_F32 && kv != PKV_BF16 && kv != PKV_FP8_E4M3FN) return PKV_ERR_DTYPE;
+  if (value_pool && value_pool->dtype != kv) return PKV_ERR_DTYPE;
+  if ((q->dtype == PKV_F32) != (kv == PKV_F32)) return PKV_ERR_DTYPE;
+  if (block_table->dtype != PKV_I64) return PKV_ERR_DTYPE;
+  if (check_runtime_args) {
+    if (seq_lens->dtype != PKV_I64 || query_start_loc->dtype != PKV_I64) return PKV_ERR_DTYPE;
+    if (out->dtype != q->dtype) return PKV_ERR_DTYPE;
+  }
+
+  // shapes
+  if (key_pool->shape[3] != D) return PKV_ERR_SHAPE;
+  if (value_pool && !same_shape(key_pool, value_pool)) return PKV_ERR_SHAPE;
+  if (check_runtime_args) {
+    if (!same_shape(q, out)) return PKV_ERR_SHAPE;
+    if (seq_lens->shape[0] != B) return PKV_ERR_SHAPE;
+    if (query_start_loc->shape[0] != B + 1) return PKV_ERR_SHAPE;
+  }
+  if (Hkv <= 0 || Hq <= 0) return PKV_ERR_SHAPE;
+  if (Hq % Hkv != 0) return PKV_ERR_SHAPE;
+
+  // supported geometry
+  const int64_t G = Hq / Hkv;
+  if (ps != kPageSize) return PKV_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  if (G > kMaxGroup) return PKV_ERR_UNSUPPORTED;
+  if (num_pages > INT32_MAX) return PKV_ERR_UNSUPPORTED;
+  if (B > 65535 || Hkv > 65535) return PKV_ERR_UNSUPPORTED;
+
+  // options
+  if (check_runtime_args && !std::isfinite(scale)) return PKV_ERR_SCALE;
+  const bool fp8 = kv == PKV_FP8_E4M3FN;
+  if (check_runtime_args) {
+    const bool has_scales = opts && opts->k_scale && opts->v_scale;
+    const bool any_scale = opts && (opts->k_scale || opts->v_scale);
+    if (fp8 && !has_scales) return PKV_ERR_SCALE;
+    if (!fp8 && any_scale) return PKV_ERR_SCALE;
+  }
+  int64_t max_q = opts ? opts->max_query_len : 0;
+  if (max_q < 0) return PKV_ERR_SHAPE;
+  if (max_q == 0 || max_q > T) max_q = T;
+  int split = opts ? opts->split_tokens : 0;
+  if (split < 0 || split % kPageSize != 0 || split > kMaxSplitTokens) return PKV_ERR_UNSUPPORTED;
+
+  AttnParams& p = plan.p;
+  memset(&p, 0, sizeof p);
+  p.q = q->data;
+  p.out = out ? out->data : nullptr;
+  p.key_pool = key_pool->data;
+  p.value_pool = value_pool ? value_pool->data : nullptr;
+  p.block_table = (const int64_t*)block_table->data;
+  p.seq_lens = seq_lens ? (const int64_t*)seq_lens->data : nullptr;
+  p.qsl = query_start_loc ? (const int64_t*)query_start_loc->data : nullptr;
+  p.k_scale = opts ? opts->k_scale : nullptr;
+  p.v_scale = opts ? opts->v_scale : nullptr;
+  p.T = T;
+  p.B = B;
+  p.max_blocks = max_blocks;
+  p.num_pages = num_pages;
+  p.Hq = (int)Hq;
+  p.Hkv = (int)Hkv;
+  p.D = (int)D;
+  p.G = (int)G;
+  p.scale = scale;
+  p.kv_type = kv == PKV_F32 ? pkv::KV_F32 : (fp8 ? pkv::KV_FP8 : pkv::KV_BF16);
+  p.max_query_len = (int)std::min<int64_t>(max_q, INT32_MAX);
+
+  plan.workspace = 0;
+  if (T == 0 || B == 0) {
+    plan.kernel = AttnPlan::kNone;
+  } else if (kv == PKV_F32) {
+    plan.kernel = AttnPlan::kF32;
+  } else if (max_q == 1) {
+    plan.kernel = AttnPlan::kDecode;
+    const int64_t max_len = max_blocks * kPageSize;
+    if (split == 0) split = default_split_tokens(B, Hkv, max_len);
+    p.split_tokens = split;
+    p.n_splits = (int)std::max<int64_t>(1, (max_len + split - 1) / split);
+    if (p.n_splits > 65535) return PKV_ERR_UNSUPPORTED;
+    plan.workspace = pkv::decode_workspace_bytes(B, (int)Hq, (int)D, p.n_splits);
+  } else {
+    plan.kernel = AttnPlan::kPrefill;
+    plan.workspace = pkv::prefill_workspace_bytes(p);
+  }
+
+  if (check_runtime_args && plan.workspace > 0) {
+    if (!opts || !opts->workspace) return PKV_ERR_WORKSPACE;
+    if (opts->workspace_bytes < plan.workspace) return PKV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(opts->workspace) % 16 != 0) return PKV_ERR_WORKSPACE;
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return 1; }
+
+const char* pkv_status_string(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "required pointer is NULL";
+    case PKV_ERR_SHAPE: return "shape mismatch";
+    case PKV_ERR_DTYPE: return "element type not allowed";
+    case PKV_ERR_UNSUPPORTED: return "unsupported geometry or alignment";
+    case PKV_ERR_SCALE: return "bad scale (non-finite, or fp8 pool without k/v scales)";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_INDEX: return "index value out of range";
+    default: return "unknown status";
+  }
+}
+
+int paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+                   pkv_tensor* key_pool, pkv_tensor* value_pool, void* stream) {
+  PKV_TRY(check_tensor(k, 3, 16));
+  PKV_TRY(check_tensor(v, 3, 16));
+  PKV_TRY(check_tensor(slot_mapping, 1, 8));
+  PKV_TRY(check_tensor(key_pool, 4, 16));
+  PKV_TRY(check_tensor(value_pool, 4, 16));
+  const int kv = key_pool->dtype;
+  if (kv != PKV_F32 && kv != PKV_BF16 && kv != PKV_FP8_E4M3FN) return PKV_ERR_DTYPE;
+  if (value_pool->dtype != kv || k->dtype != kv || v->dtype != kv) return PKV_ERR_DTYPE;
+  if (slot_mapping->dtype != PKV_I64) return PKV_ERR_DTYPE;
+  if (!same_shape(key_pool, value_pool) || !same_shape(k, v)) return PKV_ERR_SHAPE;
+  if (slot_mapping->shape[0] != k->shape[0]) return PKV_ERR_SHAPE;
+  if (k->shape[1] != key_pool->shape[2] || k->shape[2] != key_pool->shape[3]) return PKV_ERR_SHAPE;
+  const int64_t row_bytes = key_pool->shape[2] * key_pool->shape[3] * elem_bytes(kv);
+  if (row_bytes <= 0 || row_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
+  WriteParams p;
+  p.k = k->data;
+  p.v = v->data;
+  p.slots = (const int64_t*)slot_mapping->data;
+  p.key_pool = key_pool->data;
+  p.value_pool = value_pool->data;
+  p.n_tokens = k->shape[0];
+  p.row_bytes = row_bytes;
+  if (p.n_tokens == 0) return PKV_OK;
+  return pkv::launch_write(p, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+size_t paged_attention_workspace_size(const pkv_tensor* q, const pkv_tensor* key_pool,
+                                      const pkv_tensor* block_table, const pkv_attn_opts* opts) {
+  AttnPlan plan;
+  if (plan_attention(q, key_pool, nullptr, block_table, nullptr, nullptr, 1.0f, nullptr, opts,
+                     false, plan) != PKV_OK)
+    return (size_t)-1;
+  return plan.workspace;
+}
+
+int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_tensor* value_pool,
+                    const pkv_tensor* block_table, const pkv_tensor* seq_lens,
+                    const pkv_tensor* query_start_loc, float scale, pkv_tensor* out,
+                    const pkv_attn_opts* opts, void* stream) {
+  AttnPlan plan;
+  PKV_TRY(plan_attention(q, key_pool, value_pool, block_table, seq_lens, query_start_loc, scale,
+                         out, opts, true, plan));
+  AttnParams& p = plan.p;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = hipSuccess;
+  switch (plan.kernel) {
+    case AttnPlan::kNone:
+      return PKV_OK;
+    case AttnPlan::kF32:
+      err = pkv::launch_attention_f32(p, s);
+      break;
+    case AttnPlan::kDecode:
+      if (plan.workspace > 0) {
+        const size_t slots = (size_t)p.B * p.n_splits * p.Hq;
+        p.ws_o = (float*)opts->workspace;
+        p.ws_ml = p.ws_o + slots * p.D;
+      }
+      err = pkv::launch_decode(p, s);
+      break;
+    case AttnPlan::kPrefill:
+      p.ws_plan = plan.workspace > 0 ? (int32_t*)opts->workspace : nullptr;
+      err = pkv::launch_prefill(p, s);
+      break;
+  }
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+// Host-memory form of the metadata check; paged_validate_metadata copies the
+// device tensors and calls it.
+int pkv_check_metadata_host(const int64_t* slots, int64_t n_slots, const int64_t* block_table,
+                            int64_t B, int64_t max_blocks, const int64_t* seq_lens,
+                            const int64_t* qsl, int64_t num_pages, int64_t page_size,
+                            int64_t num_query_rows, char* message, size_t message_len) {
+  auto fail = [&](const char* fmt, long long a, long long b) {
+    if (message && message_len) snprintf(message, message_len, fmt, a, b);
+    return PKV_ERR_INDEX;
+  };
+  if (page_size <= 0 || num_pages < 0) return PKV_ERR_SHAPE;
+  const int64_t capacity = num_pages * page_size;
+  if (slots) {
+    std::vector<int64_t> seen;
+    seen.reserve((size_t)n_slots);
+    for (int64_t t = 0; t < n_slots; ++t) {
+      if (slots[t] < -1 || slots[t] >= capacity)
+        return fail("slot_mapping[%lld] = %lld is out of range", (long long)t, (long long)slots[t]);
+      if (slots[t] >= 0) seen.push_back(slots[t]);
+    }
+    std::sort(seen.begin(), seen.end());
+    for (size_t i = 1; i < seen.size(); ++i)
+      if (seen[i] == seen[i - 1]) return fail("slot %lld appears twice (%lld)", (long long)seen[i], 2);
+  }
+  if (qsl[0] != 0) return fail("query_start_loc[%lld] = %lld, expected 0", 0, (long long)qsl[0]);
+  if (qsl[B] != num_query_rows)
+    return fail("query_start_loc[B] = %lld, expected T = %lld", (long long)qsl[B], (long long)num_query_rows);
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t n = qsl[b + 1] - qsl[b];
+    if (n < 0) return fail("query_start_loc decreases at %lld (%lld)", (long long)b, (long long)n);
+    if (n > seq_lens[b]) return fail("sequence %lld has more query rows than keys (%lld)", (long long)b, (long long)n);
+    if (seq_lens[b] > max_blocks * page_size)
+      return fail("seq_lens[%lld] = %lld exceeds the block table", (long long)b, (long long)seq_lens[b]);
+    const int64_t nblk = (seq_lens[b] + page_size - 1) / page_size;
+    for (int64_t j = 0; j < nblk; ++j) {
+      const int64_t pg = block_table[b * max_blocks + j];
+      if (pg < 0 || pg >= num_pages)
+        return fail("block_table[%lld] names page %lld, out of range", (long long)(b * max_blocks + j), (long long)pg);
+    }
+  }
+  return PKV_OK;
+}
+
+int paged_validate_metadata(const pkv_tensor* slot_mapping, const pkv_tensor* block_table,
+                            const pkv_tensor* seq_lens, const pkv_tensor* query_start_loc,
+                            int64_t num_pages, int64_t page_size, int64_t num_query_rows,
+                            void* stream, char* message, size_t message_len) {
+  if (slot_mapping) PKV_TRY(check_tensor(slot_mapping, 1, 8));
+  PKV_TRY(check_tensor(block_table, 2, 8));
+  PKV_TRY(check_tensor(seq_lens, 1, 8));
+  PKV_TRY(check_tensor(query_start_loc, 1, 8));
+  if ((slot_mapping && slot_mapping->dtype != PKV_I64) || block_table->dtype != PKV_I64 ||
+      seq_lens->dtype != PKV_I64 || query_start_loc->dtype != PKV_I64)
+    return PKV_ERR_DTYPE;
+  const int64_t B = block_table->shape[0];
+  if (seq_lens->shape[0] != B || query_start_loc->shape[0] != B + 1) return PKV_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  auto fetch = [&](const pkv_tensor* t, std::vector<int64_t>& host) -> bool {
+    host.resize((size_t)numel(t));
+    if (host.empty()) return true;
+    return hipMemcpyAsync(host.data(), t->data, host.size() * sizeof(int64_t), hipMemcpyDeviceToHost, s) ==
+           hipSuccess;
+  };
+  std::vector<int64_t> sm, bt, sl, qs;
+  if ((slot_mapping && !fetch(slot_mapping, sm)) || !fetch(block_table, bt) || !fetch(seq_lens, sl) ||
+      !fetch(query_start_loc, qs))
+    return PKV_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return PKV_ERR_HIP;
+  return pkv_check_metadata_host(slot_mapping ? sm.data() : nullptr, (int64_t)sm.size(), bt.data(), B,
+                                 block_table->shape[1], sl.data(), qs.data(), num_pages, page_size,
+                                 num_query_rows, message, message_len);
+}
+
+}  // extern "C"

@@ -1,0 +1,177 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Pools after the write must match bit for bit; attention outputs must be within
+the stated bound of the fp64 oracle (fp32 1e-5, bf16 KV 2e-2, fp8 KV 6e-2).
+Small configurations (several tiles, partitions and ragged tails) are checked
+on every output; the full configurations, in the launch configuration the
+benchmark times, on sampled rows the oracle computes one by one."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_kv_cache_243_amd import workloads as W
+from tests import helpers as H
+from tests.gpu_helpers import (TOL, as_f64, assert_close, gpu_attend, gpu_step, gpu_write, note,
+                               sample_rows)
+from tests.helpers import S
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _bytes(t):
+    return S(t).view(np.uint8)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_write_bitwise_small(gpu, cid):
+    note(f"write small config {cid}")
+    w = W.generate(W.SMALL[cid], DEV)
+    kp, vp = gpu_write(gpu, w)
+    torch.cuda.synchronize()
+    okp, ovp = H.oracle_write(w)
+    assert np.array_equal(_bytes(kp), okp.view(np.uint8))
+    assert np.array_equal(_bytes(vp), ovp.view(np.uint8))
+
+
+@pytest.mark.parametrize("cid", [2, 3, 5])
+def test_write_bitwise_full(gpu, cid):
+    note(f"write full config {cid}")
+    w = W.generate(cid, DEV)
+    kp, vp = gpu_write(gpu, w)
+    torch.cuda.synchronize()
+    okp, ovp = H.oracle_write(w)
+    assert np.array_equal(_bytes(kp), okp.view(np.uint8))
+    assert np.array_equal(_bytes(vp), ovp.view(np.uint8))
+
+
+def test_write_preserves_nan_payloads_and_skips_negative_slots(gpu):
+    note("write NaN payloads / negative slots")
+    w = W.generate(W.SMALL[2], DEV)
+    k = w.k_new.clone()
+    kb = k.view(torch.int16)
+    kb[0, 0, :4] = torch.tensor([0x7FC1, -127, 0x7F80, 0x0001], dtype=torch.int16, device=DEV)
+    sm = w.slot_mapping.clone()
+    sm[1::2] = -1
+    w2 = dataclasses.replace(w, k_new=k, slot_mapping=sm)
+    kp, vp = gpu_write(gpu, w2)
+    torch.cuda.synchronize()
+    okp, ovp = H.oracle_write(w2)
+    assert np.array_equal(_bytes(kp), okp.view(np.uint8))
+    assert np.array_equal(_bytes(vp), ovp.view(np.uint8))
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_attention_small_all_rows(gpu, cid):
+    note(f"attention small config {cid}")
+    w = W.generate(W.SMALL[cid], DEV)
+    kp, vp, out = gpu_step(gpu, w)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, w.kv_dtype, f"small config {cid}")
+
+
+def test_config1_session_fp32(gpu):
+    """Config 1: 37-token fp32 prefill then 8 decode steps, each against the
+    oracle at 1e-5; the incremental rows also equal one 45-token prefill."""
+    note("config 1 fp32 session")
+    kp0, vp0, bt, steps, full, scale = W.config1_session(DEV)
+    kp, vp = kp0.clone(), vp0.clone()
+    okp, ovp = S(kp0).copy(), S(vp0).copy()
+    rows = []
+    for i, st in enumerate(steps):
+        gpu.paged_kv_write(st.k_new, st.v_new, st.slot_mapping, kp, vp)
+        out = torch.empty_like(st.q)
+        gpu.paged_attention(st.q, kp, vp, bt, st.seq_lens, st.query_start_loc, scale, out,
+                            max_query_len=st.max_query_len)
+        torch.cuda.synchronize()
+        oracle.paged_kv_write(S(st.k_new), S(st.v_new), S(st.slot_mapping), okp, ovp)
+        ref = oracle.paged_attention(S(st.q), "f32", okp, ovp, "f32", S(bt), S(st.seq_lens),
+                                     S(st.query_start_loc), scale)
+        assert np.array_equal(_bytes(kp), okp.view(np.uint8))
+        assert_close(out, ref, "f32", f"config 1 step {i}")
+        rows.append(as_f64(out))
+    inc = np.concatenate(rows)
+    kp2, vp2 = kp0.clone(), vp0.clone()
+    gpu.paged_kv_write(full.k_new, full.v_new, full.slot_mapping, kp2, vp2)
+    out_full = torch.empty_like(full.q)
+    gpu.paged_attention(full.q, kp2, vp2, bt, full.seq_lens, full.query_start_loc, scale, out_full,
+                        max_query_len=full.max_query_len)
+    torch.cuda.synchronize()
+    assert np.max(np.abs(inc - as_f64(out_full))) <= TOL["f32"]
+
+
+FULL_SAMPLES = {2: 1, 3: 12, 4: 1, 5: 1}
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_attention_full_size_sampled(gpu, cid):
+    """Full configuration in the benchmark's launch configuration; the oracle
+    computes the sampled rows (every row for the decode configurations except
+    config 4, where 64 of 256 sequences are checked)."""
+    note(f"attention full config {cid}")
+    w = W.generate(cid, DEV)
+    kp, vp, out = gpu_step(gpu, w)
+    rows = sample_rows(w, FULL_SAMPLES[cid], seed=cid)
+    if cid == 4:
+        rows = rows[np.random.default_rng(4).choice(rows.shape[0], 64, replace=False)]
+    okp, ovp = H.oracle_write(w)
+    ref = H.oracle_attend(w, okp, ovp, sel_tokens=rows)
+    got = as_f64(out)[rows]
+    assert_close(got, ref, w.kv_dtype, f"full config {cid} ({rows.shape[0]} rows)")
+
+
+@pytest.mark.parametrize("g,d,kv", [(1, 128, "bf16"), (16, 64, "bf16"), (3, 64, "fp8_e4m3fn"),
+                                    (8, 128, "fp8_e4m3fn"), (2, 64, "f32")])
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_other_geometries(gpu, g, d, kv, mode):
+    note(f"geometry G={g} D={d} {kv} {mode}")
+    base = W.SMALL[2] if mode == "decode" else W.SMALL[3]
+    q_dtype = "f32" if kv == "f32" else "bf16"
+    cfg = dataclasses.replace(base, hq=2 * g, hkv=2, head_dim=d, kv_dtype=kv, q_dtype=q_dtype,
+                              split_tokens=128 if mode == "decode" else 0)
+    w = W.generate(cfg, DEV, seed=7)
+    kp, vp, out = gpu_step(gpu, w)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, kv, f"G={g} D={d} {kv} {mode}")
+
+
+def test_ragged_prefill_with_empty_and_single_row_sequences(gpu):
+    """A mixed batch through the prefill kernel: sequences with 0, 1 and many
+    query rows, empty and long old contexts."""
+    note("ragged prefill")
+    cfg = dataclasses.replace(W.SMALL[3], batch=6, n_new=70, old_min=0, old_max=200)
+    w = W.generate(cfg, DEV, seed=21)
+    # keep the first n = [0, 1, 70, 17, 70, 2] new tokens of each sequence: they
+    # sit at positions old_b .. old_b + n_b - 1, so L_b becomes old_b + n_b
+    n = np.array([0, 1, 70, 17, 70, 2])
+    qsl = np.concatenate([[0], np.cumsum(n)])
+    keep = np.concatenate([np.arange(70 * b, 70 * b + n[b]) for b in range(6)])
+    keep_t = torch.as_tensor(keep, device=DEV)
+    w2 = dataclasses.replace(w, q=w.q[keep_t].contiguous(), k_new=w.k_new[keep_t].contiguous(),
+                             v_new=w.v_new[keep_t].contiguous(), slot_mapping=w.slot_mapping[keep_t].contiguous(),
+                             query_start_loc=torch.as_tensor(qsl, device=DEV),
+                             seq_lens=w.seq_lens - 70 + torch.as_tensor(n, device=DEV),
+                             max_query_len=70)
+    w2.meta = dict(w.meta, n_new=n)
+    kp, vp, out = gpu_step(gpu, w2)
+    _, _, ref = H.oracle_step(w2)
+    assert_close(out, ref, "bf16", "ragged prefill")
+
+
+def test_decode_batch_with_sequences_without_query_rows(gpu):
+    note("decode with empty query spans")
+    w = W.generate(W.SMALL[2], DEV)
+    keep = torch.as_tensor([0, 2, 3, 5], device=DEV)
+    n = np.array([1, 0, 1, 1, 0, 1])
+    qsl = np.concatenate([[0], np.cumsum(n)])
+    w2 = dataclasses.replace(w, q=w.q[keep].contiguous(), k_new=w.k_new[keep].contiguous(),
+                             v_new=w.v_new[keep].contiguous(), slot_mapping=w.slot_mapping[keep].contiguous(),
+                             query_start_loc=torch.as_tensor(qsl, device=DEV),
+                             seq_lens=w.seq_lens - 1 + torch.as_tensor(n, device=DEV))
+    w2.meta = dict(w.meta, n_new=n)
+    kp, vp, out = gpu_step(gpu, w2, split_tokens=64)
+    _, _, ref = H.oracle_step(w2)
+    assert_close(out, ref, "bf16", "decode with empty spans")
