@@ -1,0 +1,359 @@
+"""Benchmark of the paged KV write + paged attention step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu-baseline]
+
+One step = the whole hot path over one batch of the decode workload
+(64 sequences, Hq 32, Hkv 8, head_dim 128, page_size 16, bf16 KV, context
+lengths U{512..4096}, 65536-page pools): the slot-mapping write of the 64 new
+tokens, then paged decode attention (split-K partitions + log-sum-exp merge)
+over every sequence's pages.  Inputs are resident in HBM before timing starts.
+Each timed step is preceded, outside its timed region, by a 1 GiB device fill
+that evicts L2 and the 256 MB Infinity Cache, so KV reads come from HBM.  Every
+step is timed with a pair of HIP events on the stream the kernels run on.
+
+The printed JSON line carries:
+  value        decode KV-read GB/s of the step: algorithmic bytes / step time,
+  roofline     the decode attention call against the 8 TB/s HBM peak,
+  prefill, ... the other workloads (chunked prefill TFLOP/s against the bf16
+               MFMA peak, shared-prefix decode, fp8 long-context decode),
+  cpu_baseline the CPU oracle on the same decode workload.
+Algorithmic bytes count each sequence's K and V rows once per KV head, plus q,
+out and the block_table entries read; flops count causally visible (query,
+key) pairs, 4 * D per pair per head.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # dense: 256 CU x 4096 flop/clk x 2.4 GHz
+METRIC = "decode KV-read GB/s (% of HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
+PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(os.path.join(ROOT, "paged_kv_cache_243_amd", "csrc"))):
+        with open(os.path.join(ROOT, "paged_kv_cache_243_amd", "csrc", name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def decode_bytes(w) -> int:
+    """K+V rows once per (sequence, KV head), q, out, block_table entries read."""
+    cfg = w.cfg
+    esz = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[cfg.kv_dtype]
+    qsz = 4 if cfg.q_dtype == "f32" else 2
+    lens = w.seq_lens.cpu().numpy().astype(int)
+    kv = int(lens.sum()) * cfg.hkv * cfg.head_dim * esz * 2
+    T = w.q.shape[0]
+    qo = 2 * T * cfg.hq * cfg.head_dim * qsz
+    table = int(sum(-(-l // cfg.page_size) for l in lens)) * 8
+    scales = 2 * cfg.hkv * 4 if cfg.kv_dtype == "fp8_e4m3fn" else 0
+    return int(kv + qo + table + scales)
+
+
+def unique_decode_bytes(w) -> int:
+    """Distinct pages touched (shared pages once) x page bytes for K and V."""
+    cfg = w.cfg
+    esz = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[cfg.kv_dtype]
+    bt = w.block_table.cpu().numpy()
+    lens = w.seq_lens.cpu().numpy().astype(int)
+    pages = set()
+    for b in range(bt.shape[0]):
+        pages.update(bt[b, :-(-lens[b] // cfg.page_size)].tolist())
+    return int(len(pages) * cfg.page_size * cfg.hkv * cfg.head_dim * esz * 2)
+
+
+def prefill_flops(w) -> int:
+    """4 * D * Hq per causally visible (query, key) pair: QK^T and PV."""
+    cfg = w.cfg
+    lens = w.seq_lens.cpu().numpy().astype(int)
+    qsl = w.query_start_loc.cpu().numpy().astype(int)
+    pairs = 0
+    for b in range(len(lens)):
+        n = qsl[b + 1] - qsl[b]
+        P = lens[b] - n
+        pairs += n * P + n * (n + 1) // 2
+    return int(4 * cfg.head_dim * cfg.hq * pairs)
+
+
+def write_bytes(w) -> int:
+    esz = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[w.cfg.kv_dtype]
+    T = w.k_new.shape[0]
+    return int(2 * 2 * T * w.cfg.hkv * w.cfg.head_dim * esz + 8 * T)
+
+
+class Runner:
+    """Write + attention of one workload with preallocated buffers."""
+
+    def __init__(self, pkv, w, torch):
+        self.pkv, self.w, self.torch = pkv, w, torch
+        self.kp, self.vp = w.key_pool, w.value_pool  # written in place each step (same rows)
+        self.out = torch.empty_like(w.q)
+        need = pkv.paged_attention_workspace_size(w.q, w.key_pool, w.block_table,
+                                                  max_query_len=w.max_query_len,
+                                                  split_tokens=w.split_tokens)
+        self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.q.device)
+
+    def write(self):
+        w = self.w
+        self.pkv.paged_kv_write(w.k_new, w.v_new, w.slot_mapping, self.kp, self.vp)
+
+    def attend(self):
+        w = self.w
+        self.pkv.paged_attention(w.q, self.kp, self.vp, w.block_table, w.seq_lens, w.query_start_loc,
+                                 w.scale, self.out, k_scale=w.k_scale, v_scale=w.v_scale,
+                                 max_query_len=w.max_query_len, split_tokens=w.split_tokens,
+                                 workspace=self.ws)
+
+
+def time_steps(runner, torch, steps, warmup, flush, progress=""):
+    """Per-step HIP event times (ms) of write and attention; flush outside."""
+    for _ in range(warmup):
+        runner.write()
+        runner.attend()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        ev[i][0].record()
+        runner.write()
+        ev[i][1].record()
+        runner.attend()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    write_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    attn_ms = [b.elapsed_time(c) for _, b, c in ev]
+    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+    if progress:
+        log(f"{progress}: {steps} steps, median step {statistics.median(step_ms):.4f} ms")
+    return write_ms, attn_ms, step_ms, wall
+
+
+def traffic_from_profile(kernel: str):
+    """Counter-derived HBM bytes per launch from the committed rocprofv3 PMC
+    summary, or None when the kernels changed since the counters were taken."""
+    try:
+        with open(PROFILE_TRAFFIC) as f:
+            prof = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if prof.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    entry = prof.get("kernels", {}).get(kernel)
+    return None if entry is None else entry.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(w):
+    """The oracle as it stands (fp64, OpenMP) on the whole decode step of the
+    same workload: write of the 64 new tokens + attention of all 64 rows."""
+    import numpy as np
+    import oracle
+    from paged_kv_cache_243_amd import workloads as W
+    S = W.to_numpy_storage
+    threads = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
+    kp, vp = S(w.key_pool).copy(), S(w.value_pool).copy()
+    k, v, sm = S(w.k_new), S(w.v_new), S(w.slot_mapping)
+    q, bt, sl, qsl = S(w.q), S(w.block_table), S(w.seq_lens), S(w.query_start_loc)
+    times = []
+    for rep in range(3):
+        t0 = time.perf_counter()
+        oracle.paged_kv_write(k, v, sm, kp, vp)
+        oracle.paged_attention(q, w.q_dtype, kp, vp, w.kv_dtype, bt, sl, qsl, w.scale, threads=threads)
+        times.append(time.perf_counter() - t0)
+        if times[-1] > 10:
+            break
+    t = statistics.median(times)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(decode_bytes(w) / t / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "ms_per_step": round(t * 1e3, 1), "cpu": cpu,
+            "sample": f"the full decode step of the timed workload ({w.cfg.batch} sequences: write of "
+                      f"{w.k_new.shape[0]} tokens + attention of every row), fp64, median of {len(times)} runs"}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-extra", action="store_true", help="time only the decode workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
+    ap.add_argument("--profile-workload", choices=["decode", "prefill", "shared", "fp8"],
+                    help="time one workload only and print its median times (for profiler runs)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_cache_243_amd as pkv
+    from paged_kv_cache_243_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pkv.load()
+    dev = torch.device("cuda:0")
+    flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    if args.profile_workload:
+        cid = {"decode": 2, "prefill": 3, "shared": 4, "fp8": 5}[args.profile_workload]
+        w = W.generate(cid, dev)
+        wr, at, st, _ = time_steps(Runner(pkv, w, torch), torch, args.steps, args.warmup, flush,
+                                   args.profile_workload)
+        print(json.dumps({"workload": w.cfg.name, "write_ms_median": statistics.median(wr),
+                          "attention_ms_median": statistics.median(at),
+                          "step_ms_median": statistics.median(st)}), flush=True)
+        return 0
+
+    # ---- headline: decode workload, write + attention per step
+    log("generating decode workload (config 2)")
+    w2 = W.generate(2, dev)
+    r2 = Runner(pkv, w2, torch)
+    wr, at, st, wall = time_steps(r2, torch, args.steps, args.warmup, flush, "decode bf16")
+    bytes2 = decode_bytes(w2)
+    step_ms = statistics.median(st)
+    attn_ms = statistics.median(at)
+    achieved = bytes2 / (attn_ms * 1e-3) / 1e9
+    _, warm_at, _, _ = time_steps(r2, torch, max(5, args.steps // 3), 2, None)
+    result = {
+        "metric": METRIC,
+        "value": round(bytes2 / (step_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "paged decode, bf16 KV: write 1 new token per sequence, then split-K decode "
+                        "attention over each sequence's pages",
+            "batch": w2.cfg.batch, "q_heads": w2.cfg.hq, "kv_heads": w2.cfg.hkv,
+            "head_dim": w2.cfg.head_dim, "page_size": w2.cfg.page_size, "num_pages": w2.cfg.num_pages,
+            "context_lengths": "U{512..4096}", "kv_dtype": "bf16", "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode attention call (decode_split_kernel + merge_kernel)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic_from_profile("decode_split_kernel<2,128>"),
+            "algorithmic_bytes_per_launch": bytes2,
+            "launch_ms_median": round(attn_ms, 5),
+            "launch_ms_min": round(min(at), 5),
+            "launch_ms_warm_median": round(statistics.median(warm_at), 5),
+        },
+        "write_ms_median": round(statistics.median(wr), 5),
+        "timed_loop_wall_s": round(wall, 4),
+    }
+    del r2
+
+    if not args.no_extra:
+        extra = {}
+        # chunked prefill
+        log("generating prefill workload (config 3)")
+        w3 = W.generate(3, dev)
+        r3 = Runner(pkv, w3, torch)
+        wr3, at3, st3, _ = time_steps(r3, torch, max(5, args.steps // 2), args.warmup, flush, "prefill bf16")
+        fl = prefill_flops(w3)
+        a3 = statistics.median(at3)
+        extra["prefill"] = {
+            "workload": "chunked causal prefill, bf16: 8 sequences x 512 new tokens on U{0..8192} old "
+                        "context, Hq 32, Hkv 8, head_dim 128",
+            "bound": "mfma", "unit": "TFLOP/s",
+            "achieved": round(fl / (a3 * 1e-3) / 1e12, 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "frac": round(fl / (a3 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "flop_per_launch": fl,
+            "attention_ms_median": round(a3, 5),
+            "write_ms_median": round(statistics.median(wr3), 5),
+            "write_GBps": round(write_bytes(w3) / (statistics.median(wr3) * 1e-3) / 1e9, 1),
+            "step_ms_median": round(statistics.median(st3), 5),
+        }
+        del r3, w3
+        torch.cuda.empty_cache()
+        # shared-prefix decode
+        log("generating shared-prefix decode workload (config 4)")
+        w4 = W.generate(4, dev)
+        r4 = Runner(pkv, w4, torch)
+        _, at4, st4, _ = time_steps(r4, torch, args.steps, args.warmup, flush, "shared-prefix decode")
+        a4 = statistics.median(at4)
+        extra["shared_prefix_decode"] = {
+            "workload": "256 sequences sharing 128 prefix pages + U{0..512} private tokens, Hq 64, Hkv 8",
+            "unit": "GB/s",
+            "logical_GBps": round(decode_bytes(w4) / (a4 * 1e-3) / 1e9, 1),
+            "unique_GBps": round(unique_decode_bytes(w4) / (a4 * 1e-3) / 1e9, 1),
+            "attention_ms_median": round(a4, 5),
+            "step_ms_median": round(statistics.median(st4), 5),
+        }
+        del r4, w4
+        torch.cuda.empty_cache()
+        # long-context fp8 decode
+        log("generating long-context fp8 decode workload (config 5)")
+        w5 = W.generate(5, dev)
+        r5 = Runner(pkv, w5, torch)
+        _, at5, st5, _ = time_steps(r5, torch, args.steps, args.warmup, flush, "fp8 long decode")
+        a5 = statistics.median(at5)
+        b5 = decode_bytes(w5)
+        extra["fp8_long_decode"] = {
+            "workload": "16 sequences, U{32768..131072} positions, fp8 E4M3FN KV with per-head scales, "
+                        "Hq 64, Hkv 8, split-K over 2048-position partitions",
+            "bound": "hbm", "unit": "GB/s",
+            "achieved": round(b5 / (a5 * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "frac": round(b5 / (a5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": b5,
+            "attention_ms_median": round(a5, 5),
+            "step_ms_median": round(statistics.median(st5), 5),
+        }
+        del r5, w5
+        torch.cuda.empty_cache()
+        result.update(extra)
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the decode workload")
+        result["cpu_baseline"] = cpu_baseline(w2)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -34,8 +34,8 @@
  *    that exceed the block table) are not checked by the fast path; call
  *    paged_validate_metadata to find them.
  *  - Supported geometry: page_size 16; head_dim 64 or 128; Hq a multiple of
- *    Hkv with Hq / Hkv <= 16.  Anything else is PKV_ERR_UNSUPPORTED; there is
- *    no fallback path.
+ *    Hkv with Hq / Hkv <= 16; at most 8192 sequences per decode call.
+ *    Anything else is PKV_ERR_UNSUPPORTED; there is no fallback path.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -89,8 +89,13 @@ typedef struct {
                              over b (1 for pure decode); sizes the grid without a
                              device->host copy.  A value below the true maximum is
                              undefined behaviour; 0 means "T" (always safe). */
-  int32_t split_tokens;   /* decode only: KV positions per split-K partition; a multiple of
-                             the page size, or 0 for the library's choice */
+  int32_t split_tokens;   /* decode only: approximate KV positions per split-K partition (a
+                             multiple of the page size, at most 4096).  The decode work is
+                             cut into equal contiguous ranges of (sequence, 32-position)
+                             units, one per workgroup; split_tokens sets how many ranges
+                             (about B * max_blocks * page_size / 2 / split_tokens, rounded
+                             to a multiple of the CU count).  0 = one range per CU.  The
+                             result does not depend on it beyond rounding. */
 } pkv_attn_opts;
 
 /*

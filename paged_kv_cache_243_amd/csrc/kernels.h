@@ -33,11 +33,12 @@ struct AttnParams {
   float scale;
   int kv_type;         // KvType
   int max_query_len;   // grid sizing hint (>= true max n_b)
-  // decode split-K
-  int split_tokens;    // positions per partition (multiple of 16)
-  int n_splits;        // partitions per sequence the grid covers
-  float* ws_o;         // [B, n_splits, Hq, D] unnormalised partial outputs
-  float* ws_ml;        // [B, n_splits, Hq, 2] (running max in log2 units, sum)
+  // decode: stream-K over (sequence, 32-position block) units
+  int split_tokens;    // requested positions per partition (0 = library choice)
+  int grid_parts;      // workgroups of the decode grid = partition ranges
+  int32_t* ws_cum;     // [B + 1] units before each sequence (written by workgroup 0)
+  float* ws_ml;        // [B + grid_parts, Hq, 2] partial (max in log2 units, sum)
+  float* ws_o;         // [B + grid_parts, Hq, D] unnormalised partial outputs
   // prefill work list
   int32_t* ws_plan;    // prefill tile schedule
 };
@@ -48,7 +49,11 @@ hipError_t launch_prefill(const AttnParams& p, hipStream_t stream);
 hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream);
 
 // workspace helpers shared by the ABI layer and the launchers
-size_t decode_workspace_bytes(int64_t B, int Hq, int D, int n_splits);
+size_t decode_workspace_bytes(int64_t B, int Hq, int D);
+int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu);
+void decode_workspace_carve(AttnParams& p, void* workspace);
+constexpr int kDecodeMaxParts = 2048;
+constexpr int kDecodeMaxSeqs = 8192;
 size_t prefill_workspace_bytes(const AttnParams& p);
 int prefill_tokens_per_tile(int G);
 

@@ -65,14 +65,17 @@ bool same_shape(const pkv_tensor* a, const pkv_tensor* b) {
     if (_st != PKV_OK) return _st; \
   } while (0)
 
-// Library choice of the decode partition: aim at ~2048 partitions for the
-// largest lengths the block table allows, clamped to [256, 2048] positions.
-int default_split_tokens(int64_t B, int64_t Hkv, int64_t max_len) {
-  const int64_t target_parts = 2048;
-  const int64_t work = B * Hkv * std::max<int64_t>(max_len / 2, 1);
-  int64_t s = (work + target_parts - 1) / target_parts;
-  s = (s + 63) / 64 * 64;
-  return (int)std::min<int64_t>(std::max<int64_t>(s, 256), 2048);
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 struct AttnPlan {
@@ -177,12 +180,9 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
     plan.kernel = AttnPlan::kF32;
   } else if (max_q == 1) {
     plan.kernel = AttnPlan::kDecode;
-    const int64_t max_len = max_blocks * kPageSize;
-    if (split == 0) split = default_split_tokens(B, Hkv, max_len);
+    if (B > pkv::kDecodeMaxSeqs) return PKV_ERR_UNSUPPORTED;
     p.split_tokens = split;
-    p.n_splits = (int)std::max<int64_t>(1, (max_len + split - 1) / split);
-    if (p.n_splits > 65535) return PKV_ERR_UNSUPPORTED;
-    plan.workspace = pkv::decode_workspace_bytes(B, (int)Hq, (int)D, p.n_splits);
+    plan.workspace = pkv::decode_workspace_bytes(B, (int)Hq, (int)D);
   } else {
     plan.kernel = AttnPlan::kPrefill;
     plan.workspace = pkv::prefill_workspace_bytes(p);
@@ -271,11 +271,8 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
       err = pkv::launch_attention_f32(p, s);
       break;
     case AttnPlan::kDecode:
-      if (plan.workspace > 0) {
-        const size_t slots = (size_t)p.B * p.n_splits * p.Hq;
-        p.ws_o = (float*)opts->workspace;
-        p.ws_ml = p.ws_o + slots * p.D;
-      }
+      pkv::decode_workspace_carve(p, opts->workspace);
+      p.grid_parts = pkv::decode_grid_parts(p.B, p.max_blocks * kPageSize, p.split_tokens, device_cu_count());
       err = pkv::launch_decode(p, s);
       break;
     case AttnPlan::kPrefill:

@@ -58,7 +58,7 @@ def call_write(a):
 
 
 @pytest.mark.parametrize("case,status", [
-    ("null k", B.STATUS and -1),
+    ("null k", -1),
     ("k rank", -2),
     ("slot count", -2),
     ("k/v shape", -2),
@@ -158,6 +158,9 @@ ATTN_CASES = {
     "scales on a bf16 pool": (dict(opts=opts(max_query_len=1, k_scale=FAKE, v_scale=FAKE)), -5),
     "negative max_query_len": (dict(opts=opts(max_query_len=-1)), -2),
     "missing workspace": (dict(bt=T([4, 256], B.PKV_I64), opts=opts(max_query_len=1, split_tokens=256)), -6),
+    "too many decode sequences": (dict(q=T([9000, 32, 128], B.PKV_BF16), out=T([9000, 32, 128], B.PKV_BF16),
+                                       bt=T([9000, 8], B.PKV_I64), sl=T([9000], B.PKV_I64),
+                                       qsl=T([9001], B.PKV_I64)), -4),
     "small workspace": (dict(bt=T([4, 256], B.PKV_I64),
                              opts=opts(max_query_len=1, split_tokens=256, workspace=FAKE, workspace_bytes=64)), -6),
 }
@@ -181,11 +184,15 @@ def test_workspace_size():
     bt = T([64, 256], B.PKV_I64)
     ws = lambda o: lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt),
                                                       ctypes.byref(o))
-    # decode with 4096-position table and 512-position partitions: 8 partitions
-    n = ws(opts(max_query_len=1, split_tokens=512))
-    assert n == 64 * 8 * 32 * (128 + 2) * 4
-    # one partition covers everything: no workspace
-    assert ws(opts(max_query_len=1, split_tokens=4096)) == 0
+    # decode: per-sequence unit offsets, then (B + 2048) partial slots of
+    # Hq x (2 + D) floats, whatever the partition size
+    align = lambda n: (n + 255) // 256 * 256
+    slots = (64 + 2048) * 32
+    want = align(65 * 4) + align(slots * 2 * 4) + slots * 128 * 4
+    assert ws(opts(max_query_len=1, split_tokens=512)) == want
+    assert ws(opts(max_query_len=1, split_tokens=0)) == want
+    # prefill needs none
+    assert ws(opts(max_query_len=7)) == 0
     # invalid arguments
     assert ws(opts(max_query_len=1, split_tokens=20)) == ctypes.c_size_t(-1).value
 
