@@ -39,6 +39,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # dense: 256 CU x 4096 flop/clk x 2.4 GHz
 METRIC = "decode KV-read GB/s (% of HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
+CALIB_BYTES = 256 << 20
 
 
 def log(msg: str) -> None:
@@ -231,6 +232,11 @@ def main(argv=None) -> int:
     if args.profile_workload:
         cid = {"decode": 2, "prefill": 3, "shared": 4, "fp8": 5}[args.profile_workload]
         w = W.generate(cid, dev)
+        # calibration for hardware byte counters: a plain device copy of known
+        # size (256 MiB read + 256 MiB written), launched once
+        calib = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+        torch.empty_like(calib).copy_(calib)
+        del calib
         wr, at, st, _ = time_steps(Runner(pkv, w, torch), torch, args.steps, args.warmup, flush,
                                    args.profile_workload)
         print(json.dumps({"workload": w.cfg.name, "write_ms_median": statistics.median(wr),

@@ -34,7 +34,7 @@
  *    that exceed the block table) are not checked by the fast path; call
  *    paged_validate_metadata to find them.
  *  - Supported geometry: page_size 16; head_dim 64 or 128; Hq a multiple of
- *    Hkv with Hq / Hkv <= 16; at most 8192 sequences per decode call.
+ *    Hkv with Hq / Hkv <= 16; at most 4096 sequences per decode call.
  *    Anything else is PKV_ERR_UNSUPPORTED; there is no fallback path.
  */
 #ifndef PAGEDKV_H

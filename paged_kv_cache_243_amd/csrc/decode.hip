@@ -19,22 +19,26 @@
 //    head k (or heads k, k + 8, ...): the waves of a workgroup read the same
 //    pages together, so HBM sees whole 2 KiB rows.  Every K/V byte of (b, h) is
 //    read from HBM once and serves all G query heads.
-//  * Page ids come from block_table through a 64-entry window held one per
-//    lane and broadcast with v_readlane; the next unit's loads are issued
-//    before the current unit is computed (register double buffering).
+//  * Page ids come from block_table through wave-uniform scalar loads, two
+//    units ahead.  K and V are read with buffer loads (page base in a scalar
+//    descriptor, 32-bit lane offsets), non-temporal, in whole-row runs: each
+//    load instruction covers complete 2*D-byte (bf16) rows of the head, the
+//    access shape HBM streams fastest.  Each unit is then staged into per-wave
+//    LDS tiles (chunk-swizzled against bank conflicts; fp8 widened to bf16 on
+//    the way) and the next unit's loads are issued at once into the freed
+//    registers, so every load has a whole unit of compute to land.
 //  * Scores use v_mfma_f32_16x16x32_bf16 as S^T = K . Q^T: A = 16 keys (one
-//    page) x 32 dims read straight from the pool into registers, B = the G query
-//    heads (zero-padded to 16 columns).  Lane l then holds 4 keys of one head,
-//    so the softmax max needs two cross-lane steps and the sum none until the end.
-//  * P.V uses the same MFMA as O^T = V^T . P^T.  Lane (r, g) loads an 8-key x
-//    D/16-dim block of V (coalesced full rows per 16 lanes) and transposes it in
-//    registers with v_perm_b32, so no LDS round trip is needed.
+//    page) x 32 dims from the K tile, B = the G query heads (zero-padded to 16
+//    columns).  Lane l then holds 4 keys of one head, so the softmax max needs
+//    two cross-lane steps and the sum none until the end.
+//  * P.V uses the same MFMA as O^T = V^T . P^T; the V^T operand comes straight
+//    out of the V tile with ds_read_b64_tr_b16 (gfx950's transposing LDS read).
 //  * fp8 E4M3FN codes are widened to bf16 (exact) with v_cvt_scalef32_pk_bf16_fp8;
 //    the per-head k scale is folded into the logit scale and the v scale into
 //    the output.
 //  * Masking selects -inf for positions >= seq_lens (never multiplies by zero),
-//    and V rows of masked positions are zeroed before the MFMA, so stale or NaN
-//    bytes in unused slots cannot reach the output.
+//    and V rows of masked positions are stored as zeros in the tile, so stale
+//    or NaN bytes in unused slots cannot reach the output.
 //  * A segment (the part of one sequence inside a workgroup's range) that is a
 //    whole sequence writes its normalised output directly; otherwise it writes
 //    its unnormalised O with (m, l) to a partial slot and merge_kernel combines
@@ -68,13 +72,29 @@ __device__ __forceinline__ int32_t seq_units(const AttnParams& p, int b) {
   return (int32_t)((p.seq_lens[b] + kUnit - 1) / kUnit);
 }
 
-// Raw K and V bytes of one unit for one KV head, as one lane holds them.
+// K of a unit is read in whole-row runs (each load instruction covers RPI
+// complete rows of the head's D*ESZ bytes), then transposed into the MFMA
+// layout through a per-wave LDS tile of 32 bf16 rows.
+template <int ESZ, int D>
+struct KGeom {
+  static constexpr int LPR = D * ESZ / 16;  // lanes per K row (16 bytes each)
+  static constexpr int RPI = 64 / LPR;      // rows per load instruction
+  static constexpr int NKI = kUnit / RPI;   // load instructions per unit
+  static constexpr int IPP = NKI / 2;       // ... per page
+  static constexpr int NC = D / 8;          // 16-byte bf16 chunks per LDS row
+  // chunk swizzles.  K: the 16 rows an MFMA operand read touches land in 16
+  // different bank groups.  V: the 4 rows x 2 chunks a transposing read
+  // touches land in 8 different bank groups.
+  __device__ static int swz(int row) { return (row / (16 / NC)) % NC; }
+  __device__ static int swz_v(int row) { return (2 * ((row / (16 / NC)) % 4)) % NC; }
+};
+
+// Raw K and V bytes of one unit for one KV head, as one lane holds them
+// (both read in whole-row runs).
 template <int ESZ, int D>
 struct UnitRegs {
-  static constexpr int KDW = 2 * ESZ;                 // dwords per K chunk of 8 elements
-  static constexpr int VDW = (D / 16) * ESZ / 4;      // dwords per V row chunk
-  uint32_t k[2][D / 32][KDW];
-  uint32_t v[8][VDW];
+  u32x4 k[KGeom<ESZ, D>::NKI];
+  u32x4 v[KGeom<ESZ, D>::NKI];
 };
 
 // Buffer resource for one page: wave-uniform base (forced into scalar
@@ -87,10 +107,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const char* base, ui
                                            (int)bytes, kBufferWord3);
 }
 
-// Per-lane address parts of a unit (32-bit offsets from a page base).
+// Per-lane address parts of a unit (32-bit offsets from a page base): load i
+// of a page reads row (i*RPI + lane/LPR), bytes [16*(lane%LPR), +16).
 struct LaneOffsets {
-  uint32_t k;     // K row (lane & 15), dims [8*grp, +8) of each 32-dim chunk
-  uint32_t v[4];  // V rows 4*grp + e (e < 4), dims [col*NJ, +NJ)
+  uint32_t k[8];
 };
 
 // Loads of one unit: page bases live in buffer descriptors (scalar
@@ -98,20 +118,28 @@ struct LaneOffsets {
 template <int ESZ, int D>
 __device__ __forceinline__ void issue_k(UnitRegs<ESZ, D>& u, __amdgpu_buffer_rsrc_t kp0, __amdgpu_buffer_rsrc_t kp1,
                                         const LaneOffsets& off) {
-  constexpr int NKK = D / 32;
-  using U = UnitRegs<ESZ, D>;
+  using G = KGeom<ESZ, D>;
 #pragma unroll
-  for (int pp = 0; pp < 2; ++pp) {
+  for (int i = 0; i < G::NKI; ++i)
+    u.k[i] = __builtin_amdgcn_raw_buffer_load_b128(i < G::IPP ? kp0 : kp1, (int)off.k[i % G::IPP], 0, kStreamAux);
+}
+
+// Raw K of the unit -> the wave's LDS tile (bf16, 32 rows x D, swizzled chunks).
+template <int ESZ, int D>
+__device__ __forceinline__ void stage_k(const UnitRegs<ESZ, D>& u, __bf16* __restrict__ tile, int lane) {
+  using G = KGeom<ESZ, D>;
+  const int cs = lane % G::LPR;
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int o = (int)off.k + 32 * kk * ESZ;
-      if constexpr (U::KDW == 4) {
-        const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(pp ? kp1 : kp0, o, 0, kStreamAux);
-        u.k[pp][kk][0] = x.x; u.k[pp][kk][1] = x.y; u.k[pp][kk][2] = x.z; u.k[pp][kk][3] = x.w;
-      } else {
-        const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(pp ? kp1 : kp0, o, 0, kStreamAux);
-        u.k[pp][kk][0] = x.x; u.k[pp][kk][1] = x.y;
-      }
+  for (int i = 0; i < G::NKI; ++i) {
+    const int row = (i / G::IPP) * 16 + (i % G::IPP) * G::RPI + lane / G::LPR;
+    __bf16* r = tile + row * D;
+    if constexpr (ESZ == 2) {
+      *(u32x4*)(r + 8 * (cs ^ G::swz(row))) = u.k[i];
+    } else {
+      const u32x2 c0 = fp8x4_to_bf16x4(u.k[i].x), c1 = fp8x4_to_bf16x4(u.k[i].y);
+      const u32x2 c2 = fp8x4_to_bf16x4(u.k[i].z), c3 = fp8x4_to_bf16x4(u.k[i].w);
+      *(u32x4*)(r + 8 * ((2 * cs) ^ G::swz(row))) = u32x4{c0.x, c0.y, c1.x, c1.y};
+      *(u32x4*)(r + 8 * ((2 * cs + 1) ^ G::swz(row))) = u32x4{c2.x, c2.y, c3.x, c3.y};
     }
   }
 }
@@ -119,21 +147,10 @@ __device__ __forceinline__ void issue_k(UnitRegs<ESZ, D>& u, __amdgpu_buffer_rsr
 template <int ESZ, int D>
 __device__ __forceinline__ void issue_v(UnitRegs<ESZ, D>& u, __amdgpu_buffer_rsrc_t vp0, __amdgpu_buffer_rsrc_t vp1,
                                         const LaneOffsets& off) {
-  using U = UnitRegs<ESZ, D>;
+  using G = KGeom<ESZ, D>;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __amdgpu_buffer_rsrc_t r = e < 4 ? vp0 : vp1;
-    const int o = (int)off.v[e & 3];
-    if constexpr (U::VDW == 4) {
-      const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, kStreamAux);
-      u.v[e][0] = x.x; u.v[e][1] = x.y; u.v[e][2] = x.z; u.v[e][3] = x.w;
-    } else if constexpr (U::VDW == 2) {
-      const u32x2 x = __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, kStreamAux);
-      u.v[e][0] = x.x; u.v[e][1] = x.y;
-    } else {
-      u.v[e][0] = __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, kStreamAux);
-    }
-  }
+  for (int i = 0; i < G::NKI; ++i)
+    u.v[i] = __builtin_amdgcn_raw_buffer_load_b128(i < G::IPP ? vp0 : vp1, (int)off.k[i % G::IPP], 0, kStreamAux);
 }
 
 // Page ids of unit j of a sequence (its logical pages 2j and 2j+1), read with
@@ -148,37 +165,84 @@ __device__ __forceinline__ UnitPages unit_pages(const __attribute__((address_spa
   return UnitPages{bt_row[a], bt_row[b]};
 }
 
-// K chunk (page pp, MFMA kk) as a bf16 operand.
+// Raw V of the unit -> the wave's V tile (bf16, 32 rows x D, swizzled
+// chunks).  Rows at positions >= len are stored as zeros: a masked key has
+// P = 0, and 0 * NaN would poison the MFMA sum.
 template <int ESZ, int D>
-__device__ __forceinline__ bf16x8 k_operand(const UnitRegs<ESZ, D>& u, int pp, int kk) {
-  if constexpr (ESZ == 2) {
-    const u32x4 w = {u.k[pp][kk][0], u.k[pp][kk][1], u.k[pp][kk][2], u.k[pp][kk][3]};
-    return __builtin_bit_cast(bf16x8, w);
-  } else {
-    const u32x2 a = fp8x4_to_bf16x4(u.k[pp][kk][0]), b = fp8x4_to_bf16x4(u.k[pp][kk][1]);
-    const u32x4 w = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(bf16x8, w);
+__device__ __forceinline__ void stage_v(const UnitRegs<ESZ, D>& u, __bf16* __restrict__ tile, int lane, int64_t pos0,
+                                        int64_t len) {
+  using G = KGeom<ESZ, D>;
+  const int cs = lane % G::LPR;
+#pragma unroll
+  for (int i = 0; i < G::NKI; ++i) {
+    const int row = (i / G::IPP) * 16 + (i % G::IPP) * G::RPI + lane / G::LPR;
+    const bool live = pos0 + row < len;
+    __bf16* r = tile + row * D;
+    if constexpr (ESZ == 2) {
+      *(u32x4*)(r + 8 * (cs ^ G::swz_v(row))) = live ? u.v[i] : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const u32x2 c0 = fp8x4_to_bf16x4(u.v[i].x), c1 = fp8x4_to_bf16x4(u.v[i].y);
+      const u32x2 c2 = fp8x4_to_bf16x4(u.v[i].z), c3 = fp8x4_to_bf16x4(u.v[i].w);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      *(u32x4*)(r + 8 * ((2 * cs) ^ G::swz_v(row))) = live ? u32x4{c0.x, c0.y, c1.x, c1.y} : z;
+      *(u32x4*)(r + 8 * ((2 * cs + 1) ^ G::swz_v(row))) = live ? u32x4{c2.x, c2.y, c3.x, c3.y} : z;
+    }
   }
+}
+
+__device__ __forceinline__ s16x4 lds_read_tr16(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<__bf16*>(p)));
+}
+
+// V^T operand of output MFMA t: dims [16t, 16t+16) as rows, the lane group's
+// 8 keys (4*grp + e of page 0, then of page 1) as the reduction index, read
+// with two transposing LDS reads of 4 keys each.
+template <int ESZ, int D>
+__device__ __forceinline__ bf16x8 v_operand(const __bf16* __restrict__ tile, int t, int lane) {
+  using G = KGeom<ESZ, D>;
+  const int grp = lane >> 4, li = lane & 15;
+  const int dim = 16 * t + 4 * (li & 3);  // this lane's 4-element run
+  const int c = dim / 8, within = dim % 8;
+  const int k0 = 4 * grp + (li >> 2), k1 = k0 + 16;
+  const s16x4 lo = lds_read_tr16(tile + k0 * D + 8 * (c ^ G::swz_v(k0)) + within);
+  const s16x4 hi = lds_read_tr16(tile + k1 * D + 8 * (c ^ G::swz_v(k1)) + within);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// K operand of score MFMA kk on page pp: row 16*pp + (lane & 15), dims
+// [32*kk + 8*grp, +8), read from the wave's LDS tile.
+template <int ESZ, int D>
+__device__ __forceinline__ bf16x8 k_operand(const __bf16* __restrict__ tile, int pp, int kk, int col, int grp) {
+  using G = KGeom<ESZ, D>;
+  const int row = 16 * pp + col;
+  return *(const bf16x8*)(tile + row * D + 8 * ((4 * kk + grp) ^ G::swz(row)));
 }
 
 // One unit of the online softmax for one KV head: scores for 32 keys, running
 // max/sum update, P.V accumulation.  pos0 = position of the unit's first key;
 // keys at positions >= len are masked.
-// next_k() runs once the K registers have been consumed (it issues the next
-// unit's K loads into them); next_v() runs once the V registers have been
-// consumed.
-template <int ESZ, int D, class NextK, class NextV>
-__device__ __forceinline__ void consume_unit(UnitRegs<ESZ, D>& u, const bf16x8 (&qb)[D / 32], f32x4 (&acc)[D / 16],
-                                             float& m_run, float& l_run, float logit_scale, int64_t pos0,
-                                             int64_t len, int grp, NextK next_k, NextV next_v) {
+// One unit of the online softmax for one KV head: stage the unit's K and V
+// into the wave's LDS tiles, call next() (which issues the following unit's
+// loads into the now free registers), then scores for 32 keys, the running
+// max/sum update and the P.V accumulation.  pos0 = position of the unit's first
+// key; keys at positions >= len are masked.
+template <int ESZ, int D, class Next>
+__device__ __forceinline__ void consume_unit(UnitRegs<ESZ, D>& u, __bf16* __restrict__ ktile, __bf16* __restrict__ vtile,
+                                             const bf16x8 (&qb)[D / 32], f32x4 (&acc)[D / 16], float& m_run,
+                                             float& l_run, float logit_scale, int64_t pos0, int64_t len, int lane,
+                                             Next next) {
   constexpr int NKK = D / 32, NJ = D / 16;
+  const int col = lane & 15, grp = lane >> 4;
+  stage_k<ESZ, D>(u, ktile, lane);
+  stage_v<ESZ, D>(u, vtile, lane, pos0, len);
+  next();
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
-    s0 = mfma16(k_operand<ESZ, D>(u, 0, kk), qb[kk], s0);
-    s1 = mfma16(k_operand<ESZ, D>(u, 1, kk), qb[kk], s1);
+    s0 = mfma16(k_operand<ESZ, D>(ktile, 0, kk, col, grp), qb[kk], s0);
+    s1 = mfma16(k_operand<ESZ, D>(ktile, 1, kk, col, grp), qb[kk], s1);
   }
-  next_k();
   // lane holds keys pos0 + 4*grp + i (s0) and pos0 + 16 + 4*grp + i (s1)
   float x[8];
 #pragma unroll
@@ -191,8 +255,6 @@ __device__ __forceinline__ void consume_unit(UnitRegs<ESZ, D>& u, const bf16x8 (
     for (int e = 0; e < 8; ++e) {
       const bool valid = pos0 + (e < 4 ? 0 : 16) + 4 * grp + (e & 3) < len;
       x[e] = valid ? x[e] : -INFINITY;
-#pragma unroll
-      for (int i = 0; i < UnitRegs<ESZ, D>::VDW; ++i) u.v[e][i] = valid ? u.v[e][i] : 0u;
     }
   }
   float mx = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
@@ -215,38 +277,24 @@ __device__ __forceinline__ void consume_unit(UnitRegs<ESZ, D>& u, const bf16x8 (
 #pragma unroll
   for (int q = 0; q < 4; ++q) pw[q] = pack_bf16x2(pr[2 * q], pr[2 * q + 1]);
   const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
-
-  // P.V: operand j holds dim r*NJ + j of the lane's 8 keys; built right before
-  // its MFMA so the raw rows die progressively
-  if constexpr (ESZ == 2) {
+  // P.V: acc[t][i] = O^T[dim 16t + 4*grp + i][head col]
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      u32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = __builtin_amdgcn_perm(u.v[2 * q + 1][j >> 1], u.v[2 * q][j >> 1], sel);
-      acc[j] = mfma16(__builtin_bit_cast(bf16x8, o), pb, acc[j]);
-    }
-  } else {
-#pragma unroll
-    for (int wd = 0; wd < NJ / 4; ++wd) {
-      u32x4 o[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t x = u.v[2 * q][wd], y = u.v[2 * q + 1][wd];
-        const u32x2 ab = fp8x4_to_bf16x4(__builtin_amdgcn_perm(y, x, 0x05010400u));  // keys 2q, 2q+1 dims 0, 1
-        const u32x2 cd = fp8x4_to_bf16x4(__builtin_amdgcn_perm(y, x, 0x07030602u));  // dims 2, 3
-        o[0][q] = ab.x;
-        o[1][q] = ab.y;
-        o[2][q] = cd.x;
-        o[3][q] = cd.y;
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) acc[4 * wd + t] = mfma16(__builtin_bit_cast(bf16x8, o[t]), pb, acc[4 * wd + t]);
-    }
-  }
-  next_v();
+  for (int t = 0; t < NJ; ++t) acc[t] = mfma16(v_operand<ESZ, D>(vtile, t, lane), pb, acc[t]);
 }
+
+// Cut of U units into W contiguous ranges: the first r = U mod W workgroups
+// take q + 1 = floor(U / W) + 1 units, the others q.  start() is
+// division-free; owner(u) is the workgroup whose range holds unit u.
+struct Partition {
+  int32_t q, r;
+  __device__ Partition(int64_t U, int64_t W) : q((int32_t)(U / W)), r((int32_t)(U % W)) {}
+  __device__ int32_t start(int32_t w) const { return w * q + min(w, r); }
+  __device__ int32_t owner(int32_t u) const {
+    const int32_t big = r * (q + 1);  // units held by the q+1-unit ranges
+    return u < big ? u / (q + 1) : r + (u - big) / q;
+  }
+  __device__ bool empty(int32_t w) const { return q == 0 && w >= r; }
+};
 
 // Stream-K decode.  The flattened list of (sequence, unit) pairs is cut into
 // gridDim.x equal contiguous ranges, one per workgroup; a workgroup walks the
@@ -261,6 +309,8 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   constexpr int NJ = D / 16;
   __shared__ int32_t s_cum[kDecodeMaxSeqs + 1];
   __shared__ int32_t s_scan[512];
+  __shared__ __bf16 s_ktile[kMaxWaves][kUnit * D];
+  __shared__ __bf16 s_vtile[kMaxWaves][kUnit * D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nthreads = blockDim.x;
   const int col = lane & 15, grp = lane >> 4;
@@ -298,8 +348,10 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   if (wg == 0)
     for (int b = tid; b <= B; b += nthreads) p.ws_cum[b] = s_cum[b];
   const int64_t U = s_cum[B];
-  const int32_t u0 = (int32_t)(((int64_t)wg * U) / W);
-  const int32_t u1 = (int32_t)(((int64_t)(wg + 1) * U) / W);
+  if (U == 0) return;
+  const Partition part(U, W);
+  const int32_t u0 = part.start(wg);
+  const int32_t u1 = part.start(wg + 1);
   if (u0 >= u1) return;
 
   // sequence holding unit u0: the largest b with s_cum[b] <= u0
@@ -314,9 +366,14 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   const uint32_t row_stride = (uint32_t)p.Hkv * D * ESZ;
   const int64_t page_stride = (int64_t)row_stride * kPageSize;
   LaneOffsets off;
-  off.k = (uint32_t)col * row_stride + 8 * grp * ESZ;
+  {
+    using G = KGeom<ESZ, D>;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) off.v[e] = (uint32_t)(4 * grp + e) * row_stride + col * NJ * ESZ;
+    for (int i = 0; i < 8; ++i)
+      off.k[i] = (uint32_t)((i % G::IPP) * G::RPI + lane / G::LPR) * row_stride + 16 * (lane % G::LPR);
+  }
+  __bf16* const ktile = s_ktile[wave];
+  __bf16* const vtile = s_vtile[wave];
 
   for (int b = __builtin_amdgcn_readfirstlane(lo); b < B; ++b) {
     const int32_t cb = s_cum[b], ce = s_cum[b + 1];
@@ -359,10 +416,9 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       float m_run = -INFINITY, l_run = 0.f;
 
-      // One unit of registers: unit j+1's K loads are issued into them as soon
-      // as unit j's scores are computed, its V loads as soon as unit j's P.V is
-      // done, so each load has a whole unit of compute to land.  Page ids are
-      // fetched one unit further ahead.
+      // One unit of registers: as soon as unit j is staged into LDS, unit j+1's
+      // loads are issued into them, so each load has a whole unit of compute to
+      // land.  Page ids are fetched one unit further ahead.
       UnitRegs<ESZ, D> u;
       const UnitPages first = unit_pages(bt_row, j0, last_page);
       UnitPages nxt = unit_pages(bt_row, j0 + 1, last_page);
@@ -371,13 +427,14 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       // the loop issues unconditionally (straight-line load order, so each wait
       // covers exactly the loads it needs); the last unit is peeled
       for (int j = j0; j < j1 - 1; ++j) {
-        consume_unit<ESZ, D>(
-            u, qb, acc, m_run, l_run, logit_scale, (int64_t)j * kUnit, L, grp,
-            [&] { issue_k<ESZ, D>(u, krsrc(nxt.p0), krsrc(nxt.p1), off); },
-            [&] { issue_v<ESZ, D>(u, vrsrc(nxt.p0), vrsrc(nxt.p1), off); });
+        consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, (int64_t)j * kUnit, L, lane, [&] {
+          issue_k<ESZ, D>(u, krsrc(nxt.p0), krsrc(nxt.p1), off);
+          issue_v<ESZ, D>(u, vrsrc(nxt.p0), vrsrc(nxt.p1), off);
+        });
         nxt = unit_pages(bt_row, j + 2, last_page);
       }
-      consume_unit<ESZ, D>(u, qb, acc, m_run, l_run, logit_scale, (int64_t)(j1 - 1) * kUnit, L, grp, [] {}, [] {});
+      consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, (int64_t)(j1 - 1) * kUnit, L, lane,
+                           [] {});
 
       // the four lane groups hold partial sums of the same head (same max)
       l_run += xor_shuffle(l_run, 16);
@@ -386,29 +443,19 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       if constexpr (ESZ == 1) out_scale = p.v_scale[h];
       if (col < p.G) {
         const int hq = h * p.G + col;
-        // acc[j][i] = O^T[dim (4*grp + i)*NJ + j][head col]
+        // acc[t][i] = O^T[dim 16t + 4*grp + i][head col]
         if (whole) {
           const float inv = out_scale / l_run;
           __bf16* orow = (__bf16*)p.out + (q_row * p.Hq + hq) * D;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            uint32_t w[NJ / 2];
-#pragma unroll
-            for (int j = 0; j < NJ / 2; ++j) w[j] = pack_bf16x2(acc[2 * j][i] * inv, acc[2 * j + 1][i] * inv);
-            __bf16* dst = orow + (4 * grp + i) * NJ;
-            if constexpr (NJ == 8) *(u32x4*)dst = u32x4{w[0], w[1], w[2], w[3]};
-            else *(u32x2*)dst = u32x2{w[0], w[1]};
-          }
+          for (int t = 0; t < NJ; ++t)
+            *(u32x2*)(orow + 16 * t + 4 * grp) =
+                u32x2{pack_bf16x2(acc[t][0] * inv, acc[t][1] * inv), pack_bf16x2(acc[t][2] * inv, acc[t][3] * inv)};
         } else {
           const int64_t slot = ((int64_t)b + wg) * p.Hq + hq;
           float* orow = p.ws_o + slot * D;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < NJ; j += 4)
-              *(f32x4*)(orow + (4 * grp + i) * NJ + j) =
-                  f32x4{acc[j][i] * out_scale, acc[j + 1][i] * out_scale, acc[j + 2][i] * out_scale,
-                        acc[j + 3][i] * out_scale};
+          for (int t = 0; t < NJ; ++t) *(f32x4*)(orow + 16 * t + 4 * grp) = acc[t] * out_scale;
           if (grp == 0) {
             p.ws_ml[2 * slot] = m_run;
             p.ws_ml[2 * slot + 1] = l_run;
@@ -419,45 +466,61 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   }
 }
 
-// Partition range start of workgroup w and the workgroup owning unit u, for
-// U units cut into W ranges (start(w) = floor(w * U / W)).
-__device__ __forceinline__ int64_t range_start(int64_t w, int64_t U, int64_t W) { return (w * U) / W; }
-__device__ __forceinline__ int64_t range_owner(int64_t u, int64_t U, int64_t W) { return ((u + 1) * W - 1) / U; }
-
-// One wave per (query head, sequence): log-sum-exp merge of the partials of a
-// sequence whose units span several workgroups:
+// Log-sum-exp merge of the partials of a sequence whose units span several
+// workgroups:
 //   M = max_w m_w,  out = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w.
+// One wave per (query head, sequence).  Partials are taken in chunks of 16
+// workgroups: every (m, l) and O load of a chunk is issued before any of them
+// is used, so a chunk costs one memory round trip.
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
+  constexpr int PER = D / 64;
+  constexpr int CHUNK = 8;
   const int hq = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
   const int64_t q_row = p.qsl[b];
   if (p.qsl[b + 1] == q_row) return;
-  const int64_t cb = p.ws_cum[b], ce = p.ws_cum[b + 1], U = p.ws_cum[p.B];
-  const int64_t W = p.grid_parts;
+  const int32_t cb = p.ws_cum[b], ce = p.ws_cum[b + 1];
   if (ce <= cb) return;
-  const int64_t wa = range_owner(cb, U, W), wz = range_owner(ce - 1, U, W);
+  const Partition part(p.ws_cum[p.B], p.grid_parts);
+  const int32_t wa = part.owner(cb), wz = part.owner(ce - 1);
   if (wa == wz) return;  // written directly by decode_kernel
-  float M = -INFINITY;
-  for (int64_t w0 = wa; w0 <= wz; w0 += 64) {
-    const int64_t w = w0 + lane;
-    if (w <= wz && range_start(w, U, W) < range_start(w + 1, U, W))
-      M = fmaxf(M, p.ws_ml[2 * ((b + w) * p.Hq + hq)]);
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, __shfl_xor(M, m, 64));
-  constexpr int PER = D / 64;
+  const f32x2* ml = (const f32x2*)p.ws_ml;
+  float M = -INFINITY, l = 0.f;
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  float l = 0.f;
-  for (int64_t w = wa; w <= wz; ++w) {
-    if (range_start(w, U, W) >= range_start(w + 1, U, W)) continue;  // empty range wrote nothing
-    const int64_t slot = (b + w) * p.Hq + hq;
-    const float f = __builtin_amdgcn_exp2f(p.ws_ml[2 * slot] - M);
-    l += f * p.ws_ml[2 * slot + 1];
+  for (int32_t w0 = wa; w0 <= wz; w0 += CHUNK) {
+    f32x2 mlw[CHUNK];
+    float ow[CHUNK][PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] += f * p.ws_o[slot * D + lane + 64 * i];
+    for (int c = 0; c < CHUNK; ++c) {
+      const int32_t w = min(w0 + c, wz);
+      const int64_t slot = ((int64_t)b + w) * p.Hq + hq;
+      mlw[c] = ml[slot];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ow[c][i] = p.ws_o[slot * D + lane + 64 * i];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int c = 0; c < CHUNK; ++c) {
+      // slots past wz repeat wz, and empty ranges wrote nothing: weight 0
+      const bool live = w0 + c <= wz && !part.empty(w0 + c);
+      mlw[c][0] = live ? mlw[c][0] : -INFINITY;
+      Mc = fmaxf(Mc, mlw[c][0]);
+    }
+    const float alpha = __builtin_amdgcn_exp2f(M - Mc);  // rescale what earlier chunks summed
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] *= alpha;
+#pragma unroll
+    for (int c = 0; c < CHUNK; ++c) {
+      const float f = __builtin_amdgcn_exp2f(mlw[c][0] - Mc);
+      l += f * mlw[c][1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] += f * ow[c][i];
+    }
+    M = Mc;
   }
   const float inv = 1.0f / l;
 #pragma unroll

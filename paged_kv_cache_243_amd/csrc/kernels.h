@@ -53,7 +53,7 @@ size_t decode_workspace_bytes(int64_t B, int Hq, int D);
 int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu);
 void decode_workspace_carve(AttnParams& p, void* workspace);
 constexpr int kDecodeMaxParts = 2048;
-constexpr int kDecodeMaxSeqs = 8192;
+constexpr int kDecodeMaxSeqs = 4096;
 size_t prefill_workspace_bytes(const AttnParams& p);
 int prefill_tokens_per_tile(int G);
 
