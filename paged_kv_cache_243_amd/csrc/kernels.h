@@ -56,5 +56,6 @@ constexpr int kDecodeMaxParts = 2048;
 constexpr int kDecodeMaxSeqs = 4096;
 size_t prefill_workspace_bytes(const AttnParams& p);
 int prefill_tokens_per_tile(int G);
+int64_t prefill_max_items(int64_t T, int64_t B, int G);
 
 }  // namespace pkv

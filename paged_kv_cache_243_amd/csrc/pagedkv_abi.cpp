@@ -185,6 +185,11 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
     plan.workspace = pkv::decode_workspace_bytes(B, (int)Hq, (int)D);
   } else {
     plan.kernel = AttnPlan::kPrefill;
+    // the prefill kernels index positions with 32-bit integers and its work
+    // list packs (sequence, query tile) into 16 + 16 bits
+    const int64_t tpt = pkv::prefill_tokens_per_tile((int)G);
+    if (max_blocks * kPageSize > INT32_MAX) return PKV_ERR_UNSUPPORTED;
+    if ((T + tpt - 1) / tpt > 65535) return PKV_ERR_UNSUPPORTED;
     plan.workspace = pkv::prefill_workspace_bytes(p);
   }
 

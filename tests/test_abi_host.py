@@ -191,8 +191,9 @@ def test_workspace_size():
     want = align(65 * 4) + align(slots * 2 * 4) + slots * 128 * 4
     assert ws(opts(max_query_len=1, split_tokens=512)) == want
     assert ws(opts(max_query_len=1, split_tokens=0)) == want
-    # prefill needs none
-    assert ws(opts(max_query_len=7)) == 0
+    # prefill: the tile work list, one count plus at most ceil(T / tile) + B
+    # items of 4 bytes (tile = 256 / G query tokens, G = 4 here)
+    assert ws(opts(max_query_len=7)) == (1 + 64 + (64 + 63) // 64) * 4
     # invalid arguments
     assert ws(opts(max_query_len=1, split_tokens=20)) == ctypes.c_size_t(-1).value
 
