@@ -33,8 +33,10 @@ def sources():
 
 # Per-source extra flags.  The prefill kernel never produces a NaN score
 # (rows past seq_lens are zero-filled, masked scores are -inf), so its float
-# max/min need no NaN quieting.
-EXTRA = {"prefill.hip": ["-fno-honor-nans"]}
+# max/min need no NaN quieting; its MFMAs keep results in VGPRs (the softmax
+# reads every score, and AGPR results would each need a v_accvgpr_read, which
+# contends with the MFMAs for the AGPR file).
+EXTRA = {"prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -32,11 +32,12 @@
 //  * Software pipeline: the scores of tile t+1 are computed in the same
 //    iteration as the softmax and PV of tile t, so MFMA and VALU work of
 //    different tiles can overlap within a wave.
-//  * Online softmax in the exp2 domain with a lazy reference max: the
-//    accumulator is rescaled only when a row's max grows by more than 2^8 over
-//    the reference, so the common step is one FMA and one exp2 per score.  The
-//    scale's sign is moved into q (an exact sign flip), so the running max can
-//    be taken over raw scores.
+//  * Online softmax in the exp2 domain with a lazy reference max: P is taken
+//    against a reference that moves (and the accumulator is rescaled) only
+//    when some P of a tile could exceed 2^8, which the tile's own row sums
+//    reveal, so the common step is one FMA, one exp2 and half a dot2 per score
+//    and no max.  The scale's sign is moved into q (an exact sign flip), so
+//    maxima can be taken over raw scores.
 //  * Masking selects -inf for keys after the row's position, only on tiles
 //    that cross the diagonal.  The fp8 k scale joins the logit scale, the v
 //    scale the output normalisation.
@@ -49,10 +50,15 @@
 
 namespace pkv {
 
-constexpr int kPrefillRows = 256;      // query rows per workgroup (4 waves x 64)
+constexpr int kPrefillRows = 256;      // query rows per workgroup
+#ifndef PKV_PREFILL_ROW_BLOCKS
+#define PKV_PREFILL_ROW_BLOCKS 1
+#endif
+constexpr int kPrefillRowBlocks = PKV_PREFILL_ROW_BLOCKS;  // 32-row blocks per wave (8 / NB waves)
 constexpr int kKeyTile = 32;           // key positions per LDS tile (2 pages)
 constexpr int kPlanSortMax = 2048;     // items the plan kernel orders by length
-constexpr float kLazyRescale = 8.0f;   // log2 growth of a row max tolerated before rescaling
+constexpr int kValuPerMfma = 4;        // softmax VALU instructions placed after each MFMA
+constexpr float kLazyBound = 256.0f;   // largest P (= exp2 of 8) a tile may hold before the reference moves
 constexpr int kRawBufferWord3 = 0x00020000;
 
 int prefill_tokens_per_tile(int G) { return kPrefillRows / G; }
@@ -160,28 +166,41 @@ struct TileSrc {
 // bf16: one 32-row tile (K or V) straight into LDS.  One load moves 1 KiB per
 // wave (lane l -> LDS bytes 16 l after the wave's base), i.e. 1024 / (2 D)
 // whole rows of one page, so the swizzle is applied by choosing which global
-// chunk each lane fetches.  Tiles before position 0 or past seq_lens read as
-// zeros and touch no memory.
-template <int D>
+// chunk each lane fetches.  The D / 16 loads of a tile are spread over the
+// waves (waves past the last load fetch nothing).  Tiles before position 0 or
+// past seq_lens read as zeros and touch no memory.
+template <int D, int WAVES>
 struct Dma {
-  static constexpr int ROWS = 1024 / (2 * D);        // rows per load: 4 (D = 128) or 8 (D = 64)
-  static constexpr int LOADS = kKeyTile / ROWS / 4;  // loads per wave and tile
+  static constexpr int ROWS = 1024 / (2 * D);                 // rows per load: 4 (D = 128) or 8 (D = 64)
+  static constexpr int TOTAL = kKeyTile / ROWS;               // loads per tile
+  static constexpr int LOADS = TOTAL >= WAVES ? TOTAL / WAVES : 1;  // loads per active wave
+  static constexpr int ACTIVE = TOTAL / LOADS;                // waves that load
+  static constexpr int WROWS = LOADS * ROWS;                  // rows per active wave (within one page)
+  static_assert(TOTAL % LOADS == 0 && kPageSize % WROWS == 0, "a wave's rows share a page");
 };
 
-template <int D, bool IS_V>
-__device__ __forceinline__ void dma_tile(const TileSrc& c, __bf16* tile, int t, int wave, int lane) {
+// Page holding this wave's rows of tile t; tiles outside the sequence map to a
+// page it owns, whose rows the descriptor range then excludes.
+template <int D, int WAVES>
+__device__ __forceinline__ int64_t wave_page(const TileSrc& c, int t, int wave) {
+  const int lp = (t * kKeyTile + wave * Dma<D, WAVES>::WROWS) >> 4;
+  const int lpc = lp < 0 ? 0 : (lp < c.last_page ? lp : c.last_page);
+  return c.bt[lpc];
+}
+
+template <int D, int WAVES, bool IS_V>
+__device__ __forceinline__ void dma_tile(const TileSrc& c, __bf16* tile, int t, int64_t page, int wave, int lane) {
   using TL = TileLayout<D>;
-  using M = Dma<D>;
+  using M = Dma<D, WAVES>;
+  if (wave >= M::ACTIVE) return;
   const char* base = IS_V ? c.vbase : c.kbase;
+  const int lp = (t * kKeyTile + wave * M::WROWS) >> 4;  // logical page (negative before position 0)
+  int valid = c.L - (lp << 4);  // rows of this page the sequence holds
+  valid = lp < 0 || valid < 0 ? 0 : (valid > kPageSize ? kPageSize : valid);
+  const __amdgpu_buffer_rsrc_t r = uniform_rsrc(base + page * c.page_stride, (uint32_t)valid * c.row_stride);
 #pragma unroll
   for (int i = 0; i < M::LOADS; ++i) {
     const int first_row = (wave * M::LOADS + i) * M::ROWS;
-    const int lp = (t * kKeyTile + first_row) >> 4;  // logical page (negative before position 0)
-    const int lpc = lp < 0 ? 0 : (lp < c.last_page ? lp : c.last_page);
-    const int64_t page = c.bt[lpc];
-    int valid = c.L - (lp << 4);  // rows of this page the sequence holds
-    valid = lp < 0 || valid < 0 ? 0 : (valid > kPageSize ? kPageSize : valid);
-    const __amdgpu_buffer_rsrc_t r = uniform_rsrc(base + page * c.page_stride, (uint32_t)valid * c.row_stride);
     const int row = first_row + lane / TL::NC;
     const int logical = (lane % TL::NC) ^ (IS_V ? TL::swz_v(row) : TL::swz_k(row));
     const uint32_t voff = (uint32_t)(row & 15) * c.row_stride + 16u * logical;
@@ -191,17 +210,18 @@ __device__ __forceinline__ void dma_tile(const TileSrc& c, __bf16* tile, int t, 
 }
 
 // fp8: a tile's codes through registers (one 16-byte chunk per thread and pass)
-template <int D>
+template <int D, int THREADS>
 struct Fp8Tile {
-  static constexpr int CPR = D / 16;     // 16-byte code chunks per row
-  static constexpr int RPP = 256 / CPR;  // rows per pass
+  static constexpr int CPR = D / 16;         // 16-byte code chunks per row
+  static constexpr int RPP = THREADS / CPR;  // rows per pass
   static constexpr int PASSES = RPP >= kKeyTile ? 1 : kKeyTile / RPP;
   u32x4 x[PASSES];
 };
 
-template <int D>
-__device__ __forceinline__ void fp8_fetch(Fp8Tile<D>& st, const TileSrc& c, const char* base, int t, int tid) {
-  using S = Fp8Tile<D>;
+template <int D, int THREADS>
+__device__ __forceinline__ void fp8_fetch(Fp8Tile<D, THREADS>& st, const TileSrc& c, const char* base, int t,
+                                          int tid) {
+  using S = Fp8Tile<D, THREADS>;
   const int chunk = tid % S::CPR, r0 = tid / S::CPR;
 #pragma unroll
   for (int i = 0; i < S::PASSES; ++i) {
@@ -215,9 +235,9 @@ __device__ __forceinline__ void fp8_fetch(Fp8Tile<D>& st, const TileSrc& c, cons
   }
 }
 
-template <int D, bool IS_V>
-__device__ __forceinline__ void fp8_store(const Fp8Tile<D>& st, __bf16* tile, int t, int64_t L, int tid) {
-  using S = Fp8Tile<D>;
+template <int D, int THREADS, bool IS_V>
+__device__ __forceinline__ void fp8_store(const Fp8Tile<D, THREADS>& st, __bf16* tile, int t, int64_t L, int tid) {
+  using S = Fp8Tile<D, THREADS>;
   using TL = TileLayout<D>;
   const int chunk = tid % S::CPR, r0 = tid / S::CPR;
 #pragma unroll
@@ -272,13 +292,11 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-// Iteration t of the main loop (after a barrier) fetches K(t + NS) and
-// V(t + NS - 2), computes the scores of tile t+1, adds P(t-1) V(t-1) into the
-// output and turns the scores of tile t into P(t).  Tile j lives in ring slot
-// j % NS; at the top of iteration t the ring holds K(t+1) and V(t-1), and no
-// wave still reads the slots the iteration overwrites.
-template <int ESZ, int D>
-__global__ __launch_bounds__(256, 1) void prefill_kernel(AttnParams p) {
+template <int ESZ, int D, int NB>
+__global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
+void prefill_kernel(AttnParams p) {
+  constexpr int WAVES = 8 / NB;            // 32 NB query rows per wave, 256 per workgroup
+  constexpr int THREADS = 64 * WAVES;
   constexpr int NKS = D / 16;              // score MFMA k-steps
   constexpr int NDB = D / 32;              // output dim blocks
   constexpr int NS = ESZ == 2 ? 4 : 2;     // K/V ring depth
@@ -332,11 +350,11 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AttnParams p) {
   // ---- query operand (B of S^T = K Q^T): lane l holds row (l & 31) of block
   // nb, dims [16 ks + 8 (l >> 5), +8)
   const int qcol = lane & 31, qgrp = lane >> 5;
-  bf16x8 qb[2][NKS];
-  int32_t qrel[2];  // row position - first_pos - 4 qgrp
+  bf16x8 qb[NB][NKS];
+  int32_t qrel[NB];  // row position - first_pos - 4 qgrp
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int r = wave * 64 + nb * 32 + qcol;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int r = wave * 32 * NB + nb * 32 + qcol;
     const int64_t tok = tok0 + r / G;
     const bool live = r < tpt * G && tok < tok_end;
     qrel[nb] = (int32_t)((live ? tok : tok_end - 1) - tok0) - 4 * qgrp;
@@ -345,11 +363,15 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AttnParams p) {
     for (int ks = 0; ks < NKS; ++ks) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (live) x = *(const u32x4*)(qrow + 16 * ks + 8 * qgrp) ^ qflip;
-      // park the query operand in AGPRs (MFMA reads A/B from either file),
-      // leaving the VGPRs to the softmax and the LDS operand pipeline
-      u32x4 xa;
-      asm("" : "=a"(xa) : "0"(x));
-      qb[nb][ks] = __builtin_bit_cast(bf16x8, xa);
+      if constexpr (NB > 1) {
+        // park the query operand in AGPRs (MFMA reads A/B from either file),
+        // leaving the VGPRs to the softmax and the LDS operand pipeline
+        u32x4 xa;
+        asm("" : "=a"(xa) : "0"(x));
+        qb[nb][ks] = __builtin_bit_cast(bf16x8, xa);
+      } else {
+        qb[nb][ks] = __builtin_bit_cast(bf16x8, x);
+      }
     }
   }
 
@@ -365,34 +387,42 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AttnParams p) {
   const uint32_t vA = (uint32_t)vrow * 2 * D +
                       16u * (uint32_t)((2 * (blk16 & 1) + ((li & 3) >> 1)) ^ TL::swz_v(vrow)) + 8u * (li & 1);
 
-  f32x16 acc[NDB][2];
+  f32x16 acc[NDB][NB];
 #pragma unroll
   for (int d = 0; d < NDB; ++d)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[d][nb][i] = 0.f;
-  float m_ref[2] = {-INFINITY, -INFINITY};  // reference max, log2 units
-  float l_run[2] = {0.f, 0.f};
+  // reference max (log2 units); finite so that exp2(-inf - m_ref) stays 0
+  float m_ref[NB];
+  float l_run[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m_ref[nb] = -1e30f;
+    l_run[nb] = 0.f;
+  }
 
   // S^T of the K tile in ring slot `slot`: s[nb][i] = score of key 8 (i / 4) +
   // 4 qgrp + i % 4 of the tile and query row 32 nb + qcol
-  auto scores = [&](int slot, f32x16 (&s)[2]) __attribute__((always_inline)) {
+  auto read_k = [&](int slot, bf16x8 (&ka)[NKS]) __attribute__((always_inline)) {
     const char* k = sk[slot];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int ks = 0; ks < NKS; ++ks) ka[ks] = *(const bf16x8*)(k + (kA ^ (32u * ks)));
+  };
+  auto scores = [&](const bf16x8 (&ka)[NKS], f32x16 (&s)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[nb][i] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const bf16x8 ka = *(const bf16x8*)(k + (kA ^ (32u * ks)));
-      s[0] = mfma32(ka, qb[0][ks], s[0]);
-      s[1] = mfma32(ka, qb[1][ks], s[1]);
-    }
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[nb] = mfma32(ka[ks], qb[nb][ks], s[nb]);
   };
 
-  // O^T += V^T P^T for the V tile in ring slot `slot`
-  auto pv = [&](int slot, const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
+  // V^T operands of the V tile in ring slot `slot`, then O^T += V^T P^T
+  auto read_v = [&](int slot, bf16x8 (&va)[NDB][2]) __attribute__((always_inline)) {
     const char* v = sv[slot];
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
@@ -401,37 +431,43 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AttnParams p) {
       for (int hh = 0; hh < 2; ++hh) {
         const s16x4 lo = lds_read_tr16(vd + (16 * hh) * 2 * D);
         const s16x4 hi = lds_read_tr16(vd + (16 * hh + 8) * 2 * D);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[d][0] = mfma32(va, pb[hh][0], acc[d][0]);
-        acc[d][1] = mfma32(va, pb[hh][1], acc[d][1]);
+        va[d][hh] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
     }
   };
+  auto scores_pv = [&](const bf16x8 (&ka)[NKS], const bf16x8 (&va)[NDB][2], f32x16 (&s)[NB],
+                       const bf16x8 (&pb)[2][NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[nb][i] = 0.f;
+    static_assert(NKS == 2 * NDB, "one PV MFMA per score k-step");
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) s[nb] = mfma32(ka[ks], qb[nb][ks], s[nb]);
+      const int d = ks / 2, hh = ks % 2;  // PV MFMA (d, hh) after score k-step ks
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) acc[d][nb] = mfma32(va[d][hh], pb[hh][nb], acc[d][nb]);
+    }
+  };
+  auto pv = [&](const bf16x8 (&va)[NDB][2], const bf16x8 (&pb)[2][NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[d][nb] = mfma32(va[d][hh], pb[hh][nb], acc[d][nb]);
+  };
 
-  // P(t) from the raw scores of tile t.  The reference max moves only when a
-  // row's max passes it by more than kLazyRescale; alpha is the factor the
-  // accumulator then needs (1 otherwise).  Returns whether any row moved.
-  auto softmax = [&](auto mask_c, int t, f32x16 (&s)[2], bf16x8 (&pb)[2][2], float (&alpha)[2]) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_c)::value;
-    bool moved = false;
+  // P(t) = exp2(s * cs - m_ref) from the raw scores of tile t, rounded to
+  // bf16; lt = this lane's share of the tile's row sums of the rounded P.
+  auto exps = [&](const f32x16 (&s)[NB], bf16x8 (&pb)[2][NB], float (&lt)[NB]) __attribute__((always_inline)) {
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      if constexpr (MASK) {
-        const int32_t lim = (int32_t)(first_pos - (int64_t)t * kKeyTile) + qrel[nb];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[nb][i] = 8 * (i >> 2) + (i & 3) > lim ? -INFINITY : s[nb][i];
-      }
-      float mx = __builtin_fmaxf(s[nb][0], s[nb][1]);
-#pragma unroll
-      for (int i = 2; i < 16; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[nb][i], s[nb][i + 1]));
-      mx = max_pair(mx) * cs;
-      const bool need = mx > m_ref[nb] + kLazyRescale;
-      alpha[nb] = need ? __builtin_amdgcn_exp2f(m_ref[nb] - mx) : 1.0f;
-      m_ref[nb] = need ? mx : m_ref[nb];
-      moved |= need;
-      float l = l_run[nb] * alpha[nb];
+    for (int nb = 0; nb < NB; ++nb) {
       const float neg_m = -m_ref[nb];
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+      float l = 0.f;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         u32x4 w;
@@ -445,81 +481,168 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AttnParams p) {
         }
         pb[hh][nb] = __builtin_bit_cast(bf16x8, w);
       }
-      l_run[nb] = l;
+      lt[nb] = l;
     }
-    return __builtin_amdgcn_ballot_w64(moved) != 0;
+  };
+
+  // Softmax of tile t with a lazy reference max m_ref.  The common step never
+  // computes a max: P is taken against the current reference and, as long as
+  // no lane's partial row sum exceeds kLazyBound (so no single P does),
+  // the reference stands.  Otherwise (always on the first tile, where m_ref
+  // starts at -1e30) the reference moves to the row max, P is recomputed and
+  // alpha = exp2(m_old - m_new) is returned for the accumulator; the function
+  // then returns true.
+  auto softmax = [&](auto mask_c, int t, f32x16 (&s)[NB], bf16x8 (&pb)[2][NB], float (&alpha)[NB]) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_c)::value;
+    if constexpr (MASK) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int32_t lim = (int32_t)(first_pos - (int64_t)t * kKeyTile) + qrel[nb];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[nb][i] = 8 * (i >> 2) + (i & 3) > lim ? -INFINITY : s[nb][i];
+      }
+    }
+    float lt[NB];
+    exps(s, pb, lt);
+    bool over = false;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) over |= lt[nb] > kLazyBound;
+    const bool moved = __builtin_amdgcn_ballot_w64(over) != 0;
+    // Instruction order of the iteration up to here: the first operand reads,
+    // then each MFMA followed by the next operand reads and a run of softmax
+    // VALU work that co-executes with it.
+    constexpr int kMfma = NKS * NB + 2 * NDB * NB, kReads = NKS + 4 * NDB;
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < kMfma; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (4 + 2 * i < kReads) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
+    }
+    if (moved) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        float mx = __builtin_fmaxf(s[nb][0], s[nb][1]);
+#pragma unroll
+        for (int i = 2; i < 16; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[nb][i], s[nb][i + 1]));
+        mx = max_pair(mx) * cs;  // -inf if every key of the row is masked in this tile
+        const float m_new = __builtin_fmaxf(m_ref[nb], mx);
+        alpha[nb] = m_new == m_ref[nb] ? 1.0f : __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
+        m_ref[nb] = m_new;
+        l_run[nb] *= alpha[nb];
+      }
+      exps(s, pb, lt);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) l_run[nb] += lt[nb];
+    return moved;
   };
 
   // (one 16-register block at a time, so the rare rescale needs few
   // temporaries beside the live state)
-  auto rescale = [&](const float (&alpha)[2]) __attribute__((always_inline)) {
+  auto rescale = [&](const float (&alpha)[NB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NB; ++nb) {
         acc[d][nb] *= alpha[nb];
         __builtin_amdgcn_sched_barrier(0);
       }
   };
 
   // ---- tile fetches.  Tile j lives in ring slot j % NS.  bf16: DMA issued
-  // for "virtual iteration" u (K(u+NS-1), V(u+NS-2)), so that every iteration
+  // for "virtual iteration" u (K(u+NS), V(u+NS-2)), so that every iteration
   // issues the same number of loads and vmcnt(LOADS_AFTER) leaves exactly the
   // tiles the next iteration needs in flight.
-  constexpr int LOADS_AFTER = (NS - 2) * 2 * Dma<D>::LOADS;
-  auto issue = [&](int u, int slot_k, int slot_v) __attribute__((always_inline)) {
-    dma_tile<D, false>(c, (__bf16*)sk[slot_k], u + NS - 1, wave, lane);
-    dma_tile<D, true>(c, (__bf16*)sv[slot_v], u + NS - 2, wave, lane);
+  constexpr int LOADS_AFTER = (NS - 2) * 2 * Dma<D, WAVES>::LOADS;
+  auto issue = [&](int u, int slot_k, int slot_v, int64_t page_k, int64_t page_v) __attribute__((always_inline)) {
+    dma_tile<D, WAVES, false>(c, (__bf16*)sk[slot_k], u + NS, page_k, wave, lane);
+    dma_tile<D, WAVES, true>(c, (__bf16*)sv[slot_v], u + NS - 2, page_v, wave, lane);
   };
-  Fp8Tile<D> fk, fv;  // fp8 staging: iteration t fetches K(t+1) and V(t)
-  auto store8 = [&](int t, int slot_k, int slot_v) __attribute__((always_inline)) {
-    fp8_store<D, false>(fk, (__bf16*)sk[slot_k], t + 1, L, tid);
-    fp8_store<D, true>(fv, (__bf16*)sv[slot_v], t, L, tid);
+  // Page ids of this wave's rows, K(j) and V(j) sharing them: the V fetch of
+  // an iteration reuses the id its K fetch used two iterations earlier, and
+  // the next K id is loaded one iteration ahead.
+  int64_t page_q[3] = {0, 0, 0};  // K page of this, the previous and the one before
+  Fp8Tile<D, THREADS> fk, fv;     // fp8 staging: iteration t fetches K(t+2) and V(t)
+  auto store8 = [&](int t, int slot) __attribute__((always_inline)) {
+    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[slot], t + 2, L, tid);
+    fp8_store<D, THREADS, true>(fv, (__bf16*)sv[slot], t, L, tid);
   };
 
-  // ---- prologue: K(0) resident, V(-1) zero (the PV of the first iteration
-  // multiplies it by P(-1) = 0), later tiles in flight
-  bf16x8 pb_prev[2][2];
+  // ---- prologue: K(0) and K(1) resident, V(-2) and V(-1) zero (the PV of
+  // the first iteration multiplies V(-1) by P(-1) = 0), later tiles in flight
+  bf16x8 pb_prev[2][NB];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) pb_prev[hh][nb] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int nb = 0; nb < NB; ++nb) pb_prev[hh][nb] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
   if constexpr (ESZ == 2) {
 #pragma unroll
-    for (int u = 1 - NS; u < 0; ++u) issue(u, (u + NS - 1) % NS, (u + 2 * NS - 2) % NS);
-    wait_vmem<LOADS_AFTER + Dma<D>::LOADS>();  // K(0) landed (V(-1) is a zero fill)
+    for (int u = -NS; u < 0; ++u)
+      issue(u, (u + NS) % NS, (u + 2 * NS - 2) % NS, wave_page<D, WAVES>(c, u + NS, wave),
+            wave_page<D, WAVES>(c, u + NS - 2, wave));
+    page_q[2] = wave_page<D, WAVES>(c, NS - 2, wave);
+    page_q[1] = wave_page<D, WAVES>(c, NS - 1, wave);
+    page_q[0] = wave_page<D, WAVES>(c, NS, wave);
+    wait_vmem<LOADS_AFTER + Dma<D, WAVES>::LOADS>();  // K(0) and K(1) landed
   } else {
-    fp8_fetch<D>(fk, c, c.kbase, 0, tid);
-    fp8_store<D, false>(fk, (__bf16*)sk[0], 0, L, tid);
-    for (int i = tid; i < TB / 16; i += 256) ((u32x4*)sv[NS - 1])[i] = u32x4{0u, 0u, 0u, 0u};
+    fp8_fetch<D, THREADS>(fk, c, c.kbase, 0, tid);
+    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[0], 0, L, tid);
+    fp8_fetch<D, THREADS>(fk, c, c.kbase, 1, tid);
+    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[1], 1, L, tid);
+    for (int i = tid; i < TB / 16; i += THREADS) ((u32x4*)sv[1])[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  barrier_lds();
+  f32x16 s_cur[NB];
+  {
+    bf16x8 ka[NKS];
+    read_k(0, ka);
+    scores(ka, s_cur);
   }
 
   // Iteration t, ring position R = t % NS (a compile-time constant at every
-  // call, so every LDS access names its slot variable): scores of tile t,
-  // then P(t-1) V(t-1) into the output while the softmax of tile t runs, so
-  // MFMA and VALU work overlap.  At the top (after the barrier) K(t) and
-  // V(t-1) are resident and no wave still reads K(t-1) or V(t-2), whose slots
-  // the iteration's fetches overwrite.  Tiles past the sequence are zero
-  // filled and fully masked, so iterations past the last tile add nothing.
+  // call, so every LDS access names its slot variable).  At the top (after the
+  // barrier) K(t+1) and V(t-1) are resident and no wave still reads K(t) or
+  // V(t-2), whose slots the iteration's fetches overwrite.  The MFMAs of the
+  // iteration (scores of tile t+1, P(t-1) V(t-1) into the output) do not
+  // depend on its VALU work (the softmax of tile t), and the two are
+  // interleaved instruction by instruction so that they co-execute.  Tiles
+  // past the sequence are zero filled and fully masked, so iterations past the
+  // last tile add nothing.
   auto iteration = [&](auto mask_c, auto r_c, int t) __attribute__((always_inline)) {
     constexpr int R = decltype(r_c)::value;
     barrier_lds();
     if constexpr (ESZ == 2) {
-      issue(t, (R + NS - 1) % NS, (R + NS - 2) % NS);
+      issue(t, R, (R + NS - 2) % NS, page_q[0], page_q[2]);
+      page_q[2] = page_q[1];
+      page_q[1] = page_q[0];
     } else {
-      fp8_fetch<D>(fk, c, c.kbase, t + 1, tid);
-      fp8_fetch<D>(fv, c, c.vbase, t, tid);
+      fp8_fetch<D, THREADS>(fk, c, c.kbase, t + 2, tid);
+      fp8_fetch<D, THREADS>(fv, c, c.vbase, t, tid);
     }
-    f32x16 s[2];
-    scores(R, s);
-    pv((R + NS - 1) % NS, pb_prev);
-    float alpha[2];
-    bf16x8 pb[2][2];
-    if (softmax(mask_c, t, s, pb, alpha)) rescale(alpha);
-    if constexpr (ESZ == 2) wait_vmem<LOADS_AFTER>();
-    else store8(t, (R + 1) % NS, R);
+    bf16x8 ka[NKS], va[NDB][2];
+    read_k((R + 1) % NS, ka);
+    read_v((R + NS - 1) % NS, va);
+    // score MFMAs (one accumulation chain per row block) alternate with the
+    // independent PV MFMAs, so no MFMA waits for its predecessor's result
+    f32x16 s_next[NB];
+    scores_pv(ka, va, s_next, pb_prev);
+    float alpha[NB];
+    bf16x8 pb[2][NB];
+    if (softmax(mask_c, t, s_cur, pb, alpha)) rescale(alpha);
+    if constexpr (ESZ == 2) {
+      wait_vmem<LOADS_AFTER>();
+      // the next K page id, loaded just before the barrier that waits for it
+      // anyway (an earlier scalar load would force a full LDS drain at the
+      // first operand wait after it)
+      __builtin_amdgcn_sched_barrier(0);
+      page_q[0] = wave_page<D, WAVES>(c, t + NS + 1, wave);
+    } else {
+      store8(t, R);
+    }
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NB; ++nb) {
+      s_cur[nb] = s_next[nb];
       pb_prev[0][nb] = pb[0][nb];
       pb_prev[1][nb] = pb[1][nb];
     }
@@ -545,9 +668,9 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(AttnParams p) {
   float out_scale = 1.0f;
   if constexpr (ESZ == 1) out_scale = p.v_scale[h];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const float l = sum_pair(l_run[nb]);
-    const int r = wave * 64 + nb * 32 + qcol;
+    const int r = wave * 32 * NB + nb * 32 + qcol;
     const int64_t tok = tok0 + r / G;
     if (r >= tpt * G || tok >= tok_end) continue;
     const float inv = out_scale / l;
@@ -568,13 +691,15 @@ hipError_t launch_prefill(const AttnParams& p, hipStream_t stream) {
   if (p.T == 0 || p.B == 0) return hipSuccess;
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, p);
   const dim3 grid((unsigned)(prefill_max_items(p.T, p.B, p.G) * p.Hkv));
+  constexpr int NB = kPrefillRowBlocks;
+  const dim3 block(512 / NB);
   const bool fp8 = p.kv_type == KV_FP8;
   if (p.D == 128) {
-    if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 128>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((prefill_kernel<2, 128>), grid, dim3(256), 0, stream, p);
+    if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 128, NB>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_kernel<2, 128, NB>), grid, block, 0, stream, p);
   } else {
-    if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 64>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((prefill_kernel<2, 64>), grid, dim3(256), 0, stream, p);
+    if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 64, NB>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_kernel<2, 64, NB>), grid, block, 0, stream, p);
   }
   return hipGetLastError();
 }
