@@ -13,7 +13,9 @@ step is timed with a pair of HIP events on the stream the kernels run on.
 
 The printed JSON line carries:
   value        decode KV-read GB/s of the step: algorithmic bytes / step time,
-  roofline     the decode attention call against the 8 TB/s HBM peak,
+  roofline     the split-K decode kernel (the step's dominant kernel), timed
+               alone with HIP events the library records around it, against
+               the 8 TB/s HBM peak; decode_call has the whole attention call,
   prefill, ... the other workloads (chunked prefill TFLOP/s against the bf16
                MFMA peak, shared-prefix decode, fp8 long-context decode),
   cpu_baseline the CPU oracle on the same decode workload.
@@ -53,6 +55,21 @@ def kernel_source_hash() -> str:
             h.update(name.encode())
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def decode_kernel_bytes(w) -> int:
+    """Algorithmic bytes of the split-K decode kernel alone: K+V rows once per
+    (sequence, KV head), q and the block_table entries it reads (its partial
+    results are an implementation artefact and are not counted)."""
+    cfg = w.cfg
+    esz = {"f32": 4, "bf16": 2, "fp8_e4m3fn": 1}[cfg.kv_dtype]
+    qsz = 4 if cfg.q_dtype == "f32" else 2
+    lens = w.seq_lens.cpu().numpy().astype(int)
+    kv = int(lens.sum()) * cfg.hkv * cfg.head_dim * esz * 2
+    q = w.q.shape[0] * cfg.hq * cfg.head_dim * qsz
+    table = int(sum(-(-l // cfg.page_size) for l in lens)) * 8
+    scales = 2 * cfg.hkv * 4 if cfg.kv_dtype == "fp8_e4m3fn" else 0
+    return int(kv + q + table + scales)
 
 
 def decode_bytes(w) -> int:
@@ -116,39 +133,61 @@ class Runner:
         w = self.w
         self.pkv.paged_kv_write(w.k_new, w.v_new, w.slot_mapping, self.kp, self.vp)
 
-    def attend(self):
+    def attend(self, kernel_events=None):
         w = self.w
         self.pkv.paged_attention(w.q, self.kp, self.vp, w.block_table, w.seq_lens, w.query_start_loc,
                                  w.scale, self.out, k_scale=w.k_scale, v_scale=w.v_scale,
                                  max_query_len=w.max_query_len, split_tokens=w.split_tokens,
-                                 workspace=self.ws)
+                                 workspace=self.ws, timing_events=kernel_events)
 
 
-def time_steps(runner, torch, steps, warmup, flush, progress=""):
-    """Per-step HIP event times (ms) of write and attention; flush outside."""
+class Times:
+    """Per-step HIP event times (ms): write, attention call, its main attention
+    kernel alone (events the library records on the same stream), whole step."""
+
+    def __init__(self, write, attn, kernel, step, wall):
+        self.write, self.attn, self.kernel, self.step, self.wall = write, attn, kernel, step, wall
+
+
+def time_steps(runner, torch, steps, warmup, flush, progress="", kernel_events=True):
+    """Time `steps` steps after `warmup` untimed ones; the cache flush, when
+    given, runs before each step outside its timed region.  With
+    kernel_events the library also records a HIP event pair around the main
+    attention kernel (the two extra event packets lengthen the call by a few
+    microseconds, so whole-step figures come from a pass without them)."""
     for _ in range(warmup):
         runner.write()
         runner.attend()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
         if flush is not None:
             flush.fill_(i & 0xFF)
-        ev[i][0].record()
+        e = ev[i]
+        e[0].record()
         runner.write()
-        ev[i][1].record()
-        runner.attend()
-        ev[i][2].record()
+        e[1].record()
+        runner.attend(kernel_events=(e[3], e[4]) if kernel_events else None)
+        e[2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    write_ms = [a.elapsed_time(b) for a, b, _ in ev]
-    attn_ms = [b.elapsed_time(c) for _, b, c in ev]
-    step_ms = [a.elapsed_time(c) for a, _, c in ev]
+    t = Times(write=[e[0].elapsed_time(e[1]) for e in ev], attn=[e[1].elapsed_time(e[2]) for e in ev],
+              kernel=[e[3].elapsed_time(e[4]) for e in ev] if kernel_events else None,
+              step=[e[0].elapsed_time(e[2]) for e in ev], wall=wall)
     if progress:
-        log(f"{progress}: {steps} steps, median step {statistics.median(step_ms):.4f} ms")
-    return write_ms, attn_ms, step_ms, wall
+        extra = f", main kernel {statistics.median(t.kernel):.4f} ms" if kernel_events else ""
+        log(f"{progress}: {steps} steps, median step {statistics.median(t.step):.4f} ms{extra}")
+    return t
+
+
+def time_workload(runner, torch, steps, warmup, flush, progress):
+    """Two timed passes: whole steps without in-call events, then the main
+    kernel alone with them."""
+    plain = time_steps(runner, torch, steps, warmup, flush, progress + " (steps)", kernel_events=False)
+    kern = time_steps(runner, torch, steps, 1, flush, progress + " (main kernel)", kernel_events=True)
+    return plain, kern
 
 
 def traffic_from_profile(kernel: str):
@@ -237,23 +276,26 @@ def main(argv=None) -> int:
         calib = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
         torch.empty_like(calib).copy_(calib)
         del calib
-        wr, at, st, _ = time_steps(Runner(pkv, w, torch), torch, args.steps, args.warmup, flush,
-                                   args.profile_workload)
-        print(json.dumps({"workload": w.cfg.name, "write_ms_median": statistics.median(wr),
-                          "attention_ms_median": statistics.median(at),
-                          "step_ms_median": statistics.median(st)}), flush=True)
+        t = time_steps(Runner(pkv, w, torch), torch, args.steps, args.warmup, flush, args.profile_workload)
+        print(json.dumps({"workload": w.cfg.name, "write_ms_median": statistics.median(t.write),
+                          "attention_ms_median": statistics.median(t.attn),
+                          "main_kernel_ms_median": statistics.median(t.kernel),
+                          "main_kernel_ms_mean": statistics.fmean(t.kernel),
+                          "step_ms_median": statistics.median(t.step)}), flush=True)
         return 0
 
     # ---- headline: decode workload, write + attention per step
     log("generating decode workload (config 2)")
     w2 = W.generate(2, dev)
     r2 = Runner(pkv, w2, torch)
-    wr, at, st, wall = time_steps(r2, torch, args.steps, args.warmup, flush, "decode bf16")
+    t2, k2 = time_workload(r2, torch, args.steps, args.warmup, flush, "decode bf16")
     bytes2 = decode_bytes(w2)
-    step_ms = statistics.median(st)
-    attn_ms = statistics.median(at)
-    achieved = bytes2 / (attn_ms * 1e-3) / 1e9
-    _, warm_at, _, _ = time_steps(r2, torch, max(5, args.steps // 3), 2, None)
+    kbytes2 = decode_kernel_bytes(w2)
+    step_ms = statistics.median(t2.step)
+    attn_ms = statistics.median(t2.attn)
+    kern_ms = statistics.fmean(k2.kernel)
+    achieved = kbytes2 / (kern_ms * 1e-3) / 1e9
+    warm = time_steps(r2, torch, max(5, args.steps // 3), 2, None, kernel_events=False)
     result = {
         "metric": METRIC,
         "value": round(bytes2 / (step_ms * 1e-3) / 1e9, 2),
@@ -276,19 +318,29 @@ def main(argv=None) -> int:
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode attention call (decode_split_kernel + merge_kernel)",
+            "kernel": "decode_kernel<2,128> (split-K decode pass)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic_from_profile("decode_split_kernel<2,128>"),
-            "algorithmic_bytes_per_launch": bytes2,
-            "launch_ms_median": round(attn_ms, 5),
-            "launch_ms_min": round(min(at), 5),
-            "launch_ms_warm_median": round(statistics.median(warm_at), 5),
+            "traffic": traffic_from_profile("decode_kernel<2,128>"),
+            "algorithmic_bytes_per_launch": kbytes2,
+            "launch_ms_mean": round(kern_ms, 5),
+            "launch_ms_median": round(statistics.median(k2.kernel), 5),
+            "launch_ms_min": round(min(k2.kernel), 5),
+            "launches_timed": len(k2.kernel),
         },
-        "write_ms_median": round(statistics.median(wr), 5),
-        "timed_loop_wall_s": round(wall, 4),
+        "decode_call": {
+            "kernels": "decode_kernel + merge_kernel",
+            "algorithmic_bytes": bytes2,
+            "ms_median": round(attn_ms, 5),
+            "ms_min": round(min(t2.attn), 5),
+            "GBps": round(bytes2 / (attn_ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(bytes2 / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "ms_warm_median": round(statistics.median(warm.attn), 5),
+        },
+        "write_ms_median": round(statistics.median(t2.write), 5),
+        "timed_loop_wall_s": round(t2.wall, 4),
     }
     del r2
 
@@ -298,21 +350,25 @@ def main(argv=None) -> int:
         log("generating prefill workload (config 3)")
         w3 = W.generate(3, dev)
         r3 = Runner(pkv, w3, torch)
-        wr3, at3, st3, _ = time_steps(r3, torch, max(5, args.steps // 2), args.warmup, flush, "prefill bf16")
+        t3, kt3 = time_workload(r3, torch, max(5, args.steps // 2), args.warmup, flush, "prefill bf16")
         fl = prefill_flops(w3)
-        a3 = statistics.median(at3)
+        a3 = statistics.median(t3.attn)
+        k3 = statistics.fmean(kt3.kernel)
         extra["prefill"] = {
             "workload": "chunked causal prefill, bf16: 8 sequences x 512 new tokens on U{0..8192} old "
                         "context, Hq 32, Hkv 8, head_dim 128",
+            "kernel": "prefill_kernel<2,128,1>",
             "bound": "mfma", "unit": "TFLOP/s",
-            "achieved": round(fl / (a3 * 1e-3) / 1e12, 2),
+            "achieved": round(fl / (k3 * 1e-3) / 1e12, 2),
             "peak": BF16_MFMA_PEAK_TFLOPS,
-            "frac": round(fl / (a3 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "frac": round(fl / (k3 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
             "flop_per_launch": fl,
-            "attention_ms_median": round(a3, 5),
-            "write_ms_median": round(statistics.median(wr3), 5),
-            "write_GBps": round(write_bytes(w3) / (statistics.median(wr3) * 1e-3) / 1e9, 1),
-            "step_ms_median": round(statistics.median(st3), 5),
+            "launch_ms_mean": round(k3, 5),
+            "call_ms_median": round(a3, 5),
+            "call_TFLOPs": round(fl / (a3 * 1e-3) / 1e12, 2),
+            "write_ms_median": round(statistics.median(t3.write), 5),
+            "write_GBps": round(write_bytes(w3) / (statistics.median(t3.write) * 1e-3) / 1e9, 1),
+            "step_ms_median": round(statistics.median(t3.step), 5),
         }
         del r3, w3
         torch.cuda.empty_cache()
@@ -320,15 +376,15 @@ def main(argv=None) -> int:
         log("generating shared-prefix decode workload (config 4)")
         w4 = W.generate(4, dev)
         r4 = Runner(pkv, w4, torch)
-        _, at4, st4, _ = time_steps(r4, torch, args.steps, args.warmup, flush, "shared-prefix decode")
-        a4 = statistics.median(at4)
+        t4 = time_steps(r4, torch, args.steps, args.warmup, flush, "shared-prefix decode", kernel_events=False)
+        a4 = statistics.median(t4.attn)
         extra["shared_prefix_decode"] = {
             "workload": "256 sequences sharing 128 prefix pages + U{0..512} private tokens, Hq 64, Hkv 8",
             "unit": "GB/s",
             "logical_GBps": round(decode_bytes(w4) / (a4 * 1e-3) / 1e9, 1),
             "unique_GBps": round(unique_decode_bytes(w4) / (a4 * 1e-3) / 1e9, 1),
             "attention_ms_median": round(a4, 5),
-            "step_ms_median": round(statistics.median(st4), 5),
+            "step_ms_median": round(statistics.median(t4.step), 5),
         }
         del r4, w4
         torch.cuda.empty_cache()
@@ -336,19 +392,24 @@ def main(argv=None) -> int:
         log("generating long-context fp8 decode workload (config 5)")
         w5 = W.generate(5, dev)
         r5 = Runner(pkv, w5, torch)
-        _, at5, st5, _ = time_steps(r5, torch, args.steps, args.warmup, flush, "fp8 long decode")
-        a5 = statistics.median(at5)
+        t5, kt5 = time_workload(r5, torch, args.steps, args.warmup, flush, "fp8 long decode")
+        a5 = statistics.median(t5.attn)
+        k5 = statistics.fmean(kt5.kernel)
         b5 = decode_bytes(w5)
+        kb5 = decode_kernel_bytes(w5)
         extra["fp8_long_decode"] = {
             "workload": "16 sequences, U{32768..131072} positions, fp8 E4M3FN KV with per-head scales, "
                         "Hq 64, Hkv 8, split-K over 2048-position partitions",
+            "kernel": "decode_kernel<1,128>",
             "bound": "hbm", "unit": "GB/s",
-            "achieved": round(b5 / (a5 * 1e-3) / 1e9, 1),
+            "achieved": round(kb5 / (k5 * 1e-3) / 1e9, 1),
             "peak": HBM_PEAK_GBS,
-            "frac": round(b5 / (a5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes_per_launch": b5,
-            "attention_ms_median": round(a5, 5),
-            "step_ms_median": round(statistics.median(st5), 5),
+            "frac": round(kb5 / (k5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": kb5,
+            "launch_ms_mean": round(k5, 5),
+            "call_ms_median": round(a5, 5),
+            "call_GBps": round(b5 / (a5 * 1e-3) / 1e9, 1),
+            "step_ms_median": round(statistics.median(t5.step), 5),
         }
         del r5, w5
         torch.cuda.empty_cache()

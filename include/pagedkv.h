@@ -99,6 +99,11 @@ typedef struct {
                              (about B * max_blocks * page_size / 2 / split_tokens, rounded
                              to a multiple of the CU count).  0 = one range per CU.  The
                              result does not depend on it beyond rounding. */
+  void* timing_events[2]; /* optional pair of hipEvent_t (created by the caller), recorded on
+                             `stream` immediately before and after the call's main attention
+                             kernel: the split-K decode kernel, the prefill kernel or the fp32
+                             kernel, without the plan and merge launches around it.  NULL =
+                             none.  For measuring that kernel alone. */
 } pkv_attn_opts;
 
 /*

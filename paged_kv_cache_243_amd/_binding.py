@@ -37,7 +37,8 @@ class PkvTensor(ctypes.Structure):
 class PkvAttnOpts(ctypes.Structure):
     _fields_ = [("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("max_query_len", ctypes.c_int32), ("split_tokens", ctypes.c_int32)]
+                ("max_query_len", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
+                ("timing_events", ctypes.c_void_p * 2)]
 
 
 class PagedKVError(RuntimeError):
@@ -119,7 +120,7 @@ def paged_kv_write(k, v, slot_mapping, key_pool, value_pool) -> None:
     _check(st, "paged_kv_write")
 
 
-def _opts(k_scale, v_scale, workspace, max_query_len, split_tokens) -> PkvAttnOpts:
+def _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_events=None) -> PkvAttnOpts:
     o = PkvAttnOpts()
     o.k_scale = k_scale.data_ptr() if k_scale is not None else None
     o.v_scale = v_scale.data_ptr() if v_scale is not None else None
@@ -127,6 +128,13 @@ def _opts(k_scale, v_scale, workspace, max_query_len, split_tokens) -> PkvAttnOp
     o.workspace_bytes = workspace.numel() if workspace is not None else 0
     o.max_query_len = int(max_query_len or 0)
     o.split_tokens = int(split_tokens or 0)
+    if timing_events is not None:
+        for e in timing_events:
+            if not e.cuda_event:  # torch creates the HIP event at its first record
+                e.record()
+        begin, end = timing_events
+        o.timing_events[0] = begin.cuda_event
+        o.timing_events[1] = end.cuda_event
     return o
 
 
@@ -141,17 +149,19 @@ def paged_attention_workspace_size(q, key_pool, block_table, *, max_query_len=No
 
 def paged_attention(q, key_pool, value_pool, block_table, seq_lens, query_start_loc, scale, out, *,
                     k_scale=None, v_scale=None, max_query_len=None, split_tokens=0,
-                    workspace=None) -> torch.Tensor:
+                    workspace=None, timing_events=None) -> torch.Tensor:
     """Causal GQA attention over paged KV into ``out`` [T, Hq, D] (returned).
 
     The workspace the call needs is allocated through torch's allocator when
-    ``workspace`` is not given (a uint8 device tensor owned by the caller)."""
+    ``workspace`` is not given (a uint8 device tensor owned by the caller).
+    ``timing_events`` = (begin, end) torch.cuda.Event pair recorded around the
+    call's main attention kernel."""
     lib = load()
     if workspace is None:
         need = paged_attention_workspace_size(q, key_pool, block_table, max_query_len=max_query_len,
                                               split_tokens=split_tokens)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
-    opts = _opts(k_scale, v_scale, workspace, max_query_len, split_tokens)
+    opts = _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_events)
     st = lib.paged_attention(describe(q), describe(key_pool), describe(value_pool), describe(block_table),
                              describe(seq_lens), describe(query_start_loc), ctypes.c_float(scale),
                              describe(out), ctypes.byref(opts), _stream(q))

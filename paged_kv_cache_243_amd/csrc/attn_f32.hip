@@ -128,13 +128,15 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(AttnParams p) {
   }
 }
 
-hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
   if (p.T == 0) return hipSuccess;
   dim3 grid((unsigned)p.T, (unsigned)p.Hkv);
+  if (ev.begin) (void)hipEventRecord(ev.begin, stream);
   if (p.D == 128)
     hipLaunchKernelGGL(attention_f32_kernel<128>, grid, dim3(64), 0, stream, p);
   else
     hipLaunchKernelGGL(attention_f32_kernel<64>, grid, dim3(64), 0, stream, p);
+  if (ev.end) (void)hipEventRecord(ev.end, stream);
   return hipGetLastError();
 }
 

@@ -560,19 +560,21 @@ int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu) {
 }
 
 template <int ESZ, int D>
-static void launch_decode_t(const AttnParams& p, hipStream_t stream) {
+static void launch_decode_t(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
   const int threads = 64 * decode_waves(p.Hkv);
+  if (ev.begin) (void)hipEventRecord(ev.begin, stream);
   hipLaunchKernelGGL((decode_kernel<ESZ, D>), dim3((unsigned)p.grid_parts), dim3(threads), 0, stream, p);
+  if (ev.end) (void)hipEventRecord(ev.end, stream);
   hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)p.Hq, (unsigned)p.B), dim3(64), 0, stream, p);
 }
 
-hipError_t launch_decode(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
   if (p.B == 0) return hipSuccess;
   const bool fp8 = p.kv_type == KV_FP8;
   if (p.D == 128) {
-    if (fp8) launch_decode_t<1, 128>(p, stream); else launch_decode_t<2, 128>(p, stream);
+    if (fp8) launch_decode_t<1, 128>(p, stream, ev); else launch_decode_t<2, 128>(p, stream, ev);
   } else {
-    if (fp8) launch_decode_t<1, 64>(p, stream); else launch_decode_t<2, 64>(p, stream);
+    if (fp8) launch_decode_t<1, 64>(p, stream, ev); else launch_decode_t<2, 64>(p, stream, ev);
   }
   return hipGetLastError();
 }

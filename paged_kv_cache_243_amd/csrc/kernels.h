@@ -43,10 +43,16 @@ struct AttnParams {
   int32_t* ws_plan;    // prefill tile schedule
 };
 
+// Optional events recorded around the main attention kernel of a launch.
+struct LaunchEvents {
+  hipEvent_t begin = nullptr;
+  hipEvent_t end = nullptr;
+};
+
 hipError_t launch_write(const WriteParams& p, hipStream_t stream);
-hipError_t launch_decode(const AttnParams& p, hipStream_t stream);
-hipError_t launch_prefill(const AttnParams& p, hipStream_t stream);
-hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream);
+hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
+hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
+hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 
 // workspace helpers shared by the ABI layer and the launchers
 size_t decode_workspace_bytes(int64_t B, int Hq, int D);

@@ -205,7 +205,7 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
 
 extern "C" {
 
-int pkv_abi_version(void) { return 1; }
+int pkv_abi_version(void) { return 2; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -269,20 +269,25 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
   AttnParams& p = plan.p;
   hipStream_t s = (hipStream_t)stream;
   hipError_t err = hipSuccess;
+  pkv::LaunchEvents ev;
+  if (opts) {
+    ev.begin = (hipEvent_t)opts->timing_events[0];
+    ev.end = (hipEvent_t)opts->timing_events[1];
+  }
   switch (plan.kernel) {
     case AttnPlan::kNone:
       return PKV_OK;
     case AttnPlan::kF32:
-      err = pkv::launch_attention_f32(p, s);
+      err = pkv::launch_attention_f32(p, s, ev);
       break;
     case AttnPlan::kDecode:
       pkv::decode_workspace_carve(p, opts->workspace);
       p.grid_parts = pkv::decode_grid_parts(p.B, p.max_blocks * kPageSize, p.split_tokens, device_cu_count());
-      err = pkv::launch_decode(p, s);
+      err = pkv::launch_decode(p, s, ev);
       break;
     case AttnPlan::kPrefill:
       p.ws_plan = plan.workspace > 0 ? (int32_t*)opts->workspace : nullptr;
-      err = pkv::launch_prefill(p, s);
+      err = pkv::launch_prefill(p, s, ev);
       break;
   }
   return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;

@@ -687,9 +687,10 @@ void prefill_kernel(AttnParams p) {
   }
 }
 
-hipError_t launch_prefill(const AttnParams& p, hipStream_t stream) {
+hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
   if (p.T == 0 || p.B == 0) return hipSuccess;
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+  if (ev.begin) (void)hipEventRecord(ev.begin, stream);
   const dim3 grid((unsigned)(prefill_max_items(p.T, p.B, p.G) * p.Hkv));
   constexpr int NB = kPrefillRowBlocks;
   const dim3 block(512 / NB);
@@ -701,6 +702,7 @@ hipError_t launch_prefill(const AttnParams& p, hipStream_t stream) {
     if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 64, NB>), grid, block, 0, stream, p);
     else hipLaunchKernelGGL((prefill_kernel<2, 64, NB>), grid, block, 0, stream, p);
   }
+  if (ev.end) (void)hipEventRecord(ev.end, stream);
   return hipGetLastError();
 }
 

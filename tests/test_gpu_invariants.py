@@ -145,3 +145,24 @@ def test_fp8_decode_of_every_code(gpu):
             nan = np.isnan(want)
             assert np.array_equal(np.isnan(got[hq]), nan)
             assert np.array_equal(got[hq][~nan], want[~nan])
+
+
+@pytest.mark.parametrize("cid", [2, 3])
+def test_timing_events_bracket_the_main_kernel(gpu, cid):
+    """The optional timing events change nothing in the result and bracket a
+    non-empty interval inside the call's own."""
+    note(f"timing events config {cid}")
+    w = W.generate(W.SMALL[cid], DEV)
+    kp, vp = gpu_write(gpu, w)
+    ref = gpu_attend(gpu, w, kp, vp)
+    out = torch.empty_like(w.q)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    ev[0].record()
+    gpu.paged_attention(w.q, kp, vp, w.block_table, w.seq_lens, w.query_start_loc, w.scale, out,
+                        k_scale=w.k_scale, v_scale=w.v_scale, max_query_len=w.max_query_len,
+                        split_tokens=w.split_tokens, timing_events=(ev[1], ev[2]))
+    ev[3].record()
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(out), _bits(ref))
+    kernel_ms, call_ms = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+    assert 0.0 < kernel_ms <= call_ms
