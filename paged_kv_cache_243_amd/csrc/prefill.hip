@@ -11,33 +11,36 @@
 // Mapping onto gfx950 (FlashAttention-style online softmax):
 //  * Work item = (query tile, KV head).  A query tile packs (token,
 //    head-of-group) pairs, row = token * G + g, 256 / G tokens, so the G heads
-//    that share a KV head share every K/V tile.  One workgroup of 4 waves per
-//    item, each wave owning 64 rows (two 32-row column blocks).  A
-//    one-workgroup plan kernel lists the tiles longest first (their KV length
-//    sets their cost), so in-order dispatch fills the CUs greedily.
-//  * Keys stream in tiles of 32 positions (2 pages).  bf16 tiles go from
-//    global memory straight into LDS (buffer_load ... lds); every page gets a
-//    buffer descriptor whose range ends at the sequence's last valid row, so
-//    rows at positions >= seq_lens read as zeros whatever the pool holds.  fp8
-//    tiles go through registers and are widened to bf16 (rows past seq_lens
-//    stored as zeros).  Tiles are double buffered with one barrier per tile.
-//    LDS rows keep their 16-byte chunks XOR-swizzled so the operand reads
-//    below are spread over the banks.
+//    that share a KV head share every K/V tile.  One workgroup of 8 waves per
+//    item (two per SIMD), each wave owning 32 rows.  A one-workgroup plan
+//    kernel lists the tiles longest first (their KV length sets their cost),
+//    so in-order dispatch fills the CUs greedily.
+//  * Keys stream in tiles of 32 positions (2 pages) through a ring of 4 LDS
+//    slots.  bf16 tiles go from global memory straight into LDS (buffer_load
+//    ... lds); every page gets a buffer descriptor whose range ends at the
+//    sequence's last valid row, so rows at positions >= seq_lens read as zeros
+//    whatever the pool holds.  fp8 tiles go through registers and are widened
+//    to bf16 (rows past seq_lens stored as zeros), two slots deep.  One
+//    barrier per tile.  LDS rows keep their 16-byte chunks XOR-swizzled so the
+//    operand reads below are spread over the banks.
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from
 //    LDS, B = 16 dims x 32 query rows held in registers): each lane owns 16 keys
-//    of one query row, so a row max needs one cross-lane step.
+//    of one query row, so a row max needs one cross-lane step.  q is
+//    pre-multiplied by the logit scale in log2 units (and rounded to bf16), and
+//    the MFMA chain starts from -m_ref, so scores leave the MFMA as exp2
+//    arguments.
 //  * O^T = V^T . P^T with the same MFMA; V^T comes out of LDS through
 //    ds_read_b64_tr_b16 (gfx950's transposing LDS read); P is rounded to bf16
 //    and the softmax denominator sums the same rounded values.
-//  * Software pipeline: the scores of tile t+1 are computed in the same
-//    iteration as the softmax and PV of tile t, so MFMA and VALU work of
-//    different tiles can overlap within a wave.
+//  * Software pipeline: the scores of tile t+1 and the PV product of tile t-1
+//    are computed in the same iteration as the softmax of tile t, so MFMA and
+//    VALU work of different tiles can overlap within a wave.
 //  * Online softmax in the exp2 domain with a lazy reference max: P is taken
 //    against a reference that moves (and the accumulator is rescaled) only
 //    when some P of a tile could exceed 2^8, which the tile's own row sums
-//    reveal, so the common step is one FMA, one exp2 and half a dot2 per score
-//    and no max.  The scale's sign is moved into q (an exact sign flip), so
-//    maxima can be taken over raw scores.
+//    reveal, so the common step is one exp2, half a conversion and half a
+//    dot2 per score and no max.  The reference starts at the row max of the
+//    first tile.
 //  * Masking selects -inf for keys after the row's position, only on tiles
 //    that cross the diagonal.  The fp8 k scale joins the logit scale, the v
 //    scale the output normalisation.
@@ -143,14 +146,32 @@ struct TileLayout {
 
 typedef const __attribute__((address_space(4))) int64_t* const_i64_ptr;
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const char* base, uint32_t bytes) {
+// Raw buffer descriptor (stride 0, `bytes` addressable bytes) in scalar
+// registers.  The range is uniform too, but may be computed on the VALU (e.g. a
+// clamp): without the readfirstlane it would not be known to be scalar.
+__device__ __forceinline__ u32x4 uniform_rsrc(const char* base, uint32_t bytes) {
   const uint64_t v = reinterpret_cast<uint64_t>(base);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  // the range is uniform too, but may be computed on the VALU (e.g. a clamp):
-  // without the readfirstlane the descriptor would not be known to be scalar
-  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0,
-                                           (int)__builtin_amdgcn_readfirstlane(bytes), kRawBufferWord3);
+  u32x4 r;
+  r.x = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  r.y = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32)) & 0xFFFFu;  // stride 0
+  r.z = __builtin_amdgcn_readfirstlane(bytes);
+  r.w = kRawBufferWord3;
+  return r;
+}
+
+// One 16-byte-per-lane global -> LDS transfer: lane l's 16 bytes at voff go to
+// LDS byte lds + 16 l (buffer_load_dwordx4 ... lds, LDS base in M0).  Written
+// as inline assembly so that the compiler does not track the transfer: its
+// own tracking of LDS-DMA targets is coarse enough to put waits for unrelated
+// transfers before operand reads of ring slots that have long landed.  The
+// kernel orders these transfers itself (wait_vmem, then a barrier).  The
+// s_nop covers the wait states between writing M0 (and, just before, the
+// descriptor's scalar registers from the VALU) and the load reading them.
+__device__ __forceinline__ void dma16(const u32x4& rsrc, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 4\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
 }
 
 struct TileSrc {
@@ -197,15 +218,14 @@ __device__ __forceinline__ void dma_tile(const TileSrc& c, __bf16* tile, int t, 
   const int lp = (t * kKeyTile + wave * M::WROWS) >> 4;  // logical page (negative before position 0)
   int valid = c.L - (lp << 4);  // rows of this page the sequence holds
   valid = lp < 0 || valid < 0 ? 0 : (valid > kPageSize ? kPageSize : valid);
-  const __amdgpu_buffer_rsrc_t r = uniform_rsrc(base + page * c.page_stride, (uint32_t)valid * c.row_stride);
+  const u32x4 r = uniform_rsrc(base + page * c.page_stride, (uint32_t)valid * c.row_stride);
 #pragma unroll
   for (int i = 0; i < M::LOADS; ++i) {
     const int first_row = (wave * M::LOADS + i) * M::ROWS;
     const int row = first_row + lane / TL::NC;
     const int logical = (lane % TL::NC) ^ (IS_V ? TL::swz_v(row) : TL::swz_k(row));
     const uint32_t voff = (uint32_t)(row & 15) * c.row_stride + 16u * logical;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (__attribute__((address_space(3))) void*)(tile + first_row * D), 16, (int)voff, 0, 0, 0);
+    dma16(r, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) __bf16*)(tile + first_row * D), voff);
   }
 }
 
@@ -253,6 +273,17 @@ __device__ __forceinline__ void fp8_store(const Fp8Tile<D, THREADS>& st, __bf16*
       *(u32x4*)(tile + r * D + 8 * ((2 * chunk + 1) ^ sw)) = live ? u32x4{c2.x, c2.y, c3.x, c3.y} : z;
     }
   }
+}
+
+// eight bf16 (one 16-byte chunk) times c, rounded to bf16 (nearest even)
+__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 x, float c) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = x[i];
+    r[i] = pack_bf16x2(__builtin_bit_cast(float, w << 16) * c, __builtin_bit_cast(float, w & 0xFFFF0000u) * c);
+  }
+  return r;
 }
 
 __device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
@@ -339,41 +370,45 @@ void prefill_kernel(AttnParams p) {
   c.L = (int)L;
   c.last_page = (int)((L + 15) >> 4) - 1;
 
-  // logit scale in log2 units; its sign goes into q so maxima are taken on raw scores
+  // logit scale in log2 units (with the fp8 k scale), folded into q: the score
+  // MFMAs then yield exp2 arguments directly
   float cs = p.scale * kLog2e;
   if constexpr (ESZ == 1) cs *= p.k_scale[h];
-  const uint32_t qflip = cs < 0.f ? 0x80008000u : 0u;
-  cs = fabsf(cs);
-  // a zero scale means uniform weights; any tiny scale gives the same exp2 values
-  cs = fmaxf(cs, 1e-30f);
 
   // ---- query operand (B of S^T = K Q^T): lane l holds row (l & 31) of block
   // nb, dims [16 ks + 8 (l >> 5), +8)
   const int qcol = lane & 31, qgrp = lane >> 5;
   bf16x8 qb[NB][NKS];
   int32_t qrel[NB];  // row position - first_pos - 4 qgrp
+  // (called once the first tile fetches are in flight; every lane loads, rows
+  // past the tile from the sequence's first token, so that the loads issue
+  // together rather than one exec-masked load and wait at a time)
+  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int r = wave * 32 * NB + nb * 32 + qcol;
-    const int64_t tok = tok0 + r / G;
-    const bool live = r < tpt * G && tok < tok_end;
-    qrel[nb] = (int32_t)((live ? tok : tok_end - 1) - tok0) - 4 * qgrp;
-    const __bf16* qrow = (const __bf16*)p.q + ((q0 + (live ? tok : 0)) * p.Hq + h * G + r % G) * D;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int r = wave * 32 * NB + nb * 32 + qcol;
+      const int64_t tok = tok0 + r / G;
+      const bool live = r < tpt * G && tok < tok_end;
+      qrel[nb] = (int32_t)((live ? tok : tok_end - 1) - tok0) - 4 * qgrp;
+      const __bf16* qrow = (const __bf16*)p.q + ((q0 + (live ? tok : 0)) * p.Hq + h * G + r % G) * D;
+      u32x4 raw[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (live) x = *(const u32x4*)(qrow + 16 * ks + 8 * qgrp) ^ qflip;
-      if constexpr (NB > 1) {
-        // park the query operand in AGPRs (MFMA reads A/B from either file),
-        // leaving the VGPRs to the softmax and the LDS operand pipeline
-        u32x4 xa;
-        asm("" : "=a"(xa) : "0"(x));
-        qb[nb][ks] = __builtin_bit_cast(bf16x8, xa);
-      } else {
-        qb[nb][ks] = __builtin_bit_cast(bf16x8, x);
+      for (int ks = 0; ks < NKS; ++ks) raw[ks] = *(const u32x4*)(qrow + 16 * ks + 8 * qgrp);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const u32x4 x = live ? scale_bf16x8(raw[ks], cs) : u32x4{0u, 0u, 0u, 0u};
+        if constexpr (NB > 1) {
+          // park the query operand in AGPRs (MFMA reads A/B from either file),
+          // leaving the VGPRs to the softmax and the LDS operand pipeline
+          u32x4 xa;
+          asm("" : "=a"(xa) : "0"(x));
+          qb[nb][ks] = __builtin_bit_cast(bf16x8, xa);
+        } else {
+          qb[nb][ks] = __builtin_bit_cast(bf16x8, x);
+        }
       }
     }
-  }
+  };
 
   // ---- per-lane LDS byte offsets inside a tile.  The XOR swizzles act on
   // bits the k-step (K) or dim-block (V) index enters by XOR, so one base per
@@ -394,17 +429,20 @@ void prefill_kernel(AttnParams p) {
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[d][nb][i] = 0.f;
-  // reference max (log2 units); finite so that exp2(-inf - m_ref) stays 0
-  float m_ref[NB];
+  // -m_ref (the reference max, log2 units) in all 16 elements: the score MFMAs
+  // accumulate onto it, so a score leaves the MFMA as its exp2 argument
+  f32x16 cm[NB];
   float l_run[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    m_ref[nb] = -1e30f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cm[nb][i] = 0.f;
     l_run[nb] = 0.f;
   }
 
   // S^T of the K tile in ring slot `slot`: s[nb][i] = score of key 8 (i / 4) +
-  // 4 qgrp + i % 4 of the tile and query row 32 nb + qcol
+  // 4 qgrp + i % 4 of the tile and query row 32 nb + qcol, in log2 units,
+  // minus m_ref
   auto read_k = [&](int slot, bf16x8 (&ka)[NKS]) __attribute__((always_inline)) {
     const char* k = sk[slot];
 #pragma unroll
@@ -412,9 +450,7 @@ void prefill_kernel(AttnParams p) {
   };
   auto scores = [&](const bf16x8 (&ka)[NKS], f32x16 (&s)[NB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[nb][i] = 0.f;
+    for (int nb = 0; nb < NB; ++nb) s[nb] = cm[nb];
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -438,9 +474,7 @@ void prefill_kernel(AttnParams p) {
   auto scores_pv = [&](const bf16x8 (&ka)[NKS], const bf16x8 (&va)[NDB][2], f32x16 (&s)[NB],
                        const bf16x8 (&pb)[2][NB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[nb][i] = 0.f;
+    for (int nb = 0; nb < NB; ++nb) s[nb] = cm[nb];
     static_assert(NKS == 2 * NDB, "one PV MFMA per score k-step");
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -460,21 +494,20 @@ void prefill_kernel(AttnParams p) {
         for (int nb = 0; nb < NB; ++nb) acc[d][nb] = mfma32(va[d][hh], pb[hh][nb], acc[d][nb]);
   };
 
-  // P(t) = exp2(s * cs - m_ref) from the raw scores of tile t, rounded to
-  // bf16; lt = this lane's share of the tile's row sums of the rounded P.
+  // P(t) = exp2(s) from the scores of tile t, rounded to bf16; lt = this
+  // lane's share of the tile's row sums of the rounded P.
   auto exps = [&](const f32x16 (&s)[NB], bf16x8 (&pb)[2][NB], float (&lt)[NB]) __attribute__((always_inline)) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const float neg_m = -m_ref[nb];
       float l = 0.f;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         u32x4 w;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][8 * hh + 2 * q], cs, neg_m));
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][8 * hh + 2 * q + 1], cs, neg_m));
+          const float a = __builtin_amdgcn_exp2f(s[nb][8 * hh + 2 * q]);
+          const float e = __builtin_amdgcn_exp2f(s[nb][8 * hh + 2 * q + 1]);
           const uint32_t pk = pack_bf16x2(a, e);
           w[q] = pk;
           l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l, false);
@@ -485,23 +518,27 @@ void prefill_kernel(AttnParams p) {
     }
   };
 
+  // keys of tile t after the row's position -> -inf
+  auto apply_mask = [&](int t, f32x16 (&s)[NB]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int32_t lim = (int32_t)(first_pos - (int64_t)t * kKeyTile) + qrel[nb];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[nb][i] = 8 * (i >> 2) + (i & 3) > lim ? -INFINITY : s[nb][i];
+    }
+  };
+
   // Softmax of tile t with a lazy reference max m_ref.  The common step never
   // computes a max: P is taken against the current reference and, as long as
-  // no lane's partial row sum exceeds kLazyBound (so no single P does),
-  // the reference stands.  Otherwise (always on the first tile, where m_ref
-  // starts at -1e30) the reference moves to the row max, P is recomputed and
-  // alpha = exp2(m_old - m_new) is returned for the accumulator; the function
-  // then returns true.
-  auto softmax = [&](auto mask_c, int t, f32x16 (&s)[NB], bf16x8 (&pb)[2][NB], float (&alpha)[NB]) __attribute__((always_inline)) {
+  // no lane's partial row sum exceeds kLazyBound (so no single P does), the
+  // reference stands.  Otherwise the reference moves up to the row max, by
+  // dm >= 0: the scores of tiles t and t+1 (s_next, already computed against
+  // the old reference) and cm move down by dm, P is recomputed and alpha =
+  // exp2(-dm) is returned for the accumulator; the function then returns true.
+  auto softmax = [&](auto mask_c, int t, f32x16 (&s)[NB], f32x16 (&s_next)[NB], bf16x8 (&pb)[2][NB],
+                     float (&alpha)[NB]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
-    if constexpr (MASK) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int32_t lim = (int32_t)(first_pos - (int64_t)t * kKeyTile) + qrel[nb];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s[nb][i] = 8 * (i >> 2) + (i & 3) > lim ? -INFINITY : s[nb][i];
-      }
-    }
+    if constexpr (MASK) apply_mask(t, s);
     float lt[NB];
     exps(s, pb, lt);
     bool over = false;
@@ -525,11 +562,13 @@ void prefill_kernel(AttnParams p) {
         float mx = __builtin_fmaxf(s[nb][0], s[nb][1]);
 #pragma unroll
         for (int i = 2; i < 16; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[nb][i], s[nb][i + 1]));
-        mx = max_pair(mx) * cs;  // -inf if every key of the row is masked in this tile
-        const float m_new = __builtin_fmaxf(m_ref[nb], mx);
-        alpha[nb] = m_new == m_ref[nb] ? 1.0f : __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
-        m_ref[nb] = m_new;
+        // (a row the tile masks entirely has max -inf and keeps its reference)
+        const float dm = __builtin_fmaxf(max_pair(mx), 0.f);
+        alpha[nb] = __builtin_amdgcn_exp2f(-dm);
         l_run[nb] *= alpha[nb];
+        s[nb] -= dm;
+        s_next[nb] -= dm;
+        cm[nb] -= dm;
       }
       exps(s, pb, lt);
     }
@@ -584,8 +623,10 @@ void prefill_kernel(AttnParams p) {
     page_q[2] = wave_page<D, WAVES>(c, NS - 2, wave);
     page_q[1] = wave_page<D, WAVES>(c, NS - 1, wave);
     page_q[0] = wave_page<D, WAVES>(c, NS, wave);
+    load_q();
     wait_vmem<LOADS_AFTER + Dma<D, WAVES>::LOADS>();  // K(0) and K(1) landed
   } else {
+    load_q();
     fp8_fetch<D, THREADS>(fk, c, c.kbase, 0, tid);
     fp8_store<D, THREADS, false>(fk, (__bf16*)sk[0], 0, L, tid);
     fp8_fetch<D, THREADS>(fk, c, c.kbase, 1, tid);
@@ -593,11 +634,23 @@ void prefill_kernel(AttnParams p) {
     for (int i = tid; i < TB / 16; i += THREADS) ((u32x4*)sv[1])[i] = u32x4{0u, 0u, 0u, 0u};
   }
   barrier_lds();
+  // scores of tile 0 (cm = 0: raw log2-unit logits); the reference starts at
+  // their row max, which is finite since every row sees position 0
   f32x16 s_cur[NB];
   {
     bf16x8 ka[NKS];
     read_k(0, ka);
     scores(ka, s_cur);
+    if (t_diag == 0) apply_mask(0, s_cur);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float mx = __builtin_fmaxf(s_cur[nb][0], s_cur[nb][1]);
+#pragma unroll
+      for (int i = 2; i < 16; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s_cur[nb][i], s_cur[nb][i + 1]));
+      const float m0 = max_pair(mx);
+      s_cur[nb] -= m0;
+      cm[nb] -= m0;
+    }
   }
 
   // Iteration t, ring position R = t % NS (a compile-time constant at every
@@ -629,7 +682,7 @@ void prefill_kernel(AttnParams p) {
     scores_pv(ka, va, s_next, pb_prev);
     float alpha[NB];
     bf16x8 pb[2][NB];
-    if (softmax(mask_c, t, s_cur, pb, alpha)) rescale(alpha);
+    if (softmax(mask_c, t, s_cur, s_next, pb, alpha)) rescale(alpha);
     if constexpr (ESZ == 2) {
       wait_vmem<LOADS_AFTER>();
       // the next K page id, loaded just before the barrier that waits for it
