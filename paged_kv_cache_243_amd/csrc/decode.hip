@@ -83,10 +83,11 @@ struct KGeom {
   static constexpr int IPP = NKI / 2;       // ... per page
   static constexpr int NC = D / 8;          // 16-byte bf16 chunks per LDS row
   // chunk swizzles.  K: the 16 rows an MFMA operand read touches land in 16
-  // different bank groups.  V: the 4 rows x 2 chunks a transposing read
-  // touches land in 8 different bank groups.
+  // different bank groups.  V: one pass of a transposing read serves 32 lanes
+  // (256 bytes, all 64 banks) and touches 8 rows x 2 chunks, which land in 16
+  // different bank groups.
   __device__ static int swz(int row) { return (row / (16 / NC)) % NC; }
-  __device__ static int swz_v(int row) { return (2 * ((row / (16 / NC)) % 4)) % NC; }
+  __device__ static int swz_v(int row) { return (2 * ((row / (16 / NC)) % (NC / 2))) % NC; }
 };
 
 // Raw K and V bytes of one unit for one KV head, as one lane holds them

@@ -140,8 +140,10 @@ struct TileLayout {
   static constexpr int NC = D / 8;  // 16-byte chunks per bf16 row
   // K: the rows one 32-lane operand read touches land on distinct chunk slots
   __device__ static int swz_k(int row) { return (row / (16 / NC)) % NC; }
-  // V: the 4 rows x 2 chunks one transposing read touches land on distinct slots
-  __device__ static int swz_v(int row) { return (2 * ((row / (16 / NC)) % 4)) % NC; }
+  // V: one pass of a transposing read serves 32 lanes (256 bytes, all 64 banks)
+  // and touches 4 rows x 4 chunks; each row's 4 chunks go to their own group
+  // of 4 chunk slots, so the pass hits every bank once
+  __device__ static int swz_v(int row) { return (4 * ((row / (16 / NC)) % (NC / 4))) % NC; }
 };
 
 typedef const __attribute__((address_space(4))) int64_t* const_i64_ptr;
