@@ -25,10 +25,7 @@
 //    operand reads below are spread over the banks.
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from
 //    LDS, B = 16 dims x 32 query rows held in registers): each lane owns 16 keys
-//    of one query row, so a row max needs one cross-lane step.  q is
-//    pre-multiplied by the logit scale in log2 units (and rounded to bf16), and
-//    the MFMA chain starts from -m_ref, so scores leave the MFMA as exp2
-//    arguments.
+//    of one query row, so a row max needs one cross-lane step.
 //  * O^T = V^T . P^T with the same MFMA; V^T comes out of LDS through
 //    ds_read_b64_tr_b16 (gfx950's transposing LDS read); P is rounded to bf16
 //    and the softmax denominator sums the same rounded values.
@@ -38,9 +35,9 @@
 //  * Online softmax in the exp2 domain with a lazy reference max: P is taken
 //    against a reference that moves (and the accumulator is rescaled) only
 //    when some P of a tile could exceed 2^8, which the tile's own row sums
-//    reveal, so the common step is one exp2, half a conversion and half a
-//    dot2 per score and no max.  The reference starts at the row max of the
-//    first tile.
+//    reveal, so the common step is one FMA, one exp2, half a conversion and
+//    half a dot2 per score and no max.  The scale's sign is moved into q (an
+//    exact sign flip), so maxima can be taken over raw scores.
 //  * Masking selects -inf for keys after the row's position, only on tiles
 //    that cross the diagonal.  The fp8 k scale joins the logit scale, the v
 //    scale the output normalisation.
@@ -277,17 +274,6 @@ __device__ __forceinline__ void fp8_store(const Fp8Tile<D, THREADS>& st, __bf16*
   }
 }
 
-// eight bf16 (one 16-byte chunk) times c, rounded to bf16 (nearest even)
-__device__ __forceinline__ u32x4 scale_bf16x8(u32x4 x, float c) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w = x[i];
-    r[i] = pack_bf16x2(__builtin_bit_cast(float, w << 16) * c, __builtin_bit_cast(float, w & 0xFFFF0000u) * c);
-  }
-  return r;
-}
-
 __device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
       (__attribute__((address_space(3))) s16x4*)(const_cast<char*>(p)));
@@ -372,10 +358,13 @@ void prefill_kernel(AttnParams p) {
   c.L = (int)L;
   c.last_page = (int)((L + 15) >> 4) - 1;
 
-  // logit scale in log2 units (with the fp8 k scale), folded into q: the score
-  // MFMAs then yield exp2 arguments directly
+  // logit scale in log2 units; its sign goes into q so maxima are taken on raw scores
   float cs = p.scale * kLog2e;
   if constexpr (ESZ == 1) cs *= p.k_scale[h];
+  const uint32_t qflip = cs < 0.f ? 0x80008000u : 0u;
+  cs = fabsf(cs);
+  // a zero scale means uniform weights; any tiny scale gives the same exp2 values
+  cs = fmaxf(cs, 1e-30f);
 
   // ---- query operand (B of S^T = K Q^T): lane l holds row (l & 31) of block
   // nb, dims [16 ks + 8 (l >> 5), +8)
@@ -398,7 +387,7 @@ void prefill_kernel(AttnParams p) {
       for (int ks = 0; ks < NKS; ++ks) raw[ks] = *(const u32x4*)(qrow + 16 * ks + 8 * qgrp);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const u32x4 x = live ? scale_bf16x8(raw[ks], cs) : u32x4{0u, 0u, 0u, 0u};
+        const u32x4 x = live ? (raw[ks] ^ qflip) : u32x4{0u, 0u, 0u, 0u};
         if constexpr (NB > 1) {
           // park the query operand in AGPRs (MFMA reads A/B from either file),
           // leaving the VGPRs to the softmax and the LDS operand pipeline
@@ -431,20 +420,17 @@ void prefill_kernel(AttnParams p) {
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[d][nb][i] = 0.f;
-  // -m_ref (the reference max, log2 units) in all 16 elements: the score MFMAs
-  // accumulate onto it, so a score leaves the MFMA as its exp2 argument
-  f32x16 cm[NB];
+  // reference max (log2 units); finite so that exp2(-inf - m_ref) stays 0
+  float m_ref[NB];
   float l_run[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) cm[nb][i] = 0.f;
+    m_ref[nb] = -1e30f;
     l_run[nb] = 0.f;
   }
 
   // S^T of the K tile in ring slot `slot`: s[nb][i] = score of key 8 (i / 4) +
-  // 4 qgrp + i % 4 of the tile and query row 32 nb + qcol, in log2 units,
-  // minus m_ref
+  // 4 qgrp + i % 4 of the tile and query row 32 nb + qcol
   auto read_k = [&](int slot, bf16x8 (&ka)[NKS]) __attribute__((always_inline)) {
     const char* k = sk[slot];
 #pragma unroll
@@ -452,7 +438,9 @@ void prefill_kernel(AttnParams p) {
   };
   auto scores = [&](const bf16x8 (&ka)[NKS], f32x16 (&s)[NB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = cm[nb];
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[nb][i] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
@@ -476,7 +464,9 @@ void prefill_kernel(AttnParams p) {
   auto scores_pv = [&](const bf16x8 (&ka)[NKS], const bf16x8 (&va)[NDB][2], f32x16 (&s)[NB],
                        const bf16x8 (&pb)[2][NB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb] = cm[nb];
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[nb][i] = 0.f;
     static_assert(NKS == 2 * NDB, "one PV MFMA per score k-step");
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
@@ -496,20 +486,21 @@ void prefill_kernel(AttnParams p) {
         for (int nb = 0; nb < NB; ++nb) acc[d][nb] = mfma32(va[d][hh], pb[hh][nb], acc[d][nb]);
   };
 
-  // P(t) = exp2(s) from the scores of tile t, rounded to bf16; lt = this
-  // lane's share of the tile's row sums of the rounded P.
+  // P(t) = exp2(s * cs - m_ref) from the raw scores of tile t, rounded to
+  // bf16; lt = this lane's share of the tile's row sums of the rounded P.
   auto exps = [&](const f32x16 (&s)[NB], bf16x8 (&pb)[2][NB], float (&lt)[NB]) __attribute__((always_inline)) {
     const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
+      const float neg_m = -m_ref[nb];
       float l = 0.f;
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         u32x4 w;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float a = __builtin_amdgcn_exp2f(s[nb][8 * hh + 2 * q]);
-          const float e = __builtin_amdgcn_exp2f(s[nb][8 * hh + 2 * q + 1]);
+          const float a = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][8 * hh + 2 * q], cs, neg_m));
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[nb][8 * hh + 2 * q + 1], cs, neg_m));
           const uint32_t pk = pack_bf16x2(a, e);
           w[q] = pk;
           l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), ones, l, false);
@@ -520,27 +511,23 @@ void prefill_kernel(AttnParams p) {
     }
   };
 
-  // keys of tile t after the row's position -> -inf
-  auto apply_mask = [&](int t, f32x16 (&s)[NB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int32_t lim = (int32_t)(first_pos - (int64_t)t * kKeyTile) + qrel[nb];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[nb][i] = 8 * (i >> 2) + (i & 3) > lim ? -INFINITY : s[nb][i];
-    }
-  };
-
   // Softmax of tile t with a lazy reference max m_ref.  The common step never
   // computes a max: P is taken against the current reference and, as long as
-  // no lane's partial row sum exceeds kLazyBound (so no single P does), the
-  // reference stands.  Otherwise the reference moves up to the row max, by
-  // dm >= 0: the scores of tiles t and t+1 (s_next, already computed against
-  // the old reference) and cm move down by dm, P is recomputed and alpha =
-  // exp2(-dm) is returned for the accumulator; the function then returns true.
-  auto softmax = [&](auto mask_c, int t, f32x16 (&s)[NB], f32x16 (&s_next)[NB], bf16x8 (&pb)[2][NB],
-                     float (&alpha)[NB]) __attribute__((always_inline)) {
+  // no lane's partial row sum exceeds kLazyBound (so no single P does),
+  // the reference stands.  Otherwise (always on the first tile, where m_ref
+  // starts at -1e30) the reference moves to the row max, P is recomputed and
+  // alpha = exp2(m_old - m_new) is returned for the accumulator; the function
+  // then returns true.
+  auto softmax = [&](auto mask_c, int t, f32x16 (&s)[NB], bf16x8 (&pb)[2][NB], float (&alpha)[NB]) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_c)::value;
-    if constexpr (MASK) apply_mask(t, s);
+    if constexpr (MASK) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int32_t lim = (int32_t)(first_pos - (int64_t)t * kKeyTile) + qrel[nb];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) s[nb][i] = 8 * (i >> 2) + (i & 3) > lim ? -INFINITY : s[nb][i];
+      }
+    }
     float lt[NB];
     exps(s, pb, lt);
     bool over = false;
@@ -564,13 +551,11 @@ void prefill_kernel(AttnParams p) {
         float mx = __builtin_fmaxf(s[nb][0], s[nb][1]);
 #pragma unroll
         for (int i = 2; i < 16; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s[nb][i], s[nb][i + 1]));
-        // (a row the tile masks entirely has max -inf and keeps its reference)
-        const float dm = __builtin_fmaxf(max_pair(mx), 0.f);
-        alpha[nb] = __builtin_amdgcn_exp2f(-dm);
+        mx = max_pair(mx) * cs;  // -inf if every key of the row is masked in this tile
+        const float m_new = __builtin_fmaxf(m_ref[nb], mx);
+        alpha[nb] = m_new == m_ref[nb] ? 1.0f : __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
+        m_ref[nb] = m_new;
         l_run[nb] *= alpha[nb];
-        s[nb] -= dm;
-        s_next[nb] -= dm;
-        cm[nb] -= dm;
       }
       exps(s, pb, lt);
     }
@@ -636,23 +621,11 @@ void prefill_kernel(AttnParams p) {
     for (int i = tid; i < TB / 16; i += THREADS) ((u32x4*)sv[1])[i] = u32x4{0u, 0u, 0u, 0u};
   }
   barrier_lds();
-  // scores of tile 0 (cm = 0: raw log2-unit logits); the reference starts at
-  // their row max, which is finite since every row sees position 0
   f32x16 s_cur[NB];
   {
     bf16x8 ka[NKS];
     read_k(0, ka);
     scores(ka, s_cur);
-    if (t_diag == 0) apply_mask(0, s_cur);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float mx = __builtin_fmaxf(s_cur[nb][0], s_cur[nb][1]);
-#pragma unroll
-      for (int i = 2; i < 16; i += 2) mx = __builtin_fmaxf(mx, __builtin_fmaxf(s_cur[nb][i], s_cur[nb][i + 1]));
-      const float m0 = max_pair(mx);
-      s_cur[nb] -= m0;
-      cm[nb] -= m0;
-    }
   }
 
   // Iteration t, ring position R = t % NS (a compile-time constant at every
@@ -684,7 +657,7 @@ void prefill_kernel(AttnParams p) {
     scores_pv(ka, va, s_next, pb_prev);
     float alpha[NB];
     bf16x8 pb[2][NB];
-    if (softmax(mask_c, t, s_cur, s_next, pb, alpha)) rescale(alpha);
+    if (softmax(mask_c, t, s_cur, pb, alpha)) rescale(alpha);
     if constexpr (ESZ == 2) {
       wait_vmem<LOADS_AFTER>();
       // the next K page id, loaded just before the barrier that waits for it

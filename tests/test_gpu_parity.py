@@ -175,3 +175,26 @@ def test_decode_batch_with_sequences_without_query_rows(gpu):
     kp, vp, out = gpu_step(gpu, w2, split_tokens=64)
     _, _, ref = H.oracle_step(w2)
     assert_close(out, ref, "bf16", "decode with empty spans")
+
+
+@pytest.mark.parametrize("cid", [2, 3])
+def test_logits_growing_along_the_sequence(gpu, cid):
+    """Keys scaled up with their position (x1 .. x4), so a row's maximum keeps
+    rising from tile to tile: the running reference of the softmax has to move
+    many times after the first tile.  GPU and oracle see the same pools."""
+    note(f"growing logits config {cid}")
+    w = W.generate(W.SMALL[cid], DEV, seed=31)
+    kp, vp = gpu_write(gpu, w)
+    okp, ovp = H.oracle_write(w)
+    k = torch.from_numpy(okp.view(np.int16).copy()).view(torch.bfloat16).float()
+    bt, lens = S(w.block_table), S(w.seq_lens)
+    for b in range(w.cfg.batch):
+        L = int(lens[b])
+        for p in range(L):
+            k[int(bt[b, p // 16]), p % 16] *= 1.0 + 3.0 * p / L
+    kb = k.to(torch.bfloat16)
+    okp = kb.view(torch.int16).numpy().view(okp.dtype).reshape(okp.shape).copy()
+    kp = kb.to(DEV)
+    out = gpu_attend(gpu, w, kp, vp)
+    ref = H.oracle_attend(w, okp, ovp)
+    assert_close(out, ref, w.kv_dtype, f"growing logits config {cid}")
