@@ -34,7 +34,8 @@
  *    that exceed the block table) are not checked by the fast path; call
  *    paged_validate_metadata to find them.
  *  - Supported geometry: page_size 16; head_dim 64 or 128; Hq a multiple of
- *    Hkv with Hq / Hkv <= 16; at most 4096 sequences per decode call; for
+ *    Hkv with Hq / Hkv <= 16; at most 4096 sequences per decode call, with
+ *    B * ceil(max_blocks * 16 / 32) < 2^31; for
  *    calls with several query rows per sequence, block_table rows of at most
  *    2^31 - 1 positions and at most 65535 query tiles of 256 / (Hq / Hkv)
  *    rows (ceil(T / tile) <= 65535).  Anything else is PKV_ERR_UNSUPPORTED;

@@ -288,7 +288,8 @@ __device__ __forceinline__ void consume_unit(UnitRegs<ESZ, D>& u, __bf16* __rest
 // division-free; owner(u) is the workgroup whose range holds unit u.
 struct Partition {
   int32_t q, r;
-  __device__ Partition(int64_t U, int64_t W) : q((int32_t)(U / W)), r((int32_t)(U % W)) {}
+  // (U < 2^31 units, W <= the grid size: 32-bit division)
+  __device__ Partition(int32_t U, int32_t W) : q((int32_t)((uint32_t)U / (uint32_t)W)), r((int32_t)((uint32_t)U % (uint32_t)W)) {}
   __device__ int32_t start(int32_t w) const { return w * q + min(w, r); }
   __device__ int32_t owner(int32_t u) const {
     const int32_t big = r * (q + 1);  // units held by the q+1-unit ranges
@@ -348,7 +349,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   const int W = gridDim.x, wg = blockIdx.x;
   if (wg == 0)
     for (int b = tid; b <= B; b += nthreads) p.ws_cum[b] = s_cum[b];
-  const int64_t U = s_cum[B];
+  const int32_t U = s_cum[B];
   if (U == 0) return;
   const Partition part(U, W);
   const int32_t u0 = part.start(wg);
@@ -479,11 +480,12 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
   constexpr int CHUNK = 8;
   const int hq = blockIdx.x, b = blockIdx.y;
   const int lane = threadIdx.x;
-  const int64_t q_row = p.qsl[b];
-  if (p.qsl[b + 1] == q_row) return;
-  const int32_t cb = p.ws_cum[b], ce = p.ws_cum[b + 1];
-  if (ce <= cb) return;
-  const Partition part(p.ws_cum[p.B], p.grid_parts);
+  // every index this wave needs, loaded together (one memory round trip before
+  // the partials' own)
+  const int64_t q_row = p.qsl[b], q_end = p.qsl[b + 1];
+  const int32_t cb = p.ws_cum[b], ce = p.ws_cum[b + 1], units = p.ws_cum[p.B];
+  if (q_end == q_row || ce <= cb || units <= 0) return;
+  const Partition part(units, p.grid_parts);
   const int32_t wa = part.owner(cb), wz = part.owner(ce - 1);
   if (wa == wz) return;  // written directly by decode_kernel
   const f32x2* ml = (const f32x2*)p.ws_ml;

@@ -181,6 +181,8 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
   } else if (max_q == 1) {
     plan.kernel = AttnPlan::kDecode;
     if (B > pkv::kDecodeMaxSeqs) return PKV_ERR_UNSUPPORTED;
+    // the decode kernel counts 32-position units of all sequences in 32 bits
+    if (B * ((max_blocks * kPageSize + 31) / 32) > INT32_MAX) return PKV_ERR_UNSUPPORTED;
     p.split_tokens = split;
     plan.workspace = pkv::decode_workspace_bytes(B, (int)Hq, (int)D);
   } else {
