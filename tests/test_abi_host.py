@@ -161,6 +161,9 @@ ATTN_CASES = {
     "too many decode sequences": (dict(q=T([9000, 32, 128], B.PKV_BF16), out=T([9000, 32, 128], B.PKV_BF16),
                                        bt=T([9000, 8], B.PKV_I64), sl=T([9000], B.PKV_I64),
                                        qsl=T([9001], B.PKV_I64)), -4),
+    "decode unit count past 2^31": (dict(q=T([4096, 32, 128], B.PKV_BF16), out=T([4096, 32, 128], B.PKV_BF16),
+                                         bt=T([4096, 1 << 20], B.PKV_I64), sl=T([4096], B.PKV_I64),
+                                         qsl=T([4097], B.PKV_I64)), -4),
     "small workspace": (dict(bt=T([4, 256], B.PKV_I64),
                              opts=opts(max_query_len=1, split_tokens=256, workspace=FAKE, workspace_bytes=64)), -6),
 }
