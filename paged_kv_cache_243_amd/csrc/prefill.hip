@@ -318,15 +318,13 @@ void prefill_kernel(AttnParams p) {
   constexpr int THREADS = 64 * WAVES;
   constexpr int NKS = D / 16;              // score MFMA k-steps
   constexpr int NDB = D / 32;              // output dim blocks
-  constexpr int NS = ESZ == 2 ? 4 : 2;     // K/V ring depth
+  // K/V ring depth: bf16 tiles arrive by DMA two at a time, one workgroup
+  // barrier per two tiles; fp8 tiles go through registers, one per barrier
+  constexpr int NS = ESZ == 2 ? 6 : 2;
   constexpr int TB = kKeyTile * D * 2;     // bytes per LDS tile
   using TL = TileLayout<D>;
-  // one LDS variable per ring slot: the compiler tells LDS-DMA targets apart
-  // by variable, so reads of one slot never wait for fetches into another
-  __shared__ __attribute__((aligned(16))) char sk0[TB], sk1[TB], sk2[NS > 2 ? TB : 16], sk3[NS > 2 ? TB : 16];
-  __shared__ __attribute__((aligned(16))) char sv0[TB], sv1[TB], sv2[NS > 2 ? TB : 16], sv3[NS > 2 ? TB : 16];
-  char* const sk[4] = {sk0, sk1, sk2, sk3};
-  char* const sv[4] = {sv0, sv1, sv2, sv3};
+  __shared__ __attribute__((aligned(16))) char sk[NS][TB];
+  __shared__ __attribute__((aligned(16))) char sv[NS][TB];
 
   const int rank = (int)(blockIdx.x / (unsigned)p.Hkv), h = (int)(blockIdx.x % (unsigned)p.Hkv);
   if (rank >= p.ws_plan[0]) return;
@@ -477,14 +475,6 @@ void prefill_kernel(AttnParams p) {
       for (int nb = 0; nb < NB; ++nb) acc[d][nb] = mfma32(va[d][hh], pb[hh][nb], acc[d][nb]);
     }
   };
-  auto pv = [&](const bf16x8 (&va)[NDB][2], const bf16x8 (&pb)[2][NB]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int d = 0; d < NDB; ++d)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[d][nb] = mfma32(va[d][hh], pb[hh][nb], acc[d][nb]);
-  };
 
   // P(t) = exp2(s * cs - m_ref) from the raw scores of tile t, rounded to
   // bf16; lt = this lane's share of the tile's row sums of the rounded P.
@@ -576,78 +566,32 @@ void prefill_kernel(AttnParams p) {
       }
   };
 
-  // ---- tile fetches.  Tile j lives in ring slot j % NS.  bf16: DMA issued
-  // for "virtual iteration" u (K(u+NS), V(u+NS-2)), so that every iteration
-  // issues the same number of loads and vmcnt(LOADS_AFTER) leaves exactly the
-  // tiles the next iteration needs in flight.
-  constexpr int LOADS_AFTER = (NS - 2) * 2 * Dma<D, WAVES>::LOADS;
-  auto issue = [&](int u, int slot_k, int slot_v, int64_t page_k, int64_t page_v) __attribute__((always_inline)) {
-    dma_tile<D, WAVES, false>(c, (__bf16*)sk[slot_k], u + NS, page_k, wave, lane);
-    dma_tile<D, WAVES, true>(c, (__bf16*)sv[slot_v], u + NS - 2, page_v, wave, lane);
-  };
-  // Page ids of this wave's rows, K(j) and V(j) sharing them: the V fetch of
-  // an iteration reuses the id its K fetch used two iterations earlier, and
-  // the next K id is loaded one iteration ahead.
-  int64_t page_q[3] = {0, 0, 0};  // K page of this, the previous and the one before
-  Fp8Tile<D, THREADS> fk, fv;     // fp8 staging: iteration t fetches K(t+2) and V(t)
+  // ---- tile fetches.  Tile j lives in ring slot j % NS of its ring.
+  using DM = Dma<D, WAVES>;
+  // Page ids of this wave's rows; V(j) reuses the id fetched for K(j).
+  int64_t page_k[2] = {0, 0}, page_v[2] = {0, 0};
+  Fp8Tile<D, THREADS> fk, fv;  // fp8 staging: iteration t fetches K(t+2) and V(t)
   auto store8 = [&](int t, int slot) __attribute__((always_inline)) {
     fp8_store<D, THREADS, false>(fk, (__bf16*)sk[slot], t + 2, L, tid);
     fp8_store<D, THREADS, true>(fv, (__bf16*)sv[slot], t, L, tid);
   };
 
-  // ---- prologue: K(0) and K(1) resident, V(-2) and V(-1) zero (the PV of
-  // the first iteration multiplies V(-1) by P(-1) = 0), later tiles in flight
   bf16x8 pb_prev[2][NB];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) pb_prev[hh][nb] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-  if constexpr (ESZ == 2) {
-#pragma unroll
-    for (int u = -NS; u < 0; ++u)
-      issue(u, (u + NS) % NS, (u + 2 * NS - 2) % NS, wave_page<D, WAVES>(c, u + NS, wave),
-            wave_page<D, WAVES>(c, u + NS - 2, wave));
-    page_q[2] = wave_page<D, WAVES>(c, NS - 2, wave);
-    page_q[1] = wave_page<D, WAVES>(c, NS - 1, wave);
-    page_q[0] = wave_page<D, WAVES>(c, NS, wave);
-    load_q();
-    wait_vmem<LOADS_AFTER + Dma<D, WAVES>::LOADS>();  // K(0) and K(1) landed
-  } else {
-    load_q();
-    fp8_fetch<D, THREADS>(fk, c, c.kbase, 0, tid);
-    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[0], 0, L, tid);
-    fp8_fetch<D, THREADS>(fk, c, c.kbase, 1, tid);
-    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[1], 1, L, tid);
-    for (int i = tid; i < TB / 16; i += THREADS) ((u32x4*)sv[1])[i] = u32x4{0u, 0u, 0u, 0u};
-  }
-  barrier_lds();
   f32x16 s_cur[NB];
-  {
-    bf16x8 ka[NKS];
-    read_k(0, ka);
-    scores(ka, s_cur);
-  }
 
-  // Iteration t, ring position R = t % NS (a compile-time constant at every
-  // call, so every LDS access names its slot variable).  At the top (after the
-  // barrier) K(t+1) and V(t-1) are resident and no wave still reads K(t) or
-  // V(t-2), whose slots the iteration's fetches overwrite.  The MFMAs of the
-  // iteration (scores of tile t+1, P(t-1) V(t-1) into the output) do not
-  // depend on its VALU work (the softmax of tile t), and the two are
-  // interleaved instruction by instruction so that they co-execute.  Tiles
-  // past the sequence are zero filled and fully masked, so iterations past the
-  // last tile add nothing.
-  auto iteration = [&](auto mask_c, auto r_c, int t) __attribute__((always_inline)) {
+  // One iteration's compute for tile t in ring position R = t % NS (a
+  // compile-time constant, so every LDS address is a base plus an immediate):
+  // K(t+1) and V(t-1) are resident.  The MFMAs (scores of tile t+1, P(t-1)
+  // V(t-1) into the output) do not depend on the VALU work (the softmax of
+  // tile t), and the two are interleaved instruction by instruction so that
+  // they co-execute.  Tiles past the sequence are zero filled and fully
+  // masked, so iterations past the last tile add nothing.
+  auto compute = [&](auto mask_c, auto r_c, int t) __attribute__((always_inline)) {
     constexpr int R = decltype(r_c)::value;
-    barrier_lds();
-    if constexpr (ESZ == 2) {
-      issue(t, R, (R + NS - 2) % NS, page_q[0], page_q[2]);
-      page_q[2] = page_q[1];
-      page_q[1] = page_q[0];
-    } else {
-      fp8_fetch<D, THREADS>(fk, c, c.kbase, t + 2, tid);
-      fp8_fetch<D, THREADS>(fv, c, c.vbase, t, tid);
-    }
     bf16x8 ka[NKS], va[NDB][2];
     read_k((R + 1) % NS, ka);
     read_v((R + NS - 1) % NS, va);
@@ -658,16 +602,6 @@ void prefill_kernel(AttnParams p) {
     float alpha[NB];
     bf16x8 pb[2][NB];
     if (softmax(mask_c, t, s_cur, pb, alpha)) rescale(alpha);
-    if constexpr (ESZ == 2) {
-      wait_vmem<LOADS_AFTER>();
-      // the next K page id, loaded just before the barrier that waits for it
-      // anyway (an earlier scalar load would force a full LDS drain at the
-      // first operand wait after it)
-      __builtin_amdgcn_sched_barrier(0);
-      page_q[0] = wave_page<D, WAVES>(c, t + NS + 1, wave);
-    } else {
-      store8(t, R);
-    }
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       s_cur[nb] = s_next[nb];
@@ -675,22 +609,120 @@ void prefill_kernel(AttnParams p) {
       pb_prev[1][nb] = pb[1][nb];
     }
   };
-  auto group = [&](auto mask_c, int t) __attribute__((always_inline)) {
-    iteration(mask_c, std::integral_constant<int, 0>{}, t);
-    iteration(mask_c, std::integral_constant<int, 1>{}, t + 1);
-    if constexpr (NS == 4) {
-      iteration(mask_c, std::integral_constant<int, 2>{}, t + 2);
-      iteration(mask_c, std::integral_constant<int, 3>{}, t + 3);
-    }
-  };
 
-  // iterations 0 .. n_tiles (the last one only adds P(n_tiles - 1) V), in
-  // groups of NS: unmasked up to the group holding the diagonal, masked after
-  const int t_split = t_diag / NS * NS;
+  // iterations 0 .. n_tiles (the last one only adds P(n_tiles - 1) V):
+  // unmasked up to the group holding the diagonal, masked after
   int t = 0;
-  for (; t < t_split; t += NS) group(std::false_type{}, t);
-  for (; t <= n_tiles; t += NS) group(std::true_type{}, t);
-  if constexpr (ESZ == 2) wait_vmem<0>();  // no tile write may land after the workgroup ends
+  if constexpr (ESZ == 2) {
+    // bf16: a hand-off before every even iteration t.  After the barrier
+    // K(t+1), K(t+2), V(t-1) and V(t) are resident (read by iterations t and
+    // t+1), K(t+3), K(t+4), V(t+1) and V(t+2) may still be in flight, and no
+    // wave reads any other slot any more: the hand-off fetches K(t+5),
+    // K(t+6), V(t+3) and V(t+4) into those.  Every hand-off issues the same
+    // number of transfers, so vmcnt(4 LOADS) before the next barrier leaves
+    // exactly the latest hand-off's transfers in flight.
+    auto handoff = [&](auto r_c, int t) __attribute__((always_inline)) {
+      constexpr int R = decltype(r_c)::value;
+      barrier_lds();
+      dma_tile<D, WAVES, false>(c, (__bf16*)sk[(R + 5) % NS], t + 5, page_k[0], wave, lane);
+      dma_tile<D, WAVES, false>(c, (__bf16*)sk[R], t + 6, page_k[1], wave, lane);
+      dma_tile<D, WAVES, true>(c, (__bf16*)sv[(R + 3) % NS], t + 3, page_v[0], wave, lane);
+      dma_tile<D, WAVES, true>(c, (__bf16*)sv[(R + 4) % NS], t + 4, page_v[1], wave, lane);
+      page_v[0] = page_k[0];
+      page_v[1] = page_k[1];
+    };
+    auto pair = [&](auto mask_c, auto r_c, int t) __attribute__((always_inline)) {
+      constexpr int R = decltype(r_c)::value;
+      handoff(r_c, t);
+      compute(mask_c, r_c, t);
+      compute(mask_c, std::integral_constant<int, R + 1>{}, t + 1);
+      wait_vmem<4 * DM::LOADS>();
+      // the next page ids, loaded just before the barrier that waits for them
+      // anyway (an earlier scalar load would force a full LDS drain at the
+      // first operand wait after it)
+      __builtin_amdgcn_sched_barrier(0);
+      page_k[0] = wave_page<D, WAVES>(c, t + 7, wave);
+      page_k[1] = wave_page<D, WAVES>(c, t + 8, wave);
+    };
+
+    // prologue: K(0), K(1), K(2), V(-1) (zero: the first PV multiplies it by
+    // P(-1) = 0) and V(0) resident, the scores of tile 0, then the fetches of
+    // the hand-off before iteration -2 (no wave reads their slots yet)
+    dma_tile<D, WAVES, false>(c, (__bf16*)sk[0], 0, wave_page<D, WAVES>(c, 0, wave), wave, lane);
+    dma_tile<D, WAVES, false>(c, (__bf16*)sk[1], 1, wave_page<D, WAVES>(c, 1, wave), wave, lane);
+    dma_tile<D, WAVES, false>(c, (__bf16*)sk[2], 2, wave_page<D, WAVES>(c, 2, wave), wave, lane);
+    dma_tile<D, WAVES, true>(c, (__bf16*)sv[NS - 1], -1, wave_page<D, WAVES>(c, -1, wave), wave, lane);
+    dma_tile<D, WAVES, true>(c, (__bf16*)sv[0], 0, wave_page<D, WAVES>(c, 0, wave), wave, lane);
+    load_q();
+    wait_vmem<0>();
+    barrier_lds();
+    {
+      bf16x8 ka[NKS];
+      read_k(0, ka);
+      scores(ka, s_cur);
+    }
+    dma_tile<D, WAVES, false>(c, (__bf16*)sk[3], 3, wave_page<D, WAVES>(c, 3, wave), wave, lane);
+    dma_tile<D, WAVES, false>(c, (__bf16*)sk[4], 4, wave_page<D, WAVES>(c, 4, wave), wave, lane);
+    dma_tile<D, WAVES, true>(c, (__bf16*)sv[1], 1, wave_page<D, WAVES>(c, 1, wave), wave, lane);
+    dma_tile<D, WAVES, true>(c, (__bf16*)sv[2], 2, wave_page<D, WAVES>(c, 2, wave), wave, lane);
+    page_v[0] = wave_page<D, WAVES>(c, 3, wave);
+    page_v[1] = wave_page<D, WAVES>(c, 4, wave);
+    page_k[0] = wave_page<D, WAVES>(c, 5, wave);
+    page_k[1] = wave_page<D, WAVES>(c, 6, wave);
+
+    using I0 = std::integral_constant<int, 0>;
+    using I2 = std::integral_constant<int, 2>;
+    using I4 = std::integral_constant<int, 4>;
+    const int t_split = t_diag / NS * NS;
+    for (; t < t_split; t += NS) {
+      pair(std::false_type{}, I0{}, t);
+      pair(std::false_type{}, I2{}, t + 2);
+      pair(std::false_type{}, I4{}, t + 4);
+    }
+    for (; t <= n_tiles; t += NS) {
+      pair(std::true_type{}, I0{}, t);
+      if (t + 2 > n_tiles) break;
+      pair(std::true_type{}, I2{}, t + 2);
+      if (t + 4 > n_tiles) break;
+      pair(std::true_type{}, I4{}, t + 4);
+    }
+    wait_vmem<0>();  // no tile write may land after the workgroup ends
+  } else {
+    // fp8: iteration t converts K(t+2) and V(t) through registers into the
+    // slots that K(t) and V(t-2) held; a barrier per iteration
+    load_q();
+    fp8_fetch<D, THREADS>(fk, c, c.kbase, 0, tid);
+    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[0], 0, L, tid);
+    fp8_fetch<D, THREADS>(fk, c, c.kbase, 1, tid);
+    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[1], 1, L, tid);
+    for (int i = tid; i < TB / 16; i += THREADS) ((u32x4*)sv[1])[i] = u32x4{0u, 0u, 0u, 0u};
+    barrier_lds();
+    {
+      bf16x8 ka[NKS];
+      read_k(0, ka);
+      scores(ka, s_cur);
+    }
+    auto iteration = [&](auto mask_c, auto r_c, int t) __attribute__((always_inline)) {
+      constexpr int R = decltype(r_c)::value;
+      barrier_lds();
+      fp8_fetch<D, THREADS>(fk, c, c.kbase, t + 2, tid);
+      fp8_fetch<D, THREADS>(fv, c, c.vbase, t, tid);
+      compute(mask_c, r_c, t);
+      store8(t, R);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    const int t_split = t_diag / NS * NS;
+    for (; t < t_split; t += NS) {
+      iteration(std::false_type{}, I0{}, t);
+      iteration(std::false_type{}, I1{}, t + 1);
+    }
+    for (; t <= n_tiles; t += NS) {
+      iteration(std::true_type{}, I0{}, t);
+      iteration(std::true_type{}, I1{}, t + 1);
+    }
+  }
+
 
   // acc[d][nb][i] = O^T[dim 32 d + 8 (i / 4) + 4 qgrp + i % 4][row]
   float out_scale = 1.0f;
