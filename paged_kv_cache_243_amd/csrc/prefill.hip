@@ -15,14 +15,15 @@
 //    item (two per SIMD), each wave owning 32 rows.  A one-workgroup plan
 //    kernel lists the tiles longest first (their KV length sets their cost),
 //    so in-order dispatch fills the CUs greedily.
-//  * Keys stream in tiles of 32 positions (2 pages) through a ring of 4 LDS
-//    slots.  bf16 tiles go from global memory straight into LDS (buffer_load
-//    ... lds); every page gets a buffer descriptor whose range ends at the
-//    sequence's last valid row, so rows at positions >= seq_lens read as zeros
-//    whatever the pool holds.  fp8 tiles go through registers and are widened
-//    to bf16 (rows past seq_lens stored as zeros), two slots deep.  One
-//    barrier per tile.  LDS rows keep their 16-byte chunks XOR-swizzled so the
-//    operand reads below are spread over the banks.
+//  * Keys stream in tiles of 32 positions (2 pages) through LDS rings (K and
+//    V).  bf16 tiles go from global memory straight into LDS (buffer_load ...
+//    lds), 6 slots deep, two K and two V tiles behind each barrier; every page
+//    gets a buffer descriptor whose range ends at the sequence's last valid
+//    row, so rows at positions >= seq_lens read as zeros whatever the pool
+//    holds.  fp8 tiles go through registers and are widened to bf16 (rows past
+//    seq_lens stored as zeros), two slots deep, one barrier per tile.  LDS rows
+//    keep their 16-byte chunks XOR-swizzled so the operand reads below are
+//    spread over the banks.
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from
 //    LDS, B = 16 dims x 32 query rows held in registers): each lane owns 16 keys
 //    of one query row, so a row max needs one cross-lane step.
