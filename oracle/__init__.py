@@ -80,6 +80,12 @@ def open_library(path: str):
     lib.orc_e4m3fn_to_double.restype = dbl
     lib.orc_e4m3fn_table.argtypes = [vp]
     lib.orc_e4m3fn_table.restype = None
+    lib.orc_e4m3fn_from_float.argtypes = [ctypes.c_float]
+    lib.orc_e4m3fn_from_float.restype = ctypes.c_uint8
+    lib.orc_e4m3fn_encode_array.argtypes = [vp, i64, vp]
+    lib.orc_e4m3fn_encode_array.restype = None
+    lib.orc_paged_kv_write_fp8.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i64, i64, i64, i64]
+    lib.orc_paged_kv_write_fp8.restype = i32
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = i32
     return lib
@@ -108,6 +114,15 @@ def e4m3fn_table() -> np.ndarray:
     return out
 
 
+def e4m3fn_encode(y: np.ndarray) -> np.ndarray:
+    """E4M3FN codes (uint8) of float32 values: nearest finite code, ties to
+    even, saturating at +-448, NaN kept (see orc_e4m3fn_from_float)."""
+    yc = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(yc.shape, dtype=np.uint8)
+    _load().orc_e4m3fn_encode_array(_ptr(yc), yc.size, _ptr(out))
+    return out
+
+
 def bf16_to_f64(bits: int) -> float:
     return _load().orc_bf16_to_double(int(bits) & 0xFFFF)
 
@@ -132,6 +147,30 @@ def paged_kv_write(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray,
     st = _load().orc_paged_kv_write(_ptr(k), _ptr(v), _ptr(sm), sm.shape[0],
                                     _ptr(key_pool), _ptr(value_pool),
                                     num_pages, page_size, row_bytes)
+    if st != 0:
+        raise OracleError(st)
+
+
+def paged_kv_write_fp8(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray,
+                       k_scale: np.ndarray, v_scale: np.ndarray,
+                       key_pool: np.ndarray, value_pool: np.ndarray) -> None:
+    """Quantising scatter into fp8 pools in place.
+
+    k, v: [T_new, Hkv, D] bf16 bit patterns (uint16); pools: [num_pages,
+    page_size, Hkv, D] uint8 E4M3FN codes; k_scale, v_scale: [Hkv] float32
+    dequantisation factors (element x is stored as the code of x / scale[h]).
+    """
+    assert k.dtype == np.uint16 and v.dtype == np.uint16
+    assert key_pool.dtype == np.uint8 and value_pool.dtype == np.uint8
+    num_pages, page_size, Hkv, D = key_pool.shape
+    assert value_pool.shape == key_pool.shape and k.shape == v.shape == (slot_mapping.shape[0], Hkv, D)
+    kc, vc = np.ascontiguousarray(k), np.ascontiguousarray(v)
+    ks = np.ascontiguousarray(k_scale, dtype=np.float32)
+    vs = np.ascontiguousarray(v_scale, dtype=np.float32)
+    assert ks.shape == (Hkv,) and vs.shape == (Hkv,)
+    sm = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+    st = _load().orc_paged_kv_write_fp8(_ptr(kc), _ptr(vc), _ptr(sm), sm.shape[0], _ptr(ks), _ptr(vs),
+                                        _ptr(key_pool), _ptr(value_pool), num_pages, page_size, Hkv, D)
     if st != 0:
         raise OracleError(st)
 

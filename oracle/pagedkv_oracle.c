@@ -11,7 +11,8 @@
  * and obvious way, in fp64:
  *
  *   1. write:   every new token's K and V row is copied byte for byte into the
- *               page pool at the row named by its slot
+ *               page pool at the row named by its slot (for fp8 pools a
+ *               second form encodes bf16 rows into E4M3FN codes on the way)
  *               (page "Add paged / block-table KV cache export
  *               (--features paged-cache)", onnxruntime/mobius #395, PR summary
  *               and table "ONNX I/O contract": slot = page_id*page_size+offset,
@@ -37,6 +38,8 @@
  *   - a negative slot means "no write";
  *   - duplicate non-negative slots in one call are rejected;
  *   - fp8 pools hold OCP E4M3FN codes with one fp32 scale per KV head per pool;
+ *   - the quantising write encodes x / scale[h] (one binary32 division) by
+ *     round to nearest even, saturating at +-448;
  *   - scale multiplies q.k exactly as passed, with no implicit 1/sqrt(D)
  *     (maxtext #93, gpu_paged commit and the scale-fix commit: the caller owns
  *     the scale).
@@ -138,6 +141,69 @@ int orc_paged_kv_write(const uint8_t* k, const uint8_t* v, const int64_t* slot_m
     int64_t dst_row = page * page_size + offset;
     memcpy(key_pool + dst_row * row_bytes, k + t * row_bytes, (size_t)row_bytes);
     memcpy(value_pool + dst_row * row_bytes, v + t * row_bytes, (size_t)row_bytes);
+  }
+  return ORC_OK;
+}
+
+/* E4M3FN encoding of a binary32 value y: the finite code nearest to y, a
+ * tie going to the code whose mantissa LSB is 0 (round to nearest even), and
+ * magnitudes beyond the largest finite value (infinities included) going to
+ * +-448 (saturation: the format has no infinity).  NaN gives the NaN code
+ * with y's sign; the sign of zero is kept.  Found by plain search over the
+ * 127 non-negative finite codes. */
+uint8_t orc_e4m3fn_from_float(float y) {
+  uint8_t sign = signbit(y) ? 0x80 : 0x00;
+  if (isnan(y)) return sign | 0x7F;
+  double a = fabs((double)y);
+  if (isinf(a)) return sign | 0x7E;
+  int best = 0;
+  double best_d = a; /* distance to code 0 (+0) */
+  for (int c = 1; c <= 0x7E; ++c) {
+    double d = fabs(orc_e4m3fn_to_double((uint8_t)c) - a);
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return sign | (uint8_t)best;
+}
+
+void orc_e4m3fn_encode_array(const float* y, int64_t n, uint8_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3fn_from_float(y[i]);
+}
+
+/*
+ * Step 1 for fp8 pools, with the quantisation folded into the write: k and v
+ * are bf16 rows [n_tokens, Hkv, D]; element x of KV head h is stored as the
+ * E4M3FN code of x / scale[h], the quotient taken once in binary32 (the
+ * scales are the per-head dequantisation factors the attention multiplies
+ * codes by).  Slots are checked and skipped exactly as in the plain write.
+ */
+int orc_paged_kv_write_fp8(const uint16_t* k, const uint16_t* v, const int64_t* slot_mapping,
+                           int64_t n_tokens, const float* k_scale, const float* v_scale,
+                           uint8_t* key_pool, uint8_t* value_pool, int64_t num_pages,
+                           int64_t page_size, int64_t Hkv, int64_t D) {
+  int64_t capacity = num_pages * page_size;
+  int64_t row = Hkv * D;
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0) continue;
+    if (s >= capacity) return ORC_ERR_SLOT_RANGE;
+    for (int64_t u = 0; u < t; ++u)
+      if (slot_mapping[u] == s) return ORC_ERR_SLOT_DUPLICATE;
+  }
+  for (int64_t t = 0; t < n_tokens; ++t) {
+    int64_t s = slot_mapping[t];
+    if (s < 0) continue;
+    int64_t dst_row = (s / page_size) * page_size + s % page_size;
+    for (int64_t h = 0; h < Hkv; ++h)
+      for (int64_t i = 0; i < D; ++i) {
+        int64_t e = h * D + i;
+        float xk = (float)orc_bf16_to_double(k[t * row + e]);
+        float xv = (float)orc_bf16_to_double(v[t * row + e]);
+        key_pool[dst_row * row + e] = orc_e4m3fn_from_float(xk / k_scale[h]);
+        value_pool[dst_row * row + e] = orc_e4m3fn_from_float(xv / v_scale[h]);
+      }
   }
   return ORC_OK;
 }

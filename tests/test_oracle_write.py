@@ -2,6 +2,7 @@
 assignment (ScatterND without duplicates) and the poison invariant."""
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from paged_kv_cache_243_amd import workloads as W
@@ -74,3 +75,46 @@ def test_nan_payloads_are_copied_bit_for_bit():
     oracle.paged_kv_write(k, S(w.v_new), S(w.slot_mapping), kp, vp)
     s = int(S(w.slot_mapping)[0])
     assert list(kp.view(np.uint16).reshape(-1, k[0].size)[s, :4]) == [0x7FC1, 0xFF81, 0x7F80, 0x0001]
+
+
+def test_quantising_write_equals_torch_division_and_cast():
+    """The fp8 form of the write stores, per KV head h, the E4M3FN code of
+    x / scale[h] (binary32 division): checked against torch's float32
+    division and its round-to-nearest-even cast, with inputs kept inside the
+    cast's non-saturating range."""
+    rng = np.random.default_rng(21)
+    T, Hkv, D, num_pages, ps = 9, 3, 64, 8, 16
+    k32 = rng.standard_normal((T, Hkv, D)).astype(np.float32) * 3
+    v32 = rng.standard_normal((T, Hkv, D)).astype(np.float32) * 3
+    kb = torch.from_numpy(k32).to(torch.bfloat16)
+    vb = torch.from_numpy(v32).to(torch.bfloat16)
+    ks = (np.abs(k32).reshape(T, Hkv, D).max(axis=(0, 2)) / 400).astype(np.float32)
+    vs = (np.abs(v32).reshape(T, Hkv, D).max(axis=(0, 2)) / 400).astype(np.float32)
+    slots = rng.permutation(num_pages * ps)[:T].astype(np.int64)
+    slots[4] = -1
+    kp = np.full((num_pages, ps, Hkv, D), 0x7F, dtype=np.uint8)
+    vp = kp.copy()
+    oracle.paged_kv_write_fp8(kb.view(torch.int16).numpy().view(np.uint16), vb.view(torch.int16).numpy().view(np.uint16),
+                              slots, ks, vs, kp, vp)
+    kq = (kb.float() / torch.from_numpy(ks)[None, :, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    vq = (vb.float() / torch.from_numpy(vs)[None, :, None]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    want_k = np.full_like(kp, 0x7F)
+    want_v = np.full_like(vp, 0x7F)
+    for t, s in enumerate(slots):
+        if s >= 0:
+            want_k[s // ps, s % ps] = kq[t]
+            want_v[s // ps, s % ps] = vq[t]
+    assert np.array_equal(kp, want_k) and np.array_equal(vp, want_v)
+
+
+def test_quantising_write_rejects_bad_slots_before_writing():
+    T, Hkv, D, num_pages, ps = 3, 1, 64, 2, 16
+    k = np.zeros((T, Hkv, D), dtype=np.uint16)
+    ones = np.ones(Hkv, dtype=np.float32)
+    for slots, status in (([0, 5, 5], -2), ([0, 1, 32], -1)):
+        kp = np.full((num_pages, ps, Hkv, D), 0x7F, dtype=np.uint8)
+        vp = kp.copy()
+        with pytest.raises(oracle.OracleError) as e:
+            oracle.paged_kv_write_fp8(k, k, np.array(slots, dtype=np.int64), ones, ones, kp, vp)
+        assert e.value.status == status
+        assert (kp == 0x7F).all() and (vp == 0x7F).all()
