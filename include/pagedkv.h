@@ -130,6 +130,36 @@ int paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* s
                    pkv_tensor* key_pool, pkv_tensor* value_pool, void* stream);
 
 /*
+ * paged_kv_write_fp8 -- the write for fp8 pools, quantising on the way.
+ *
+ * For every t with s = slot_mapping[t] >= 0 and every KV head h, element x
+ * of k[t][h] is stored in key_pool[s / page_size][s % page_size][h] as the
+ * OCP E4M3FN code of y = x / k_scale[h] (one IEEE binary32 division), and
+ * likewise for v with v_scale: round to nearest even, |y| beyond 448
+ * (infinities included) saturated to +-448, a NaN x stored as the NaN code
+ * with x's sign.  k_scale and v_scale are the per-head factors paged_attention
+ * multiplies codes by, so a row written here reads back as code * scale.
+ * Negative slots are skipped; everything else in the pools is untouched.
+ * (The pages name an fp8 KV cache as a feature, mobius #395 "Features";
+ * they do not say where quantisation happens.  The plain write above stores
+ * codes the caller already holds; this form produces them from bf16 rows.)
+ *
+ *   k, v              [T_new, Hkv, D]                  PKV_BF16, D a multiple of 8
+ *   slot_mapping      [T_new]                          PKV_I64
+ *   key_pool,         [num_pages, page_size, Hkv, D]   PKV_FP8_E4M3FN
+ *   value_pool        (same shape and dtype as key_pool)
+ *   k_scale, v_scale  device pointers to [Hkv] fp32, positive and finite (not
+ *                     checked: the host cannot read them without a sync)
+ *
+ * Duplicate non-negative slots are a caller error, as for paged_kv_write.
+ * Returns PKV_OK, PKV_ERR_SCALE for a NULL scale pointer, or another
+ * negative status for a bad argument; nothing is enqueued on error.
+ */
+int paged_kv_write_fp8(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+                       pkv_tensor* key_pool, pkv_tensor* value_pool, const float* k_scale,
+                       const float* v_scale, void* stream);
+
+/*
  * paged_attention -- causal GQA attention over paged KV.
  *
  * Sequence b owns query rows query_start_loc[b] .. query_start_loc[b+1]-1

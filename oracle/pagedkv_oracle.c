@@ -177,7 +177,8 @@ void orc_e4m3fn_encode_array(const float* y, int64_t n, uint8_t* out) {
  * are bf16 rows [n_tokens, Hkv, D]; element x of KV head h is stored as the
  * E4M3FN code of x / scale[h], the quotient taken once in binary32 (the
  * scales are the per-head dequantisation factors the attention multiplies
- * codes by).  Slots are checked and skipped exactly as in the plain write.
+ * codes by); a NaN input is stored as the NaN code with its own sign.
+ * Slots are checked and skipped exactly as in the plain write.
  */
 int orc_paged_kv_write_fp8(const uint16_t* k, const uint16_t* v, const int64_t* slot_mapping,
                            int64_t n_tokens, const float* k_scale, const float* v_scale,
@@ -201,8 +202,11 @@ int orc_paged_kv_write_fp8(const uint16_t* k, const uint16_t* v, const int64_t* 
         int64_t e = h * D + i;
         float xk = (float)orc_bf16_to_double(k[t * row + e]);
         float xv = (float)orc_bf16_to_double(v[t * row + e]);
-        key_pool[dst_row * row + e] = orc_e4m3fn_from_float(xk / k_scale[h]);
-        value_pool[dst_row * row + e] = orc_e4m3fn_from_float(xv / v_scale[h]);
+        /* a NaN input keeps its own sign (a quotient's NaN sign is not fixed by IEEE 754) */
+        key_pool[dst_row * row + e] =
+            isnan(xk) ? (uint8_t)(signbit(xk) ? 0xFF : 0x7F) : orc_e4m3fn_from_float(xk / k_scale[h]);
+        value_pool[dst_row * row + e] =
+            isnan(xv) ? (uint8_t)(signbit(xv) ? 0xFF : 0x7F) : orc_e4m3fn_from_float(xv / v_scale[h]);
       }
   }
   return ORC_OK;

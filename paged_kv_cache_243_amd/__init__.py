@@ -18,5 +18,6 @@ from ._binding import (  # noqa: F401
     paged_attention,
     paged_attention_workspace_size,
     paged_kv_write,
+    paged_kv_write_fp8,
     paged_validate_metadata,
 )

@@ -24,7 +24,7 @@ STATUS = {
     -7: "PKV_ERR_HIP", -8: "PKV_ERR_INDEX",
 }
 # every symbol include/pagedkv.h declares
-EXPORTS = ("paged_kv_write", "paged_attention", "paged_attention_workspace_size",
+EXPORTS = ("paged_kv_write", "paged_kv_write_fp8", "paged_attention", "paged_attention_workspace_size",
            "paged_validate_metadata", "pkv_check_metadata_host", "pkv_status_string",
            "pkv_abi_version")
 
@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         lib.paged_kv_write.argtypes = [P, P, P, P, P, vp]
         lib.paged_kv_write.restype = i32
+        lib.paged_kv_write_fp8.argtypes = [P, P, P, P, P, vp, vp, vp]
+        lib.paged_kv_write_fp8.restype = i32
         lib.paged_attention.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, ctypes.POINTER(PkvAttnOpts), vp]
         lib.paged_attention.restype = i32
         lib.paged_attention_workspace_size.argtypes = [P, P, P, ctypes.POINTER(PkvAttnOpts)]
@@ -118,6 +120,21 @@ def paged_kv_write(k, v, slot_mapping, key_pool, value_pool) -> None:
     st = lib.paged_kv_write(describe(k), describe(v), describe(slot_mapping), describe(key_pool),
                             describe(value_pool), _stream(key_pool))
     _check(st, "paged_kv_write")
+
+
+def paged_kv_write_fp8(k, v, slot_mapping, key_pool, value_pool, k_scale, v_scale) -> None:
+    """Quantise bf16 k/v [T, Hkv, D] to E4M3FN codes of x / scale[h] and
+    scatter them into the fp8 pools [num_pages, 16, Hkv, D] in place;
+    k_scale, v_scale: [Hkv] float32 device tensors."""
+    lib = load()
+    for s_ in (k_scale, v_scale):
+        if s_ is None or s_.dtype != torch.float32 or s_.device != key_pool.device or not s_.is_contiguous():
+            raise PagedKVError(-5, "paged_kv_write_fp8: scales must be contiguous float32 tensors on the pool's device")
+        if s_.numel() != key_pool.shape[2]:
+            raise PagedKVError(-2, "paged_kv_write_fp8: scales need one entry per KV head")
+    st = lib.paged_kv_write_fp8(describe(k), describe(v), describe(slot_mapping), describe(key_pool),
+                                describe(value_pool), k_scale.data_ptr(), v_scale.data_ptr(), _stream(key_pool))
+    _check(st, "paged_kv_write_fp8")
 
 
 def _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_events=None) -> PkvAttnOpts:

@@ -18,6 +18,19 @@ struct WriteParams {
   int64_t row_bytes;  // Hkv * D * element size; a multiple of 16
 };
 
+// quantising form of the write: bf16 rows in, E4M3FN codes out
+struct WriteFp8Params {
+  const void* k;        // [n_tokens, Hkv, D] bf16
+  const void* v;
+  const int64_t* slots;
+  void* key_pool;       // [num_pages, page_size, Hkv, D] E4M3FN codes
+  void* value_pool;
+  const float* k_scale;  // [Hkv] dequantisation factors
+  const float* v_scale;
+  int64_t n_tokens;
+  int64_t Hkv, D;       // D a multiple of 8
+};
+
 struct AttnParams {
   const void* q;        // [T, Hq, D]
   void* out;            // [T, Hq, D]
@@ -50,6 +63,7 @@ struct LaunchEvents {
 };
 
 hipError_t launch_write(const WriteParams& p, hipStream_t stream);
+hipError_t launch_write_fp8(const WriteFp8Params& p, hipStream_t stream);
 hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);

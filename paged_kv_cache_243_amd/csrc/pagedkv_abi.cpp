@@ -252,6 +252,37 @@ int paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* s
   return pkv::launch_write(p, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int paged_kv_write_fp8(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+                       pkv_tensor* key_pool, pkv_tensor* value_pool, const float* k_scale,
+                       const float* v_scale, void* stream) {
+  PKV_TRY(check_tensor(k, 3, 16));
+  PKV_TRY(check_tensor(v, 3, 16));
+  PKV_TRY(check_tensor(slot_mapping, 1, 8));
+  PKV_TRY(check_tensor(key_pool, 4, 8));
+  PKV_TRY(check_tensor(value_pool, 4, 8));
+  if (k->dtype != PKV_BF16 || v->dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (key_pool->dtype != PKV_FP8_E4M3FN || value_pool->dtype != PKV_FP8_E4M3FN) return PKV_ERR_DTYPE;
+  if (slot_mapping->dtype != PKV_I64) return PKV_ERR_DTYPE;
+  if (!same_shape(key_pool, value_pool) || !same_shape(k, v)) return PKV_ERR_SHAPE;
+  if (slot_mapping->shape[0] != k->shape[0]) return PKV_ERR_SHAPE;
+  if (k->shape[1] != key_pool->shape[2] || k->shape[2] != key_pool->shape[3]) return PKV_ERR_SHAPE;
+  if (!k_scale || !v_scale) return PKV_ERR_SCALE;
+  if (key_pool->shape[3] <= 0 || key_pool->shape[3] % 8 != 0 || key_pool->shape[2] <= 0) return PKV_ERR_UNSUPPORTED;
+  pkv::WriteFp8Params p;
+  p.k = k->data;
+  p.v = v->data;
+  p.slots = (const int64_t*)slot_mapping->data;
+  p.key_pool = key_pool->data;
+  p.value_pool = value_pool->data;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.n_tokens = k->shape[0];
+  p.Hkv = key_pool->shape[2];
+  p.D = key_pool->shape[3];
+  if (p.n_tokens == 0) return PKV_OK;
+  return pkv::launch_write_fp8(p, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 size_t paged_attention_workspace_size(const pkv_tensor* q, const pkv_tensor* key_pool,
                                       const pkv_tensor* block_table, const pkv_attn_opts* opts) {
   AttnPlan plan;

@@ -105,6 +105,84 @@ def test_write_with_zero_tokens_is_a_no_op():
     assert call_write(a) == 0
 
 
+def write_fp8_args(**over):
+    a = dict(k=T([4, 8, 128], B.PKV_BF16), v=T([4, 8, 128], B.PKV_BF16), slots=T([4], B.PKV_I64),
+             kp=T([64, 16, 8, 128], B.PKV_FP8_E4M3FN), vp=T([64, 16, 8, 128], B.PKV_FP8_E4M3FN),
+             ks=FAKE, vs=FAKE)
+    a.update(over)
+    return a
+
+
+def call_write_fp8(a):
+    lib = pkv.load()
+    P = lambda t: ctypes.byref(t) if t is not None else None
+    return lib.paged_kv_write_fp8(P(a["k"]), P(a["v"]), P(a["slots"]), P(a["kp"]), P(a["vp"]),
+                                  a["ks"], a["vs"], None)
+
+
+@pytest.mark.parametrize("case,status", [
+    ("null k", -1),
+    ("null pool", -1),
+    ("k rank", -2),
+    ("slot count", -2),
+    ("k/v shape", -2),
+    ("pool shapes differ", -2),
+    ("row width", -2),
+    ("f32 rows", -3),
+    ("fp8 rows", -3),
+    ("bf16 pool", -3),
+    ("slot dtype", -3),
+    ("null k scale", -5),
+    ("null v scale", -5),
+    ("head dim not a multiple of 8", -4),
+    ("misaligned rows", -4),
+])
+def test_write_fp8_errors(case, status):
+    a = write_fp8_args()
+    if case == "null k":
+        a["k"] = None
+    elif case == "null pool":
+        a["vp"] = None
+    elif case == "k rank":
+        a["k"] = T([4, 1024], B.PKV_BF16)
+    elif case == "slot count":
+        a["slots"] = T([5], B.PKV_I64)
+    elif case == "k/v shape":
+        a["v"] = T([4, 8, 64], B.PKV_BF16)
+    elif case == "pool shapes differ":
+        a["vp"] = T([65, 16, 8, 128], B.PKV_FP8_E4M3FN)
+    elif case == "row width":
+        a["k"] = T([4, 4, 128], B.PKV_BF16)
+        a["v"] = T([4, 4, 128], B.PKV_BF16)
+    elif case == "f32 rows":
+        a["k"] = T([4, 8, 128], B.PKV_F32)
+        a["v"] = T([4, 8, 128], B.PKV_F32)
+    elif case == "fp8 rows":
+        a["k"] = T([4, 8, 128], B.PKV_FP8_E4M3FN)
+        a["v"] = T([4, 8, 128], B.PKV_FP8_E4M3FN)
+    elif case == "bf16 pool":
+        a["kp"] = T([64, 16, 8, 128], B.PKV_BF16)
+        a["vp"] = T([64, 16, 8, 128], B.PKV_BF16)
+    elif case == "slot dtype":
+        a["slots"] = T([4], B.PKV_BF16)
+    elif case == "null k scale":
+        a["ks"] = None
+    elif case == "null v scale":
+        a["vs"] = None
+    elif case == "head dim not a multiple of 8":
+        a = write_fp8_args(k=T([4, 8, 12], B.PKV_BF16), v=T([4, 8, 12], B.PKV_BF16),
+                           kp=T([64, 16, 8, 12], B.PKV_FP8_E4M3FN), vp=T([64, 16, 8, 12], B.PKV_FP8_E4M3FN))
+    elif case == "misaligned rows":
+        a["k"] = T([4, 8, 128], B.PKV_BF16, ptr=FAKE + 8)
+    assert call_write_fp8(a) == status
+
+
+def test_write_fp8_with_zero_tokens_is_a_no_op():
+    a = write_fp8_args(k=T([0, 8, 128], B.PKV_BF16, None), v=T([0, 8, 128], B.PKV_BF16, None),
+                       slots=T([0], B.PKV_I64, None))
+    assert call_write_fp8(a) == 0
+
+
 def attn_args(**over):
     a = dict(q=T([4, 32, 128], B.PKV_BF16), kp=T([64, 16, 8, 128], B.PKV_BF16),
              vp=T([64, 16, 8, 128], B.PKV_BF16), bt=T([4, 8], B.PKV_I64), sl=T([4], B.PKV_I64),
