@@ -117,6 +117,33 @@ def write_bytes(w) -> int:
     return int(2 * 2 * T * w.cfg.hkv * w.cfg.head_dim * esz + 8 * T)
 
 
+def fp8_write_bytes(T: int, hkv: int, d: int) -> int:
+    """Algorithmic bytes of one quantising write: bf16 K and V rows read, fp8
+    codes written, slots and the two scale vectors read."""
+    return int(2 * T * hkv * d * (2 + 1) + 8 * T + 2 * 4 * hkv)
+
+
+class Fp8WriteRunner:
+    """Quantising write of the chunked-prefill workload's 4096 new bf16 K/V
+    rows into fp8 pools of the same geometry (65536 pages), with per-head
+    scales amax / 448 of the rows."""
+
+    def __init__(self, pkv, w, torch):
+        self.pkv, self.w = pkv, w
+        shape = w.key_pool.shape
+        self.kp = torch.zeros(shape, dtype=torch.uint8, device=w.k_new.device)
+        self.vp = torch.zeros(shape, dtype=torch.uint8, device=w.k_new.device)
+        self.ks = (w.k_new.float().abs().amax(dim=(0, 2)) / 448).contiguous()
+        self.vs = (w.v_new.float().abs().amax(dim=(0, 2)) / 448).contiguous()
+
+    def write(self):
+        w = self.w
+        self.pkv.paged_kv_write_fp8(w.k_new, w.v_new, w.slot_mapping, self.kp, self.vp, self.ks, self.vs)
+
+    def attend(self, kernel_events=None):
+        pass
+
+
 class Runner:
     """Write + attention of one workload with preallocated buffers."""
 
@@ -248,7 +275,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-extra", action="store_true", help="time only the decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
-    ap.add_argument("--profile-workload", choices=["decode", "prefill", "shared", "fp8"],
+    ap.add_argument("--profile-workload", choices=["decode", "prefill", "shared", "fp8", "fp8write"],
                     help="time one workload only and print its median times (for profiler runs)")
     args = ap.parse_args(argv)
 
@@ -268,6 +295,14 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     flush = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
+    if args.profile_workload == "fp8write":
+        w = W.generate(3, dev)
+        t = time_steps(Fp8WriteRunner(pkv, w, torch), torch, args.steps, args.warmup, flush, "fp8 write",
+                       kernel_events=False)
+        print(json.dumps({"workload": "quantising fp8 write of 4096 bf16 K/V rows (Hkv 8, D 128)",
+                          "write_ms_median": statistics.median(t.write),
+                          "write_ms_mean": statistics.fmean(t.write)}), flush=True)
+        return 0
     if args.profile_workload:
         cid = {"decode": 2, "prefill": 3, "shared": 4, "fp8": 5}[args.profile_workload]
         w = W.generate(cid, dev)
@@ -354,6 +389,22 @@ def main(argv=None) -> int:
         fl = prefill_flops(w3)
         a3 = statistics.median(t3.attn)
         k3 = statistics.fmean(kt3.kernel)
+        # quantising fp8 write of the same 4096 new rows
+        fw = time_steps(Fp8WriteRunner(pkv, w3, torch), torch, args.steps, args.warmup, flush,
+                        "fp8 quantising write", kernel_events=False)
+        fw_ms = statistics.median(fw.write)
+        fw_bytes = fp8_write_bytes(w3.k_new.shape[0], w3.cfg.hkv, w3.cfg.head_dim)
+        extra["fp8_quantising_write"] = {
+            "workload": "4096 new bf16 K/V rows (Hkv 8, head_dim 128) quantised to E4M3FN with per-head "
+                        "scales and scattered into 65536-page fp8 pools",
+            "kernel": "slot_scatter_fp8_kernel",
+            "bound": "hbm", "unit": "GB/s",
+            "algorithmic_bytes": fw_bytes,
+            "ms_median": round(fw_ms, 5),
+            "achieved": round(fw_bytes / (fw_ms * 1e-3) / 1e9, 1),
+            "peak": HBM_PEAK_GBS,
+            "frac": round(fw_bytes / (fw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        }
         extra["prefill"] = {
             "workload": "chunked causal prefill, bf16: 8 sequences x 512 new tokens on U{0..8192} old "
                         "context, Hq 32, Hkv 8, head_dim 128",
