@@ -105,6 +105,16 @@ typedef struct {
                              kernel: the split-K decode kernel, the prefill kernel or the fp32
                              kernel, without the plan and merge launches around it.  NULL =
                              none.  For measuring that kernel alone. */
+  int32_t shared_prefix_pages; /* decode only (max_query_len 1): the caller states that the
+                             first shared_prefix_pages entries of every block_table row are
+                             the same pages and that every sequence with a query row holds
+                             more than shared_prefix_pages * page_size positions.  The
+                             prefix's attention then runs once for all sequences as MFMA
+                             tiles (all query rows of a group of sequences against the
+                             prefix keys) and is merged with the split-K decode of each
+                             sequence's own positions; the result is the same attention.
+                             Must be even (32-position units) and <= max_blocks; 0 = off.
+                             A statement that does not hold gives unspecified output. */
 } pkv_attn_opts;
 
 /*

@@ -38,7 +38,7 @@ class PkvAttnOpts(ctypes.Structure):
     _fields_ = [("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("max_query_len", ctypes.c_int32), ("split_tokens", ctypes.c_int32),
-                ("timing_events", ctypes.c_void_p * 2)]
+                ("timing_events", ctypes.c_void_p * 2), ("shared_prefix_pages", ctypes.c_int32)]
 
 
 class PagedKVError(RuntimeError):
@@ -137,7 +137,8 @@ def paged_kv_write_fp8(k, v, slot_mapping, key_pool, value_pool, k_scale, v_scal
     _check(st, "paged_kv_write_fp8")
 
 
-def _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_events=None) -> PkvAttnOpts:
+def _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_events=None,
+          shared_prefix_pages=0) -> PkvAttnOpts:
     o = PkvAttnOpts()
     o.k_scale = k_scale.data_ptr() if k_scale is not None else None
     o.v_scale = v_scale.data_ptr() if v_scale is not None else None
@@ -145,6 +146,7 @@ def _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_event
     o.workspace_bytes = workspace.numel() if workspace is not None else 0
     o.max_query_len = int(max_query_len or 0)
     o.split_tokens = int(split_tokens or 0)
+    o.shared_prefix_pages = int(shared_prefix_pages or 0)
     if timing_events is not None:
         for e in timing_events:
             if not e.cuda_event:  # torch creates the HIP event at its first record
@@ -155,10 +157,12 @@ def _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_event
     return o
 
 
-def paged_attention_workspace_size(q, key_pool, block_table, *, max_query_len=None, split_tokens=0) -> int:
+def paged_attention_workspace_size(q, key_pool, block_table, *, max_query_len=None, split_tokens=0,
+                                   shared_prefix_pages=0) -> int:
     lib = load()
     n = lib.paged_attention_workspace_size(describe(q), describe(key_pool), describe(block_table),
-                                           _opts(None, None, None, max_query_len, split_tokens))
+                                           _opts(None, None, None, max_query_len, split_tokens,
+                                                 shared_prefix_pages=shared_prefix_pages))
     if n == ctypes.c_size_t(-1).value:
         raise PagedKVError(-2, "invalid arguments for paged_attention_workspace_size")
     return int(n)
@@ -166,8 +170,11 @@ def paged_attention_workspace_size(q, key_pool, block_table, *, max_query_len=No
 
 def paged_attention(q, key_pool, value_pool, block_table, seq_lens, query_start_loc, scale, out, *,
                     k_scale=None, v_scale=None, max_query_len=None, split_tokens=0,
-                    workspace=None, timing_events=None) -> torch.Tensor:
+                    workspace=None, timing_events=None, shared_prefix_pages=0) -> torch.Tensor:
     """Causal GQA attention over paged KV into ``out`` [T, Hq, D] (returned).
+
+    ``shared_prefix_pages`` (decode only) states that every block_table row
+    starts with the same that many pages (see pkv_attn_opts in the header).
 
     The workspace the call needs is allocated through torch's allocator when
     ``workspace`` is not given (a uint8 device tensor owned by the caller).
@@ -176,9 +183,9 @@ def paged_attention(q, key_pool, value_pool, block_table, seq_lens, query_start_
     lib = load()
     if workspace is None:
         need = paged_attention_workspace_size(q, key_pool, block_table, max_query_len=max_query_len,
-                                              split_tokens=split_tokens)
+                                              split_tokens=split_tokens, shared_prefix_pages=shared_prefix_pages)
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
-    opts = _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_events)
+    opts = _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_events, shared_prefix_pages)
     st = lib.paged_attention(describe(q), describe(key_pool), describe(value_pool), describe(block_table),
                              describe(seq_lens), describe(query_start_loc), ctypes.c_float(scale),
                              describe(out), ctypes.byref(opts), _stream(q))

@@ -66,10 +66,12 @@ __host__ __device__ inline int decode_waves(int Hkv) {
   return (Hkv + hpw - 1) / hpw;
 }
 
-// Units of sequence b: its 32-position blocks, or none when it has no query row.
+// Units of sequence b: its 32-position blocks past the shared prefix (if
+// any), or none when it has no query row.
 __device__ __forceinline__ int32_t seq_units(const AttnParams& p, int b) {
   if (p.qsl[b + 1] == p.qsl[b]) return 0;
-  return (int32_t)((p.seq_lens[b] + kUnit - 1) / kUnit);
+  const int64_t keys = p.seq_lens[b] - p.prefix_len;
+  return keys > 0 ? (int32_t)((keys + kUnit - 1) / kUnit) : 0;
 }
 
 // K of a unit is read in whole-row runs (each load instruction covers RPI
@@ -383,13 +385,17 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     const int32_t seg_lo = __builtin_amdgcn_readfirstlane(max(u0, cb));
     const int32_t seg_hi = __builtin_amdgcn_readfirstlane(min(u1, ce));
     if (seg_lo >= seg_hi) continue;
-    const bool whole = seg_lo == cb && seg_hi == ce;
+    // (with a shared prefix, its partial joins in the merge: never whole)
+    const bool whole = seg_lo == cb && seg_hi == ce && p.prefix_len == 0;
     const int j0 = seg_lo - cb, j1 = seg_hi - cb;  // units of b in this segment
     const int64_t L = p.seq_lens[b];
     const int64_t q_row = p.qsl[b];
-    const int64_t last_page = ((L + 15) >> 4) - 1;
+    // unit j covers positions base + 32 j ..; pages are counted from base too
+    const int64_t base = p.prefix_len;
+    const int64_t last_page = ((L + 15) >> 4) - 1 - base / kPageSize;
     const __attribute__((address_space(4))) int64_t* bt_row =
-        (const __attribute__((address_space(4))) int64_t*)(p.block_table + (int64_t)b * p.max_blocks);
+        (const __attribute__((address_space(4))) int64_t*)(p.block_table + (int64_t)b * p.max_blocks +
+                                                           base / kPageSize);
 
     for (int hk = 0; hk < hpw; ++hk) {
       const int h = wave + hk * waves;
@@ -429,14 +435,14 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       // the loop issues unconditionally (straight-line load order, so each wait
       // covers exactly the loads it needs); the last unit is peeled
       for (int j = j0; j < j1 - 1; ++j) {
-        consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, (int64_t)j * kUnit, L, lane, [&] {
+        consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, base + (int64_t)j * kUnit, L, lane, [&] {
           issue_k<ESZ, D>(u, krsrc(nxt.p0), krsrc(nxt.p1), off);
           issue_v<ESZ, D>(u, vrsrc(nxt.p0), vrsrc(nxt.p1), off);
         });
         nxt = unit_pages(bt_row, j + 2, last_page);
       }
-      consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, (int64_t)(j1 - 1) * kUnit, L, lane,
-                           [] {});
+      consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, base + (int64_t)(j1 - 1) * kUnit, L,
+                           lane, [] {});
 
       // the four lane groups hold partial sums of the same head (same max)
       l_run += xor_shuffle(l_run, 16);
@@ -469,11 +475,11 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
 }
 
 // Log-sum-exp merge of the partials of a sequence whose units span several
-// workgroups:
+// workgroups (and, with a shared prefix, of the prefix chunks' partials):
 //   M = max_w m_w,  out = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w.
-// One wave per (query head, sequence).  Partials are taken in chunks of 16
-// workgroups: every (m, l) and O load of a chunk is issued before any of them
-// is used, so a chunk costs one memory round trip.
+// One wave per (query head, sequence).  Partials are taken in chunks of 8:
+// every (m, l) and O load of a chunk is issued before any of them is used, so
+// a chunk costs one memory round trip.
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
   constexpr int PER = D / 64;
@@ -484,15 +490,46 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
   // the partials' own)
   const int64_t q_row = p.qsl[b], q_end = p.qsl[b + 1];
   const int32_t cb = p.ws_cum[b], ce = p.ws_cum[b + 1], units = p.ws_cum[p.B];
-  if (q_end == q_row || ce <= cb || units <= 0) return;
+  const bool prefix = p.prefix_len > 0;
+  const bool has_units = ce > cb && units > 0;
+  if (q_end == q_row || (!prefix && !has_units)) return;
   const Partition part(units, p.grid_parts);
-  const int32_t wa = part.owner(cb), wz = part.owner(ce - 1);
-  if (wa == wz) return;  // written directly by decode_kernel
+  int32_t wa = 0, wz = -1;  // workgroups holding the sequence's units (none: wz < wa)
+  if (has_units) {
+    wa = part.owner(cb);
+    wz = part.owner(ce - 1);
+  }
+  if (!prefix && wa == wz) return;  // written directly by decode_kernel
   const f32x2* ml = (const f32x2*)p.ws_ml;
   float M = -INFINITY, l = 0.f;
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  if (prefix) {
+    // the prefix chunks' partials (at most kMaxPrefixChunks), all loads first
+    const f32x2* pml = (const f32x2*)p.ws_pre_ml;
+    f32x2 mlc[kMaxPrefixChunks];
+    float oc[kMaxPrefixChunks][PER];
+#pragma unroll
+    for (int c = 0; c < kMaxPrefixChunks; ++c) {
+      const int64_t slot = ((int64_t)min(c, p.prefix_chunks - 1) * p.B + b) * p.Hq + hq;
+      mlc[c] = pml[slot];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) oc[c][i] = p.ws_pre_o[slot * D + lane + 64 * i];
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxPrefixChunks; ++c) {
+      mlc[c][0] = c < p.prefix_chunks ? mlc[c][0] : -INFINITY;
+      M = fmaxf(M, mlc[c][0]);
+    }
+#pragma unroll
+    for (int c = 0; c < kMaxPrefixChunks; ++c) {
+      const float f = __builtin_amdgcn_exp2f(mlc[c][0] - M);
+      l += f * mlc[c][1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] += f * oc[c][i];
+    }
+  }
   for (int32_t w0 = wa; w0 <= wz; w0 += CHUNK) {
     f32x2 mlw[CHUNK];
     float ow[CHUNK][PER];
@@ -512,7 +549,8 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
       mlw[c][0] = live ? mlw[c][0] : -INFINITY;
       Mc = fmaxf(Mc, mlw[c][0]);
     }
-    const float alpha = __builtin_amdgcn_exp2f(M - Mc);  // rescale what earlier chunks summed
+    // rescale what earlier chunks summed (nothing yet: M = Mc = -inf would give NaN)
+    const float alpha = M == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mc);
     l *= alpha;
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] *= alpha;
@@ -565,6 +603,7 @@ int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu) {
 template <int ESZ, int D>
 static void launch_decode_t(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
   const int threads = 64 * decode_waves(p.Hkv);
+  if (p.prefix_len > 0) (void)launch_prefix_partials(p, stream);
   if (ev.begin) (void)hipEventRecord(ev.begin, stream);
   hipLaunchKernelGGL((decode_kernel<ESZ, D>), dim3((unsigned)p.grid_parts), dim3(threads), 0, stream, p);
   if (ev.end) (void)hipEventRecord(ev.end, stream);

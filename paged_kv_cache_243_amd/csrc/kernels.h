@@ -54,6 +54,13 @@ struct AttnParams {
   float* ws_o;         // [B + grid_parts, Hq, D] unnormalised partial outputs
   // prefill work list
   int32_t* ws_plan;    // prefill tile schedule
+  // shared-prefix decode: the first prefix_len positions of every sequence
+  // are the same pages; their attention runs as MFMA items of (prefix_tiles
+  // groups of sequences) x (prefix_chunks chunks of prefix_chunk_len keys)
+  int64_t prefix_len;  // 0 = off; a multiple of 32
+  int prefix_tiles, prefix_chunks, prefix_chunk_len;
+  float* ws_pre_ml;    // [prefix_chunks, B, Hq, 2] partial (max in log2 units, sum)
+  float* ws_pre_o;     // [prefix_chunks, B, Hq, D] unnormalised partial outputs
 };
 
 // Optional events recorded around the main attention kernel of a launch.
@@ -67,6 +74,7 @@ hipError_t launch_write_fp8(const WriteFp8Params& p, hipStream_t stream);
 hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
+hipError_t launch_prefix_partials(const AttnParams& p, hipStream_t stream);
 
 // workspace helpers shared by the ABI layer and the launchers
 size_t decode_workspace_bytes(int64_t B, int Hq, int D);
@@ -75,6 +83,11 @@ void decode_workspace_carve(AttnParams& p, void* workspace);
 constexpr int kDecodeMaxParts = 2048;
 constexpr int kDecodeMaxSeqs = 4096;
 size_t prefill_workspace_bytes(const AttnParams& p);
+constexpr int kMaxPrefixChunks = 8;
+// groups of decode sequences, chunks and chunk length of a shared prefix of
+// prefix_len positions (fills p.prefix_*), and the partials' workspace bytes
+size_t prefix_plan(AttnParams& p, int64_t prefix_len);
+void prefix_workspace_carve(AttnParams& p, void* region);
 int prefill_tokens_per_tile(int G);
 int64_t prefill_max_items(int64_t T, int64_t B, int G);
 

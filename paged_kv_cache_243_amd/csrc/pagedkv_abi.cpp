@@ -149,6 +149,9 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
   if (max_q == 0 || max_q > T) max_q = T;
   int split = opts ? opts->split_tokens : 0;
   if (split < 0 || split % kPageSize != 0 || split > kMaxSplitTokens) return PKV_ERR_UNSUPPORTED;
+  const int64_t shared_pages = opts ? opts->shared_prefix_pages : 0;
+  if (shared_pages < 0) return PKV_ERR_SHAPE;
+  if (shared_pages % 2 != 0 || shared_pages > max_blocks) return PKV_ERR_UNSUPPORTED;
 
   AttnParams& p = plan.p;
   memset(&p, 0, sizeof p);
@@ -178,6 +181,7 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
     plan.kernel = AttnPlan::kNone;
   } else if (kv == PKV_F32) {
     plan.kernel = AttnPlan::kF32;
+    if (shared_pages > 0) return PKV_ERR_UNSUPPORTED;
   } else if (max_q == 1) {
     plan.kernel = AttnPlan::kDecode;
     if (B > pkv::kDecodeMaxSeqs) return PKV_ERR_UNSUPPORTED;
@@ -185,8 +189,10 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
     if (B * ((max_blocks * kPageSize + 31) / 32) > INT32_MAX) return PKV_ERR_UNSUPPORTED;
     p.split_tokens = split;
     plan.workspace = pkv::decode_workspace_bytes(B, (int)Hq, (int)D);
+    if (shared_pages > 0) plan.workspace += pkv::prefix_plan(p, shared_pages * kPageSize);
   } else {
     plan.kernel = AttnPlan::kPrefill;
+    if (shared_pages > 0) return PKV_ERR_UNSUPPORTED;
     // the prefill kernels index positions with 32-bit integers and its work
     // list packs (sequence, query tile) into 16 + 16 bits
     const int64_t tpt = pkv::prefill_tokens_per_tile((int)G);
@@ -207,7 +213,7 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
 
 extern "C" {
 
-int pkv_abi_version(void) { return 2; }
+int pkv_abi_version(void) { return 3; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -315,6 +321,8 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
       break;
     case AttnPlan::kDecode:
       pkv::decode_workspace_carve(p, opts->workspace);
+      if (p.prefix_len > 0)
+        pkv::prefix_workspace_carve(p, (char*)opts->workspace + pkv::decode_workspace_bytes(p.B, p.Hq, p.D));
       p.grid_parts = pkv::decode_grid_parts(p.B, p.max_blocks * kPageSize, p.split_tokens, device_cu_count());
       err = pkv::launch_decode(p, s, ev);
       break;

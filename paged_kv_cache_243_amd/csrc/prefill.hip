@@ -44,6 +44,8 @@
 //    scale the output normalisation.
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "common.h"
@@ -312,7 +314,12 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-template <int ESZ, int D, int NB>
+// PREFIX: the shared-prefix form of decode (see launch_prefix_partials).  An
+// item is then (group of decode sequences, chunk of the shared prefix): its
+// rows are the query rows of tpt consecutive sequences, its keys the chunk's
+// positions of the prefix pages every block_table row starts with, and it
+// writes an unnormalised partial (m, l, O) per row instead of the output.
+template <int ESZ, int D, int NB, bool PREFIX = false>
 __global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
 void prefill_kernel(AttnParams p) {
   constexpr int WAVES = 8 / NB;            // 32 NB query rows per wave, 256 per workgroup
@@ -328,21 +335,42 @@ void prefill_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char sv[NS][TB];
 
   const int rank = (int)(blockIdx.x / (unsigned)p.Hkv), h = (int)(blockIdx.x % (unsigned)p.Hkv);
-  if (rank >= p.ws_plan[0]) return;
-  const uint32_t item = (uint32_t)p.ws_plan[1 + rank];
-  const int b = (int)(item >> 16), tile = (int)(item & 0xFFFF);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
-  const int tpt = kPrefillRows / G;  // tokens per tile
+  const int tpt = kPrefillRows / G;  // tokens per tile (PREFIX: sequences per item)
 
-  const int64_t q0 = p.qsl[b];
-  const int64_t n = p.qsl[b + 1] - q0;
-  const int64_t L = p.seq_lens[b];
-  const int64_t P = L - n;
-  const int64_t tok0 = (int64_t)tile * tpt;
-  const int64_t tok_end = min(tok0 + (int64_t)tpt, n);
-  const int64_t kv_len = P + tok_end;  // keys some row of this tile sees
+  // b: the sequence (PREFIX: the item's first sequence); tokens tok0 ..
+  // tok_end - 1 of it are the tile's (PREFIX: sequences b + tok), sitting at
+  // positions first_pos + (tok - tok0) (PREFIX: all at the chunk's last
+  // position, so that every key of the chunk and none past it is visible)
+  int b, chunk = 0;
+  int64_t q0, n, L, P, tok0, tok_end;
+  if constexpr (PREFIX) {
+    if (rank >= p.prefix_tiles * p.prefix_chunks) return;
+    const int tile = rank / p.prefix_chunks;
+    chunk = rank - tile * p.prefix_chunks;
+    b = tile * tpt;
+    q0 = 0;
+    tok0 = 0;
+    tok_end = min((int64_t)tpt, p.B - b);
+    const int64_t c0 = (int64_t)chunk * p.prefix_chunk_len;
+    L = min((int64_t)p.prefix_chunk_len, p.prefix_len - c0);  // the chunk's keys
+    n = 0;
+    P = L - 1;
+  } else {
+    if (rank >= p.ws_plan[0]) return;
+    const uint32_t item = (uint32_t)p.ws_plan[1 + rank];
+    b = (int)(item >> 16);
+    const int tile = (int)(item & 0xFFFF);
+    q0 = p.qsl[b];
+    n = p.qsl[b + 1] - q0;
+    L = p.seq_lens[b];
+    P = L - n;
+    tok0 = (int64_t)tile * tpt;
+    tok_end = min(tok0 + (int64_t)tpt, n);
+  }
+  const int64_t kv_len = PREFIX ? L : P + tok_end;  // keys some row of this tile sees
   const int n_tiles = (int)((kv_len + kKeyTile - 1) / kKeyTile);
   const int64_t first_pos = P + tok0;  // position of the tile's first token
   // first key tile that reaches past first_pos, i.e. needs the causal mask
@@ -353,7 +381,9 @@ void prefill_kernel(AttnParams p) {
   c.page_stride = (int64_t)c.row_stride * kPageSize;
   c.kbase = (const char*)p.key_pool + (int64_t)h * D * ESZ;
   c.vbase = (const char*)p.value_pool + (int64_t)h * D * ESZ;
-  c.bt = (const_i64_ptr)(p.block_table + (int64_t)b * p.max_blocks);
+  // (PREFIX: the chunk's pages, from the row of the item's first sequence)
+  c.bt = (const_i64_ptr)(p.block_table + (int64_t)b * p.max_blocks +
+                         (PREFIX ? (int64_t)chunk * p.prefix_chunk_len / kPageSize : 0));
   c.L = (int)L;
   c.last_page = (int)((L + 15) >> 4) - 1;
 
@@ -370,6 +400,7 @@ void prefill_kernel(AttnParams p) {
   const int qcol = lane & 31, qgrp = lane >> 5;
   bf16x8 qb[NB][NKS];
   int32_t qrel[NB];  // row position - first_pos - 4 qgrp
+  bool row_live[NB];
   // (called once the first tile fetches are in flight; every lane loads, rows
   // past the tile from the sequence's first token, so that the loads issue
   // together rather than one exec-masked load and wait at a time)
@@ -378,9 +409,21 @@ void prefill_kernel(AttnParams p) {
     for (int nb = 0; nb < NB; ++nb) {
       const int r = wave * 32 * NB + nb * 32 + qcol;
       const int64_t tok = tok0 + r / G;
-      const bool live = r < tpt * G && tok < tok_end;
-      qrel[nb] = (int32_t)((live ? tok : tok_end - 1) - tok0) - 4 * qgrp;
-      const __bf16* qrow = (const __bf16*)p.q + ((q0 + (live ? tok : 0)) * p.Hq + h * G + r % G) * D;
+      bool live = r < tpt * G && tok < tok_end;
+      int64_t qidx;  // packed query row of this lane's row
+      if constexpr (PREFIX) {
+        // sequence b + tok, if it has a query row
+        const int64_t bs = live ? b + tok : b;
+        const int64_t qa = p.qsl[bs], qz = p.qsl[bs + 1];
+        live = live && qz > qa;
+        qidx = live ? qa : 0;
+        qrel[nb] = -4 * qgrp;
+      } else {
+        qidx = q0 + (live ? tok : 0);
+        qrel[nb] = (int32_t)((live ? tok : tok_end - 1) - tok0) - 4 * qgrp;
+      }
+      row_live[nb] = live;
+      const __bf16* qrow = (const __bf16*)p.q + (qidx * p.Hq + h * G + r % G) * D;
       u32x4 raw[NKS];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) raw[ks] = *(const u32x4*)(qrow + 16 * ks + 8 * qgrp);
@@ -728,6 +771,32 @@ void prefill_kernel(AttnParams p) {
   // acc[d][nb][i] = O^T[dim 32 d + 8 (i / 4) + 4 qgrp + i % 4][row]
   float out_scale = 1.0f;
   if constexpr (ESZ == 1) out_scale = p.v_scale[h];
+  if constexpr (PREFIX) {
+    // partial of (chunk, sequence, query head): m_ref in log2 units, the row
+    // sum of the rounded P and the unnormalised O, as the merge expects them
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float l = sum_pair(l_run[nb]);
+      if (!row_live[nb]) continue;
+      const int r = wave * 32 * NB + nb * 32 + qcol;
+      const int64_t slot = ((int64_t)chunk * p.B + b + r / G) * p.Hq + h * G + r % G;
+      float* orow = p.ws_pre_o + slot * D;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[d][nb][4 * i4 + e] * out_scale;
+          *(f32x4*)(orow + d * 32 + 8 * i4 + 4 * qgrp) = o;
+        }
+      if (qgrp == 0) {
+        p.ws_pre_ml[2 * slot] = m_ref[nb];
+        p.ws_pre_ml[2 * slot + 1] = l;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float l = sum_pair(l_run[nb]);
@@ -746,6 +815,45 @@ void prefill_kernel(AttnParams p) {
         *(u32x2*)(orow + d * 32 + 8 * i4 + 4 * qgrp) = w;
       }
   }
+}
+
+// Shared-prefix decode, prefix part: one item per (group of prefill_tokens_per_tile
+// sequences, chunk of the prefix).  The chunk count is chosen for about 256
+// workgroups whatever the device, so the workspace size depends on the shapes
+// only.
+size_t prefix_plan(AttnParams& p, int64_t prefix_len) {
+  const int tpt = prefill_tokens_per_tile(p.G);
+  p.prefix_len = prefix_len;
+  p.prefix_tiles = (int)((p.B + tpt - 1) / tpt);
+  const int64_t per_chunk = (int64_t)p.prefix_tiles * p.Hkv;
+  int64_t chunks = (256 + per_chunk - 1) / per_chunk;
+  chunks = std::max<int64_t>(1, std::min<int64_t>({chunks, (int64_t)kMaxPrefixChunks, prefix_len / kKeyTile}));
+  const int64_t len = (prefix_len / chunks + kKeyTile - 1) / kKeyTile * kKeyTile;
+  p.prefix_chunk_len = (int)len;
+  p.prefix_chunks = (int)((prefix_len + len - 1) / len);
+  const size_t slots = (size_t)p.prefix_chunks * p.B * p.Hq;
+  return (slots * 2 * sizeof(float) + 255) / 256 * 256 + slots * p.D * sizeof(float);
+}
+
+void prefix_workspace_carve(AttnParams& p, void* region) {
+  const size_t slots = (size_t)p.prefix_chunks * p.B * p.Hq;
+  p.ws_pre_ml = (float*)region;
+  p.ws_pre_o = (float*)((char*)region + (slots * 2 * sizeof(float) + 255) / 256 * 256);
+}
+
+hipError_t launch_prefix_partials(const AttnParams& p, hipStream_t stream) {
+  const dim3 grid((unsigned)((int64_t)p.prefix_tiles * p.prefix_chunks * p.Hkv));
+  constexpr int NB = kPrefillRowBlocks;
+  const dim3 block(512 / NB);
+  const bool fp8 = p.kv_type == KV_FP8;
+  if (p.D == 128) {
+    if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 128, NB, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_kernel<2, 128, NB, true>), grid, block, 0, stream, p);
+  } else {
+    if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 64, NB, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((prefill_kernel<2, 64, NB, true>), grid, block, 0, stream, p);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {

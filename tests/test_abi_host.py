@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(B.EXPORTS) == names
-    assert lib.pkv_abi_version() == 2
+    assert lib.pkv_abi_version() == 3
 
 
 def T(shape, dtype, ptr=FAKE):
@@ -277,6 +277,50 @@ def test_workspace_size():
     assert ws(opts(max_query_len=7)) == (1 + 64 + (64 + 63) // 64) * 4
     # invalid arguments
     assert ws(opts(max_query_len=1, split_tokens=20)) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("pages,max_q,status", [
+    (3, 1, -4),       # odd: units are 32 positions
+    (258, 1, -4),     # more than max_blocks
+    (-2, 1, -2),
+    (4, 7, -4),       # prefill calls have no shared-prefix form
+])
+def test_shared_prefix_argument_errors(pages, max_q, status):
+    lib = pkv.load()
+    q, kp = T([64, 32, 128], B.PKV_BF16), T([65536, 16, 8, 128], B.PKV_BF16)
+    bt = T([64, 256], B.PKV_I64)
+    o = B.PkvAttnOpts()
+    o.max_query_len = max_q
+    o.shared_prefix_pages = pages
+    n = lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt), ctypes.byref(o))
+    assert n == ctypes.c_size_t(-1).value
+    a = attn_args(q=q, kp=kp, vp=T([65536, 16, 8, 128], B.PKV_BF16), bt=bt, sl=T([64], B.PKV_I64),
+                  qsl=T([65], B.PKV_I64), out=T([64, 32, 128], B.PKV_BF16))
+    a["opts"] = o
+    assert call_attn(a) == status
+
+
+def test_shared_prefix_workspace_size():
+    """decode workspace plus the prefix partials: chunks x B x Hq slots of
+    (m, l) and D floats; 64 decode rows of G = 4 make one group of 64
+    sequences, 8 KV heads -> 8 workgroups per chunk, so 32 chunks are wanted
+    for 256 workgroups, capped by the 2 chunks of 32 positions a 4-page prefix
+    holds."""
+    lib = pkv.load()
+    q, kp = T([64, 32, 128], B.PKV_BF16), T([65536, 16, 8, 128], B.PKV_BF16)
+    bt = T([64, 256], B.PKV_I64)
+    o = B.PkvAttnOpts()
+    o.max_query_len = 1
+    base = lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt), ctypes.byref(o))
+    o.shared_prefix_pages = 4
+    with_prefix = lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt), ctypes.byref(o))
+    slots = 2 * 64 * 32
+    assert with_prefix - base == (slots * 8 + 255) // 256 * 256 + slots * 128 * 4
+    # a 128-page prefix: min(32 wanted, 8 cap, 64 units) = 8 chunks of 256 positions
+    o.shared_prefix_pages = 128
+    big = lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt), ctypes.byref(o))
+    slots = 8 * 64 * 32
+    assert big - base == (slots * 8 + 255) // 256 * 256 + slots * 128 * 4
 
 
 def test_status_strings():
