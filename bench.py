@@ -147,13 +147,15 @@ class Fp8WriteRunner:
 class Runner:
     """Write + attention of one workload with preallocated buffers."""
 
-    def __init__(self, pkv, w, torch):
+    def __init__(self, pkv, w, torch, shared_prefix_pages=0):
         self.pkv, self.w, self.torch = pkv, w, torch
+        self.shared = shared_prefix_pages
         self.kp, self.vp = w.key_pool, w.value_pool  # written in place each step (same rows)
         self.out = torch.empty_like(w.q)
         need = pkv.paged_attention_workspace_size(w.q, w.key_pool, w.block_table,
                                                   max_query_len=w.max_query_len,
-                                                  split_tokens=w.split_tokens)
+                                                  split_tokens=w.split_tokens,
+                                                  shared_prefix_pages=shared_prefix_pages)
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.q.device)
 
     def write(self):
@@ -165,7 +167,8 @@ class Runner:
         self.pkv.paged_attention(w.q, self.kp, self.vp, w.block_table, w.seq_lens, w.query_start_loc,
                                  w.scale, self.out, k_scale=w.k_scale, v_scale=w.v_scale,
                                  max_query_len=w.max_query_len, split_tokens=w.split_tokens,
-                                 workspace=self.ws, timing_events=kernel_events)
+                                 workspace=self.ws, timing_events=kernel_events,
+                                 shared_prefix_pages=self.shared)
 
 
 class Times:
@@ -275,7 +278,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-extra", action="store_true", help="time only the decode workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
-    ap.add_argument("--profile-workload", choices=["decode", "prefill", "shared", "fp8", "fp8write"],
+    ap.add_argument("--profile-workload", choices=["decode", "prefill", "shared", "sharedplain", "fp8", "fp8write"],
                     help="time one workload only and print its median times (for profiler runs)")
     args = ap.parse_args(argv)
 
@@ -304,14 +307,16 @@ def main(argv=None) -> int:
                           "write_ms_mean": statistics.fmean(t.write)}), flush=True)
         return 0
     if args.profile_workload:
-        cid = {"decode": 2, "prefill": 3, "shared": 4, "fp8": 5}[args.profile_workload]
+        cid = {"decode": 2, "prefill": 3, "shared": 4, "sharedplain": 4, "fp8": 5}[args.profile_workload]
         w = W.generate(cid, dev)
         # calibration for hardware byte counters: a plain device copy of known
         # size (256 MiB read + 256 MiB written), launched once
         calib = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
         torch.empty_like(calib).copy_(calib)
         del calib
-        t = time_steps(Runner(pkv, w, torch), torch, args.steps, args.warmup, flush, args.profile_workload)
+        pages = w.cfg.shared_prefix_tokens // w.cfg.page_size if args.profile_workload == "shared" else 0
+        t = time_steps(Runner(pkv, w, torch, shared_prefix_pages=pages), torch, args.steps, args.warmup, flush,
+                       args.profile_workload)
         print(json.dumps({"workload": w.cfg.name, "write_ms_median": statistics.median(t.write),
                           "attention_ms_median": statistics.median(t.attn),
                           "main_kernel_ms_median": statistics.median(t.kernel),
@@ -426,17 +431,26 @@ def main(argv=None) -> int:
         # shared-prefix decode
         log("generating shared-prefix decode workload (config 4)")
         w4 = W.generate(4, dev)
-        r4 = Runner(pkv, w4, torch)
+        pages4 = w4.cfg.shared_prefix_tokens // w4.cfg.page_size
+        r4 = Runner(pkv, w4, torch, shared_prefix_pages=pages4)
         t4 = time_steps(r4, torch, args.steps, args.warmup, flush, "shared-prefix decode", kernel_events=False)
+        r4p = Runner(pkv, w4, torch)
+        t4p = time_steps(r4p, torch, args.steps, args.warmup, flush, "shared-prefix decode, plain call",
+                         kernel_events=False)
         a4 = statistics.median(t4.attn)
+        a4p = statistics.median(t4p.attn)
         extra["shared_prefix_decode"] = {
             "workload": "256 sequences sharing 128 prefix pages + U{0..512} private tokens, Hq 64, Hkv 8",
+            "form": f"shared_prefix_pages={pages4}: prefix once as MFMA tiles + split-K decode of the rest + merge",
             "unit": "GB/s",
             "logical_GBps": round(decode_bytes(w4) / (a4 * 1e-3) / 1e9, 1),
             "unique_GBps": round(unique_decode_bytes(w4) / (a4 * 1e-3) / 1e9, 1),
             "attention_ms_median": round(a4, 5),
             "step_ms_median": round(statistics.median(t4.step), 5),
+            "plain_call_attention_ms_median": round(a4p, 5),
+            "plain_call_logical_GBps": round(decode_bytes(w4) / (a4p * 1e-3) / 1e9, 1),
         }
+        del r4p
         del r4, w4
         torch.cuda.empty_cache()
         # long-context fp8 decode
