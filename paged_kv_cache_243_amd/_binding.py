@@ -22,6 +22,7 @@ STATUS = {
     0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_DTYPE",
     -4: "PKV_ERR_UNSUPPORTED", -5: "PKV_ERR_SCALE", -6: "PKV_ERR_WORKSPACE",
     -7: "PKV_ERR_HIP", -8: "PKV_ERR_INDEX",
+    -20: "PKV_ERR_NO_PAGES", -21: "PKV_ERR_BAD_HANDLE", -22: "PKV_ERR_DIRTY",
 }
 # every symbol include/pagedkv.h declares
 EXPORTS = ("paged_kv_write", "paged_kv_write_fp8", "paged_attention", "paged_attention_workspace_size",

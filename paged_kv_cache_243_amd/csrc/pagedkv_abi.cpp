@@ -12,6 +12,7 @@
 
 #include "kernels.h"
 #include "pagedkv.h"
+#include "pagedkv_host.h"
 
 using pkv::AttnParams;
 using pkv::WriteParams;
@@ -226,6 +227,9 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_INDEX: return "index value out of range";
+    case PKV_ERR_NO_PAGES: return "too few free pages";
+    case PKV_ERR_BAD_HANDLE: return "stale or unknown handle, or a page released more often than held";
+    case PKV_ERR_DIRTY: return "a page to describe is dirty (not confirmed overwritten since it was freed)";
     default: return "unknown status";
   }
 }

@@ -81,3 +81,64 @@ def test_shared_prefix_matches_the_plain_call(gpu):
     assert_close(a, ref, "bf16", "shared prefix form")
     assert_close(b, ref, "bf16", "plain form")
     assert float((a.float() - b.float()).abs().max()) <= 2e-2
+
+
+def test_control_plane_batch_through_the_kernels(gpu):
+    """Metadata from the host control plane driving the GPU path: a 3-page
+    prompt prefix written once and published in the prefix index; 8 requests
+    match it, append their own prompt tokens (one chunked-prefill call over
+    the batch), then one decode token each (a shared-prefix decode call).
+    Both calls against the oracle on the same pools."""
+    note("control plane batch through the kernels")
+    from paged_kv_cache_243_amd import host as Hs
+    import oracle
+    rng = np.random.default_rng(12)
+    ps, num_pages, Hkv, Hq, D = 16, 512, 8, 32, 128
+    pool = Hs.PagePool(num_pages, ps)
+    kp = torch.zeros((num_pages, ps, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    vp = torch.zeros_like(kp)
+    gen = torch.Generator(device="cpu").manual_seed(5)
+
+    def write(slots):
+        n = len(slots)
+        k = torch.randn((n, Hkv, D), generator=gen).to(torch.bfloat16).to(DEV)
+        v = torch.randn((n, Hkv, D), generator=gen).to(torch.bfloat16).to(DEV)
+        gpu.paged_kv_write(k, v, torch.as_tensor(slots, device=DEV), kp, vp)
+
+    ns = 0xABCD
+    prefix = np.arange(3 * ps, dtype=np.int32) + 7
+    owner = pool.create()
+    write(pool.append(owner, len(prefix)))
+    pool.prefix_insert(ns, owner, prefix)
+    pool.release_seq(owner)
+    seqs, rest = [], []
+    for r in range(8):
+        prompt = np.concatenate([prefix, rng.integers(0, 999, size=int(rng.integers(1, 70))).astype(np.int32)])
+        s, matched = pool.prefix_match(ns, prompt)
+        assert matched == len(prefix)
+        n = len(prompt) - matched
+        write(pool.append(s, n))
+        pool.confirm(pool.pages(s))
+        seqs.append(s)
+        rest.append(n)
+    max_blocks = 16
+
+    def run(n_new, shared):
+        bt, sl, qsl = pool.build_step(seqs, n_new, max_blocks, num_pages - 1)
+        T = int(qsl[-1])
+        q = torch.randn((T, Hq, D), generator=gen).to(torch.bfloat16).to(DEV)
+        out = torch.empty_like(q)
+        gpu.paged_attention(q, kp, vp, torch.as_tensor(bt, device=DEV), torch.as_tensor(sl, device=DEV),
+                            torch.as_tensor(qsl, device=DEV), D ** -0.5, out, max_query_len=int(max(n_new)),
+                            shared_prefix_pages=shared)
+        torch.cuda.synchronize()
+        ref = oracle.paged_attention(H.S(q), "bf16", H.S(kp), H.S(vp), "bf16", bt, sl, qsl, D ** -0.5)
+        return out, ref
+
+    out, ref = run(rest, 0)
+    assert_close(out, ref, "bf16", "control plane: prefill continuation")
+    for s in seqs:
+        write(pool.append(s, 1))
+        pool.confirm(pool.pages(s))
+    out, ref = run([1] * len(seqs), len(prefix) // ps - 1)   # an even page count
+    assert_close(out, ref, "bf16", "control plane: shared-prefix decode")
