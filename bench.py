@@ -270,6 +270,35 @@ def cpu_baseline(w):
                       f"{w.k_new.shape[0]} tokens + attention of every row), fp64, median of {len(times)} runs"}
 
 
+def host_control_plane_timing() -> dict:
+    """Host cost of one decode step's bookkeeping in the C++ control plane for
+    the decode workload's shape: 64 sequences of U{512..4096} tokens in a
+    65536-page pool, each appending one token, then the step metadata built
+    (block_table [64, 272], seq_lens, query_start_loc)."""
+    import numpy as np
+    from paged_kv_cache_243_amd.host import PagePool
+    rng = np.random.default_rng(243_002)
+    pool = PagePool(65536, 16)
+    seqs = []
+    for _ in range(64):
+        s = pool.create()
+        pool.append(s, int(rng.integers(511, 4096)))
+        seqs.append(s)
+    pool.confirm(np.concatenate([pool.pages(s) for s in seqs]))
+    n_new = np.ones(64, dtype=np.int64)
+    times = []
+    for _ in range(200):
+        t0 = time.perf_counter()
+        for s in seqs:
+            pool.append(s, 1)
+        pool.build_step(seqs, n_new, 272, 65535)
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    return {"workload": "64 sequences append one token each, then the step metadata is built "
+                        "(block_table [64, 272]); C++ control plane called from Python",
+            "us_per_step_median": round(times[len(times) // 2] * 1e6, 1)}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -479,6 +508,9 @@ def main(argv=None) -> int:
         del r5, w5
         torch.cuda.empty_cache()
         result.update(extra)
+
+    if not args.no_extra:
+        result["host_control_plane"] = host_control_plane_timing()
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the decode workload")
