@@ -86,6 +86,8 @@ def open_library(path: str):
     lib.orc_e4m3fn_encode_array.restype = None
     lib.orc_paged_kv_write_fp8.argtypes = [vp, vp, vp, i64, vp, vp, vp, vp, i64, i64, i64, i64]
     lib.orc_paged_kv_write_fp8.restype = i32
+    lib.orc_block_table_from_csr.argtypes = [vp, vp, i64, vp, i64, i64, i64, i64, vp, vp]
+    lib.orc_block_table_from_csr.restype = i32
     lib.orc_max_threads.argtypes = []
     lib.orc_max_threads.restype = i32
     return lib
@@ -173,6 +175,22 @@ def paged_kv_write_fp8(k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray,
                                         _ptr(key_pool), _ptr(value_pool), num_pages, page_size, Hkv, D)
     if st != 0:
         raise OracleError(st)
+
+
+def block_table_from_csr(kv_indptr: np.ndarray, kv_indices: np.ndarray, kv_last_page_len: np.ndarray,
+                         page_size: int, pad_page: int, max_blocks: int) -> tuple[np.ndarray, np.ndarray]:
+    """(block_table [B, max_blocks], seq_lens [B]) from the packed page list."""
+    ip = np.ascontiguousarray(kv_indptr, dtype=np.int64)
+    ix = np.ascontiguousarray(kv_indices, dtype=np.int64)
+    ll = np.ascontiguousarray(kv_last_page_len, dtype=np.int64)
+    B = ip.shape[0] - 1
+    bt = np.empty((B, int(max_blocks)), dtype=np.int64)
+    sl = np.empty(B, dtype=np.int64)
+    st = _load().orc_block_table_from_csr(_ptr(ip), _ptr(ix) if ix.size else None, ix.size, _ptr(ll), B,
+                                          int(page_size), int(pad_page), int(max_blocks), _ptr(bt), _ptr(sl))
+    if st != 0:
+        raise OracleError(st)
+    return bt, sl
 
 
 def paged_attention(q: np.ndarray, q_dtype: str, key_pool: np.ndarray, value_pool: np.ndarray,

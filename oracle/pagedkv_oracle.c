@@ -213,6 +213,35 @@ int orc_paged_kv_write_fp8(const uint16_t* k, const uint16_t* v, const int64_t* 
 }
 
 /*
+ * The packed (CSR) page-list form of the metadata, unpacked into the
+ * row-padded block table: sequence b's pages are
+ * indices[indptr[b] .. indptr[b+1]) and its last page holds last_len[b] rows
+ * (page "Refactor KV Cache Manager with a new torch exportable KVCache
+ * backend", NVIDIA/recsys-examples #400, the KVCacheMetadata fields
+ * kv_indices, kv_indptr, kv_last_page_len).  Rows are padded with pad_page;
+ * a sequence with no page has length 0.  Inconsistent metadata (indptr
+ * decreasing or past nnz, more than max_blocks pages, a last-page length
+ * outside 1..page_size) is rejected.
+ */
+int orc_block_table_from_csr(const int64_t* indptr, const int64_t* indices, int64_t nnz, const int64_t* last_len,
+                             int64_t B, int64_t page_size, int64_t pad_page, int64_t max_blocks,
+                             int64_t* block_table, int64_t* seq_lens) {
+  if (indptr[0] != 0) return ORC_ERR_METADATA;
+  for (int64_t b = 0; b < B; ++b) {
+    int64_t n = indptr[b + 1] - indptr[b];
+    if (n < 0 || indptr[b + 1] > nnz || n > max_blocks) return ORC_ERR_METADATA;
+    if (n > 0 && (last_len[b] < 1 || last_len[b] > page_size)) return ORC_ERR_METADATA;
+  }
+  for (int64_t b = 0; b < B; ++b) {
+    int64_t n = indptr[b + 1] - indptr[b];
+    for (int64_t j = 0; j < max_blocks; ++j)
+      block_table[b * max_blocks + j] = j < n ? indices[indptr[b] + j] : pad_page;
+    seq_lens[b] = n > 0 ? (n - 1) * page_size + last_len[b] : 0;
+  }
+  return ORC_OK;
+}
+
+/*
  * Steps 2 and 3: gather and attend.
  *
  *   q                [T, Hq, D]            q_dtype (f32 or bf16)

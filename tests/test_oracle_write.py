@@ -118,3 +118,44 @@ def test_quantising_write_rejects_bad_slots_before_writing():
             oracle.paged_kv_write_fp8(k, k, np.array(slots, dtype=np.int64), ones, ones, kp, vp)
         assert e.value.status == status
         assert (kp == 0x7F).all() and (vp == 0x7F).all()
+
+
+def pack_csr(block_table, seq_lens, page_size=16):
+    """The row-padded table packed into the contiguous page list (what the
+    maxtext kernels are handed), in plain numpy."""
+    n = (seq_lens + page_size - 1) // page_size
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    indices = np.concatenate([block_table[b, :n[b]] for b in range(len(n))] + [np.zeros(0, np.int64)])
+    last = np.where(n > 0, seq_lens - (n - 1) * page_size, 0).astype(np.int64)
+    return indptr, indices.astype(np.int64), last
+
+
+@pytest.mark.parametrize("cid", [2, 4, 5])
+def test_csr_unpacking_inverts_the_packing(cid):
+    """Unpacking the page list packed from a workload's table gives back the
+    table's reached entries and the lengths exactly."""
+    w = W.generate(W.SMALL[cid], "cpu")
+    bt, sl = S(w.block_table), S(w.seq_lens)
+    indptr, indices, last = pack_csr(bt, sl)
+    bt2, sl2 = oracle.block_table_from_csr(indptr, indices, last, 16, -7, bt.shape[1])
+    assert np.array_equal(sl2, sl)
+    for b in range(len(sl)):
+        n = -(-int(sl[b]) // 16)
+        assert np.array_equal(bt2[b, :n], bt[b, :n]) and (bt2[b, n:] == -7).all()
+
+
+def test_csr_unpacking_edge_cases_and_rejections():
+    indptr = np.array([0, 0, 1, 3], dtype=np.int64)
+    indices = np.array([5, 9, 2], dtype=np.int64)
+    last = np.array([0, 16, 1], dtype=np.int64)
+    bt, sl = oracle.block_table_from_csr(indptr, indices, last, 16, 0, 2)
+    assert sl.tolist() == [0, 16, 17] and bt.tolist() == [[0, 0], [5, 0], [9, 2]]
+    bad = [(np.array([0, 2, 1, 3]), last),               # decreasing
+           (indptr, np.array([0, 17, 1])),               # last page longer than a page
+           (indptr, np.array([0, 0, 1])),                # a non-empty sequence with an empty last page
+           (np.array([0, 0, 1, 4]), last)]               # past the end of the index array
+    for ip, ll in bad:
+        with pytest.raises(oracle.OracleError):
+            oracle.block_table_from_csr(ip, indices, ll, 16, 0, 2)
+    with pytest.raises(oracle.OracleError):                # more pages than the row holds
+        oracle.block_table_from_csr(indptr, indices, last, 16, 0, 1)
