@@ -217,6 +217,39 @@ size_t paged_attention_workspace_size(const pkv_tensor* q, const pkv_tensor* key
                                       const pkv_tensor* block_table, const pkv_attn_opts* opts);
 
 /*
+ * paged_block_table_from_csr -- block_table and seq_lens from the packed
+ * (CSR) page-list form of the same metadata.
+ *
+ * Sequence b's pages are kv_indices[kv_indptr[b] .. kv_indptr[b+1]) in order
+ * (n_b of them) and its last page holds kv_last_page_len[b] rows, so
+ *     block_table[b][j] = kv_indices[kv_indptr[b] + j]  for j < n_b, else pad_page
+ *     seq_lens[b]       = (n_b - 1) * page_size + kv_last_page_len[b]  (0 if n_b = 0)
+ * (page "Refactor KV Cache Manager with a new torch exportable KVCache
+ * backend", NVIDIA/recsys-examples #400, the KVCacheMetadata fields kv_indices,
+ * kv_indptr and kv_last_page_len; page "[Draft] kv paged kernels",
+ * ROCm/maxtext #93, converts a row-padded table into this packed page list
+ * for its kernels, the reverse of this call).  The result feeds
+ * paged_attention directly.
+ *
+ *   kv_indptr         [B+1]               PKV_I64, non-decreasing from 0
+ *   kv_indices        [nnz]               PKV_I64, nnz >= kv_indptr[B]
+ *   kv_last_page_len  [B]                 PKV_I64, in 1..page_size for n_b > 0
+ *   block_table       [B, max_blocks]     PKV_I64, written
+ *   seq_lens          [B]                 PKV_I64, written
+ *
+ * Index values live in device memory and are not checked here (a sequence
+ * with more than max_blocks pages, or a last-page length outside
+ * 1..page_size, is a caller error); for memory safety its row is cut at
+ * max_blocks pages and its length clamped to its row's pages, so what
+ * paged_attention reads stays inside block_table, and page ids are read only
+ * inside kv_indices.  Returns PKV_OK or a
+ * negative status for bad arguments; one kernel is enqueued on `stream`.
+ */
+int paged_block_table_from_csr(const pkv_tensor* kv_indptr, const pkv_tensor* kv_indices,
+                               const pkv_tensor* kv_last_page_len, int64_t page_size, int64_t pad_page,
+                               pkv_tensor* block_table, pkv_tensor* seq_lens, void* stream);
+
+/*
  * paged_validate_metadata -- debug check of index values in device memory.
  * Synchronises `stream`, copies the index tensors to the host and checks:
  * every slot in [-1 .. num_pages*page_size), no duplicate non-negative slot,

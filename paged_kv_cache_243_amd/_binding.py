@@ -25,7 +25,7 @@ STATUS = {
     -20: "PKV_ERR_NO_PAGES", -21: "PKV_ERR_BAD_HANDLE", -22: "PKV_ERR_DIRTY",
 }
 # every symbol include/pagedkv.h declares
-EXPORTS = ("paged_kv_write", "paged_kv_write_fp8", "paged_attention", "paged_attention_workspace_size",
+EXPORTS = ("paged_kv_write", "paged_kv_write_fp8", "paged_block_table_from_csr", "paged_attention", "paged_attention_workspace_size",
            "paged_validate_metadata", "pkv_check_metadata_host", "pkv_status_string",
            "pkv_abi_version")
 
@@ -65,6 +65,8 @@ def load() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         lib.paged_kv_write.argtypes = [P, P, P, P, P, vp]
         lib.paged_kv_write.restype = i32
+        lib.paged_block_table_from_csr.argtypes = [P, P, P, i64, i64, P, P, vp]
+        lib.paged_block_table_from_csr.restype = i32
         lib.paged_kv_write_fp8.argtypes = [P, P, P, P, P, vp, vp, vp]
         lib.paged_kv_write_fp8.restype = i32
         lib.paged_attention.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, ctypes.POINTER(PkvAttnOpts), vp]
@@ -136,6 +138,17 @@ def paged_kv_write_fp8(k, v, slot_mapping, key_pool, value_pool, k_scale, v_scal
     st = lib.paged_kv_write_fp8(describe(k), describe(v), describe(slot_mapping), describe(key_pool),
                                 describe(value_pool), k_scale.data_ptr(), v_scale.data_ptr(), _stream(key_pool))
     _check(st, "paged_kv_write_fp8")
+
+
+def paged_block_table_from_csr(kv_indptr, kv_indices, kv_last_page_len, block_table, seq_lens, *,
+                               page_size=16, pad_page=0) -> None:
+    """Fill block_table [B, max_blocks] and seq_lens [B] (int64 device tensors)
+    from the packed page-list form of the metadata."""
+    lib = load()
+    st = lib.paged_block_table_from_csr(describe(kv_indptr), describe(kv_indices), describe(kv_last_page_len),
+                                        int(page_size), int(pad_page), describe(block_table), describe(seq_lens),
+                                        _stream(block_table))
+    _check(st, "paged_block_table_from_csr")
 
 
 def _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_events=None,

@@ -75,6 +75,10 @@ hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEv
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_prefix_partials(const AttnParams& p, hipStream_t stream);
+hipError_t launch_csr_to_block_table(const int64_t* indptr, const int64_t* indices, const int64_t* last_len,
+                                     int64_t nnz, int64_t B, int64_t max_blocks, int64_t page_size,
+                                     int64_t pad_page, int64_t* block_table, int64_t* seq_lens,
+                                     hipStream_t stream);
 
 // workspace helpers shared by the ABI layer and the launchers
 size_t decode_workspace_bytes(int64_t B, int Hq, int D);

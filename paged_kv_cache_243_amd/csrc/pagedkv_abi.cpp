@@ -293,6 +293,34 @@ int paged_kv_write_fp8(const pkv_tensor* k, const pkv_tensor* v, const pkv_tenso
   return pkv::launch_write_fp8(p, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
+int paged_block_table_from_csr(const pkv_tensor* kv_indptr, const pkv_tensor* kv_indices,
+                               const pkv_tensor* kv_last_page_len, int64_t page_size, int64_t pad_page,
+                               pkv_tensor* block_table, pkv_tensor* seq_lens, void* stream) {
+  PKV_TRY(check_tensor(kv_indptr, 1, 8));
+  PKV_TRY(check_tensor(kv_indices, 1, 8));
+  PKV_TRY(check_tensor(kv_last_page_len, 1, 8));
+  PKV_TRY(check_tensor(block_table, 2, 8));
+  PKV_TRY(check_tensor(seq_lens, 1, 8));
+  if (kv_indptr->dtype != PKV_I64 || kv_indices->dtype != PKV_I64 || kv_last_page_len->dtype != PKV_I64 ||
+      block_table->dtype != PKV_I64 || seq_lens->dtype != PKV_I64)
+    return PKV_ERR_DTYPE;
+  const int64_t B = block_table->shape[0], max_blocks = block_table->shape[1];
+  if (kv_indptr->shape[0] != B + 1 || kv_last_page_len->shape[0] != B || seq_lens->shape[0] != B)
+    return PKV_ERR_SHAPE;
+  if (page_size <= 0) return PKV_ERR_SHAPE;
+  if (B == 0 || max_blocks == 0) {
+    if (B > 0 && max_blocks == 0) return PKV_ERR_SHAPE;  // lengths need a row to live in
+    return PKV_OK;
+  }
+  return pkv::launch_csr_to_block_table((const int64_t*)kv_indptr->data, (const int64_t*)kv_indices->data,
+                                        (const int64_t*)kv_last_page_len->data, kv_indices->shape[0], B, max_blocks,
+                                        page_size, pad_page,
+                                        (int64_t*)block_table->data, (int64_t*)seq_lens->data,
+                                        (hipStream_t)stream) == hipSuccess
+             ? PKV_OK
+             : PKV_ERR_HIP;
+}
+
 size_t paged_attention_workspace_size(const pkv_tensor* q, const pkv_tensor* key_pool,
                                       const pkv_tensor* block_table, const pkv_attn_opts* opts) {
   AttnPlan plan;

@@ -323,6 +323,52 @@ def test_shared_prefix_workspace_size():
     assert big - base == (slots * 8 + 255) // 256 * 256 + slots * 128 * 4
 
 
+@pytest.mark.parametrize("case,status", [
+    ("null indptr", -1),
+    ("indptr length", -2),
+    ("last length", -2),
+    ("seq_lens length", -2),
+    ("table rank", -2),
+    ("no row for the lengths", -2),
+    ("page size", -2),
+    ("i32 indices", -3),
+    ("bf16 table", -3),
+])
+def test_block_table_from_csr_argument_errors(case, status):
+    lib = pkv.load()
+    a = dict(ip=T([5], B.PKV_I64), ix=T([30], B.PKV_I64), ll=T([4], B.PKV_I64), bt=T([4, 8], B.PKV_I64),
+             sl=T([4], B.PKV_I64), ps=16)
+    if case == "null indptr":
+        a["ip"] = None
+    elif case == "indptr length":
+        a["ip"] = T([4], B.PKV_I64)
+    elif case == "last length":
+        a["ll"] = T([5], B.PKV_I64)
+    elif case == "seq_lens length":
+        a["sl"] = T([3], B.PKV_I64)
+    elif case == "table rank":
+        a["bt"] = T([32], B.PKV_I64)
+    elif case == "no row for the lengths":
+        a["bt"] = T([4, 0], B.PKV_I64)
+    elif case == "page size":
+        a["ps"] = 0
+    elif case == "i32 indices":
+        a["ix"] = T([30], B.PKV_BF16)
+    elif case == "bf16 table":
+        a["bt"] = T([4, 8], B.PKV_BF16)
+    P = lambda t: ctypes.byref(t) if t is not None else None
+    assert lib.paged_block_table_from_csr(P(a["ip"]), P(a["ix"]), P(a["ll"]), a["ps"], 0, P(a["bt"]), P(a["sl"]),
+                                          None) == status
+
+
+def test_block_table_from_csr_with_no_sequences_is_a_no_op():
+    lib = pkv.load()
+    P = ctypes.byref
+    assert lib.paged_block_table_from_csr(P(T([1], B.PKV_I64)), P(T([0], B.PKV_I64, None)),
+                                          P(T([0], B.PKV_I64, None)), 16, 0, P(T([0, 8], B.PKV_I64, None)),
+                                          P(T([0], B.PKV_I64, None)), None) == 0
+
+
 def test_status_strings():
     lib = pkv.load()
     for st, name in B.STATUS.items():
