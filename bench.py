@@ -270,6 +270,35 @@ def cpu_baseline(w):
                       f"{w.k_new.shape[0]} tokens + attention of every row), fp64, median of {len(times)} runs"}
 
 
+def csr_unpack_timing(pkv, w, torch, steps: int) -> dict:
+    """The decode workload's metadata given in the packed page-list form
+    (kv_indptr, kv_indices, kv_last_page_len) and unpacked on the GPU into
+    block_table [64, 256] and seq_lens; HIP events around each call."""
+    import numpy as np
+    bt0 = w.block_table.cpu().numpy()
+    sl0 = w.seq_lens.cpu().numpy()
+    n = (sl0 + 15) // 16
+    indptr = torch.as_tensor(np.concatenate([[0], np.cumsum(n)]), dtype=torch.int64, device=w.q.device)
+    indices = torch.as_tensor(np.concatenate([bt0[b, :n[b]] for b in range(len(n))]), device=w.q.device)
+    last = torch.as_tensor(sl0 - (n - 1) * 16, dtype=torch.int64, device=w.q.device)
+    bt = torch.empty_like(w.block_table)
+    sl = torch.empty_like(w.seq_lens)
+    call = lambda: pkv.paged_block_table_from_csr(indptr, indices, last, bt, sl, page_size=16, pad_page=0)
+    for _ in range(3):
+        call()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        call()
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    moved = int(indptr.numel() * 8 + indices.numel() * 8 + last.numel() * 8 + bt.numel() * 8 + sl.numel() * 8)
+    return {"workload": "decode workload's metadata (64 sequences, 256-entry rows) unpacked from the packed "
+                        "page list", "kernel": "csr_to_block_table_kernel",
+            "us_median": round(ms[len(ms) // 2] * 1e3, 2), "bytes": moved}
+
+
 def host_control_plane_timing() -> dict:
     """Host cost of one decode step's bookkeeping in the C++ control plane for
     the decode workload's shape: 64 sequences of U{512..4096} tokens in a
@@ -411,6 +440,8 @@ def main(argv=None) -> int:
         "write_ms_median": round(statistics.median(t2.write), 5),
         "timed_loop_wall_s": round(t2.wall, 4),
     }
+    if not args.no_extra:
+        result["csr_unpack"] = csr_unpack_timing(pkv, w2, torch, args.steps)
     del r2
 
     if not args.no_extra:
