@@ -67,10 +67,12 @@ __host__ __device__ inline int decode_waves(int Hkv) {
 }
 
 // Units of sequence b: its 32-position blocks past the shared prefix (if
-// any), or none when it has no query row.
-__device__ __forceinline__ int32_t seq_units(const AttnParams& p, int b) {
-  if (p.qsl[b + 1] == p.qsl[b]) return 0;
-  const int64_t keys = p.seq_lens[b] - p.prefix_len;
+// any), or none when it has no query row.  len_out = seq_lens[b].
+__device__ __forceinline__ int32_t seq_units(const AttnParams& p, int b, int64_t& len_out) {
+  const int64_t qa = p.qsl[b], qz = p.qsl[b + 1], L = p.seq_lens[b];
+  len_out = L;
+  if (qz == qa) return 0;
+  const int64_t keys = L - p.prefix_len;
   return keys > 0 ? (int32_t)((keys + kUnit - 1) / kUnit) : 0;
 }
 
@@ -312,7 +314,9 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   constexpr int NKK = D / 32;
   constexpr int NJ = D / 16;
   __shared__ int32_t s_cum[kDecodeMaxSeqs + 1];
-  __shared__ int32_t s_scan[512];
+  __shared__ int32_t s_wave_units[kMaxWaves];
+  __shared__ int32_t s_first;      // the sequence holding this workgroup's first unit
+  __shared__ int64_t s_first_len;  // and its length
   __shared__ __bf16 s_ktile[kMaxWaves][kUnit * D];
   __shared__ __bf16 s_vtile[kMaxWaves][kUnit * D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -320,50 +324,62 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   const int col = lane & 15, grp = lane >> 4;
   const int B = (int)p.B;
 
-  // ---- units before each sequence (block-wide exclusive scan)
+  // ---- units before each sequence: a scan of each thread's run of
+  // sequences, inclusive within the wave by lane shuffles, then over the wave
+  // totals (one barrier).  The thread whose run holds the workgroup's first
+  // unit also publishes that sequence and its length, so the first page ids
+  // can be fetched without another round trip for seq_lens.
+  const int W = gridDim.x, wg = blockIdx.x;
+  int32_t U;
   {
     const int per = (B + nthreads - 1) / nthreads;
     const int b_lo = tid * per;
     int32_t run = 0;
+    int64_t len;
     for (int i = 0; i < per; ++i) {
       const int b = b_lo + i;
-      if (b < B) run += seq_units(p, b);
+      if (b < B) run += seq_units(p, b, len);
     }
-    s_scan[tid] = run;
+    int32_t x = run;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave_units[wave] = x;
     __syncthreads();
-    for (int off = 1; off < nthreads; off <<= 1) {
-      const int32_t v = tid >= off ? s_scan[tid - off] : 0;
-      __syncthreads();
-      s_scan[tid] += v;
-      __syncthreads();
+    int32_t acc_units = x - run;
+    U = 0;
+    for (int w = 0; w < (nthreads >> 6); ++w) {
+      const int32_t t = s_wave_units[w];
+      acc_units += w < wave ? t : 0;
+      U += t;
     }
-    int32_t acc_units = tid ? s_scan[tid - 1] : 0;
+    const Partition part0(U, W);
+    const int32_t first_unit = part0.start(wg);
     if (tid == 0) s_cum[0] = 0;
     for (int i = 0; i < per; ++i) {
       const int b = b_lo + i;
       if (b < B) {
-        acc_units += seq_units(p, b);
+        const int32_t n = seq_units(p, b, len);
+        if (n > 0 && acc_units <= first_unit && first_unit < acc_units + n) {
+          s_first = b;
+          s_first_len = len;
+        }
+        acc_units += n;
         s_cum[b + 1] = acc_units;
       }
     }
     __syncthreads();
   }
-  const int W = gridDim.x, wg = blockIdx.x;
   if (wg == 0)
     for (int b = tid; b <= B; b += nthreads) p.ws_cum[b] = s_cum[b];
-  const int32_t U = s_cum[B];
   if (U == 0) return;
   const Partition part(U, W);
   const int32_t u0 = part.start(wg);
   const int32_t u1 = part.start(wg + 1);
   if (u0 >= u1) return;
-
-  // sequence holding unit u0: the largest b with s_cum[b] <= u0
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (s_cum[mid] <= u0) lo = mid; else hi = mid - 1;
-  }
+  const int lo = s_first;  // the sequence holding unit u0
 
   const int hpw = decode_heads_per_wave(p.Hkv);
   const int waves = nthreads >> 6;
@@ -388,7 +404,15 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     // (with a shared prefix, its partial joins in the merge: never whole)
     const bool whole = seg_lo == cb && seg_hi == ce && p.prefix_len == 0;
     const int j0 = seg_lo - cb, j1 = seg_hi - cb;  // units of b in this segment
-    const int64_t L = p.seq_lens[b];
+    // (the LDS copy is wave-uniform: move it to scalar registers like the load it replaces)
+    int64_t L;
+    if (b == lo) {
+      const uint64_t f = (uint64_t)s_first_len;
+      L = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(f >> 32)) << 32) |
+                    __builtin_amdgcn_readfirstlane((uint32_t)f));
+    } else {
+      L = p.seq_lens[b];
+    }
     const int64_t q_row = p.qsl[b];
     // unit j covers positions base + 32 j ..; pages are counted from base too
     const int64_t base = p.prefix_len;
