@@ -102,6 +102,12 @@ int32_t pkv_page_dirty(const pkv_page_pool* pool, int64_t page_id);
 int pkv_seq_create(pkv_page_pool* pool, int64_t* seq_out);
 int pkv_seq_append(pkv_page_pool* pool, int64_t seq, int64_t n, int64_t* slots_out);
 int pkv_seq_fork(pkv_page_pool* pool, int64_t parent, int64_t n_tokens, int64_t* child_out, int64_t* copy_out);
+/* pkv_seq_append for a batch: sequence seqs[b] grows by n[b] tokens, b in
+ * [0, B), and the slots of all new tokens are written to slots_out in
+ * sequence order (sum(n) entries).  All or nothing: with a bad handle, a
+ * repeated sequence or too few free pages for the whole batch, nothing
+ * changes.  One call per step instead of one per sequence. */
+int pkv_seq_append_batch(pkv_page_pool* pool, const int64_t* seqs, int64_t B, const int64_t* n, int64_t* slots_out);
 int pkv_seq_release(pkv_page_pool* pool, int64_t seq);
 int64_t pkv_seq_length(const pkv_page_pool* pool, int64_t seq);
 int64_t pkv_seq_pages(const pkv_page_pool* pool, int64_t seq, int64_t* page_ids_out, int64_t capacity);

@@ -232,6 +232,42 @@ int pkv_seq_append(pkv_page_pool* pool, int64_t seq, int64_t n, int64_t* slots_o
   return PKV_OK;
 }
 
+int pkv_seq_append_batch(pkv_page_pool* pool, const int64_t* seqs, int64_t B, const int64_t* n, int64_t* slots_out) {
+  if (!pool || (B > 0 && (!seqs || !n))) return PKV_ERR_NULL;
+  if (B < 0) return PKV_ERR_SHAPE;
+  const int64_t ps = pool->page_size;
+  int64_t need = 0, total = 0;
+  std::vector<int64_t> slot_of((size_t)B);
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t slot = pool->seq_slot(seqs[b]);
+    if (slot < 0) return PKV_ERR_BAD_HANDLE;
+    if (n[b] < 0) return PKV_ERR_SHAPE;
+    slot_of[(size_t)b] = slot;
+    const Seq& s = pool->seqs[(size_t)slot];
+    need += (s.len + n[b] + ps - 1) / ps - (int64_t)s.pages.size();
+    total += n[b];
+  }
+  std::vector<int64_t> sorted(slot_of);
+  std::sort(sorted.begin(), sorted.end());
+  if (std::adjacent_find(sorted.begin(), sorted.end()) != sorted.end()) return PKV_ERR_BAD_HANDLE;
+  if (total > 0 && !slots_out) return PKV_ERR_NULL;
+  if (need > (int64_t)pool->free_list.size()) return PKV_ERR_NO_PAGES;
+  int64_t k = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    Seq& s = pool->seqs[(size_t)slot_of[(size_t)b]];
+    const int64_t more = (s.len + n[b] + ps - 1) / ps - (int64_t)s.pages.size();
+    std::vector<int64_t> got;
+    if (more > 0) pool->take_pages(more, got);  // cannot fail: counted above
+    s.pages.insert(s.pages.end(), got.begin(), got.end());
+    for (int64_t i = 0; i < n[b]; ++i, ++k) {
+      const int64_t pos = s.len + i;
+      slots_out[k] = s.pages[(size_t)(pos / ps)] * ps + pos % ps;
+    }
+    s.len += n[b];
+  }
+  return PKV_OK;
+}
+
 int pkv_seq_fork(pkv_page_pool* pool, int64_t parent, int64_t n_tokens, int64_t* child_out, int64_t* copy_out) {
   if (!pool || !child_out || !copy_out) return PKV_ERR_NULL;
   const int64_t ps_slot = pool->seq_slot(parent);

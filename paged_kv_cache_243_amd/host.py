@@ -12,7 +12,7 @@ from ._binding import PagedKVError, load
 # every function include/pagedkv_host.h declares
 HOST_EXPORTS = ("pkv_pool_create", "pkv_pool_destroy", "pkv_pool_free_pages", "pkv_pool_used_pages",
                 "pkv_page_alloc", "pkv_page_release", "pkv_page_confirm", "pkv_page_refcount", "pkv_page_dirty",
-                "pkv_seq_create", "pkv_seq_append", "pkv_seq_fork", "pkv_seq_release", "pkv_seq_length",
+                "pkv_seq_create", "pkv_seq_append", "pkv_seq_append_batch", "pkv_seq_fork", "pkv_seq_release", "pkv_seq_length",
                 "pkv_seq_pages", "pkv_build_step", "pkv_prefix_insert", "pkv_prefix_match", "pkv_prefix_evict",
                 "pkv_prefix_pages")
 NO_PAGES, BAD_HANDLE, DIRTY = -20, -21, -22
@@ -37,6 +37,7 @@ def _lib():
             "pkv_page_dirty": ([vp, i64], i32),
             "pkv_seq_create": ([vp, vp], i32),
             "pkv_seq_append": ([vp, i64, i64, vp], i32),
+            "pkv_seq_append_batch": ([vp, vp, i64, vp, vp], i32),
             "pkv_seq_fork": ([vp, i64, i64, vp, vp], i32),
             "pkv_seq_release": ([vp, i64], i32),
             "pkv_seq_length": ([vp, i64], i64),
@@ -119,6 +120,14 @@ class PagePool:
     def append(self, seq: int, n: int) -> np.ndarray:
         slots = np.empty(int(n), dtype=np.int64)
         _check(self._lib.pkv_seq_append(self._h, int(seq), int(n), _ptr(slots)), "pkv_seq_append")
+        return slots
+
+    def append_batch(self, seqs, n) -> np.ndarray:
+        s = np.ascontiguousarray(seqs, dtype=np.int64)
+        k = np.ascontiguousarray(n, dtype=np.int64)
+        slots = np.empty(int(k.sum()), dtype=np.int64)
+        _check(self._lib.pkv_seq_append_batch(self._h, _ptr(s), s.size, _ptr(k), _ptr(slots)),
+               "pkv_seq_append_batch")
         return slots
 
     def fork(self, parent: int, n_tokens: int) -> tuple[int, tuple[int, int, int]]:

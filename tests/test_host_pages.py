@@ -314,3 +314,20 @@ def test_metadata_from_the_control_plane_gives_dense_attention():
                 w = torch.softmax(0.125 * (kt[:pos + 1, h] @ x), 0)
                 ref = (w[:, None] * vt[:pos + 1, h]).sum(0)
                 assert np.allclose(out[qsl[b] + i, hq], ref.numpy(), atol=1e-12), (b, i, hq)
+
+
+def test_batched_append_matches_one_call_per_sequence_and_is_all_or_nothing():
+    p, q = Hs.PagePool(40, 16), Hs.PagePool(40, 16)
+    sp = [p.create() for _ in range(5)]
+    sq = [q.create() for _ in range(5)]
+    rng = np.random.default_rng(4)
+    for _ in range(6):
+        n = rng.integers(0, 20, size=5)
+        batch = p.append_batch(sp, n)
+        one = np.concatenate([q.append(s, int(k)) for s, k in zip(sq, n)])
+        assert np.array_equal(batch, one)
+    free = p.free_pages
+    before = [p.length(s) for s in sp]
+    assert status(p.append_batch, sp, [0, 0, 0, 0, 16 * (free + 1)]) == Hs.NO_PAGES
+    assert status(p.append_batch, [sp[0], sp[0]], [1, 1]) == Hs.BAD_HANDLE
+    assert [p.length(s) for s in sp] == before and p.free_pages == free
