@@ -309,17 +309,34 @@ struct Partition {
 // the normalised output; otherwise it writes an unnormalised partial to slot
 // (b + workgroup), which merge_kernel combines.  Slots are unique because the
 // ranges are ordered: a later sequence only meets later workgroups.
+//
+// Each wave processes its work as one stream of units: a run is one KV head of
+// one segment, runs follow segment by segment (heads inside a segment), and
+// the loads of the next unit are issued while the current one is computed
+// even when the next unit opens a new run.  Page ids are fetched two units
+// ahead.  Lengths come from the
+// scan's LDS tables, so opening a run needs no dependent global load.
+
+// A position in a wave's stream: unit j of run (sequence b, head slot hk),
+// the run covering units [.., j1) of b.  b < 0 past the end of the stream.
+struct StreamPos {
+  int b, hk;
+  int32_t j, j1;
+};
+
 template <int ESZ, int D>
 __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   constexpr int NKK = D / 32;
   constexpr int NJ = D / 16;
   __shared__ int32_t s_cum[kDecodeMaxSeqs + 1];
+  // positions of each sequence's last unit (1..32), to rebuild its length
+  __shared__ uint8_t s_tail[kDecodeMaxSeqs];
   __shared__ int32_t s_wave_units[kMaxWaves];
   __shared__ int32_t s_first;      // the sequence holding this workgroup's first unit
-  __shared__ int64_t s_first_len;  // and its length
   __shared__ __bf16 s_ktile[kMaxWaves][kUnit * D];
   __shared__ __bf16 s_vtile[kMaxWaves][kUnit * D];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nthreads = blockDim.x;
   const int col = lane & 15, grp = lane >> 4;
   const int B = (int)p.B;
@@ -327,8 +344,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   // ---- units before each sequence: a scan of each thread's run of
   // sequences, inclusive within the wave by lane shuffles, then over the wave
   // totals (one barrier).  The thread whose run holds the workgroup's first
-  // unit also publishes that sequence and its length, so the first page ids
-  // can be fetched without another round trip for seq_lens.
+  // unit also publishes that sequence.
   const int W = gridDim.x, wg = blockIdx.x;
   int32_t U;
   {
@@ -362,10 +378,9 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       const int b = b_lo + i;
       if (b < B) {
         const int32_t n = seq_units(p, b, len);
-        if (n > 0 && acc_units <= first_unit && first_unit < acc_units + n) {
-          s_first = b;
-          s_first_len = len;
-        }
+        if (n > 0 && acc_units <= first_unit && first_unit < acc_units + n) s_first = b;
+        // len = prefix_len + 32 (n - 1) + tail with tail in [1, 32]
+        s_tail[b] = (uint8_t)(n > 0 ? len - p.prefix_len - (int64_t)kUnit * (n - 1) : 0);
         acc_units += n;
         s_cum[b + 1] = acc_units;
       }
@@ -374,17 +389,20 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   }
   if (wg == 0)
     for (int b = tid; b <= B; b += nthreads) p.ws_cum[b] = s_cum[b];
+  // (the wave totals come through LDS: keep the range in scalar registers)
+  U = (int32_t)__builtin_amdgcn_readfirstlane(U);
   if (U == 0) return;
   const Partition part(U, W);
-  const int32_t u0 = part.start(wg);
-  const int32_t u1 = part.start(wg + 1);
+  const int32_t u0 = (int32_t)__builtin_amdgcn_readfirstlane(part.start(wg));
+  const int32_t u1 = (int32_t)__builtin_amdgcn_readfirstlane(part.start(wg + 1));
   if (u0 >= u1) return;
-  const int lo = s_first;  // the sequence holding unit u0
 
   const int hpw = decode_heads_per_wave(p.Hkv);
   const int waves = nthreads >> 6;
   const uint32_t row_stride = (uint32_t)p.Hkv * D * ESZ;
   const int64_t page_stride = (int64_t)row_stride * kPageSize;
+  const uint32_t page_bytes = (uint32_t)page_stride;
+  const int64_t base = p.prefix_len;  // unit j of b covers positions base + 32 j ..
   LaneOffsets off;
   {
     using G = KGeom<ESZ, D>;
@@ -395,96 +413,143 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   __bf16* const ktile = s_ktile[wave];
   __bf16* const vtile = s_vtile[wave];
 
-  for (int b = __builtin_amdgcn_readfirstlane(lo); b < B; ++b) {
-    const int32_t cb = s_cum[b], ce = s_cum[b + 1];
-    if (cb >= u1) break;
-    const int32_t seg_lo = __builtin_amdgcn_readfirstlane(max(u0, cb));
-    const int32_t seg_hi = __builtin_amdgcn_readfirstlane(min(u1, ce));
-    if (seg_lo >= seg_hi) continue;
-    // (with a shared prefix, its partial joins in the merge: never whole)
-    const bool whole = seg_lo == cb && seg_hi == ce && p.prefix_len == 0;
-    const int j0 = seg_lo - cb, j1 = seg_hi - cb;  // units of b in this segment
-    // (the LDS copy is wave-uniform: move it to scalar registers like the load it replaces)
-    int64_t L;
-    if (b == lo) {
-      const uint64_t f = (uint64_t)s_first_len;
-      L = (int64_t)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(f >> 32)) << 32) |
-                    __builtin_amdgcn_readfirstlane((uint32_t)f));
-    } else {
-      L = p.seq_lens[b];
+  // ---- the wave's stream (all of it wave-uniform)
+  auto uniform = [](int32_t v) { return (int32_t)__builtin_amdgcn_readfirstlane(v); };
+  auto seq_len = [&](int b) {  // from the scan's tables
+    const int32_t n = uniform(s_cum[b + 1] - s_cum[b]), t = uniform(s_tail[b]);
+    return base + (int64_t)kUnit * (n - 1) + t;
+  };
+  auto advance = [&](StreamPos c) {
+    if (c.b < 0) return c;
+    if (++c.j < c.j1) return c;
+    if (c.hk + 1 < hpw && wave + (c.hk + 1) * waves < p.Hkv) {  // next head of the segment
+      ++c.hk;
+      const int32_t cb = uniform(s_cum[c.b]);
+      c.j = uniform(max(u0, cb) - cb);
+      return c;
     }
-    const int64_t q_row = p.qsl[b];
-    // unit j covers positions base + 32 j ..; pages are counted from base too
-    const int64_t base = p.prefix_len;
-    const int64_t last_page = ((L + 15) >> 4) - 1 - base / kPageSize;
-    const __attribute__((address_space(4))) int64_t* bt_row =
-        (const __attribute__((address_space(4))) int64_t*)(p.block_table + (int64_t)b * p.max_blocks +
-                                                           base / kPageSize);
-
-    for (int hk = 0; hk < hpw; ++hk) {
-      const int h = wave + hk * waves;
-      if (h >= p.Hkv) break;
-      // query operand: head col of the group (zero for padding columns)
-      bf16x8 qb[NKK];
-      {
-        const __bf16* qrow = (const __bf16*)p.q + (q_row * p.Hq + h * p.G + col) * D;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          u32x4 x = {0u, 0u, 0u, 0u};
-          if (col < p.G) x = *(const u32x4*)(qrow + 32 * kk + 8 * grp);
-          qb[kk] = __builtin_bit_cast(bf16x8, x);
-        }
+    for (int b = c.b + 1; b < B; ++b) {  // next segment (starts at its sequence's unit 0)
+      const int32_t cb = uniform(s_cum[b]);
+      if (cb >= u1) break;
+      const int32_t ce = uniform(s_cum[b + 1]);
+      if (ce > cb) {
+        c.b = b;
+        c.hk = 0;
+        c.j = 0;
+        c.j1 = uniform(min(u1, ce) - cb);
+        return c;
       }
-      float logit_scale = p.scale * kLog2e;
-      if constexpr (ESZ == 1) logit_scale *= p.k_scale[h];
-      const char* kbase = (const char*)p.key_pool + (int64_t)h * D * ESZ;
-      const char* vbase = (const char*)p.value_pool + (int64_t)h * D * ESZ;
-      const uint32_t page_bytes = (uint32_t)page_stride;
-      auto krsrc = [&](int64_t pg) { return page_rsrc(kbase + pg * page_stride, page_bytes); };
-      auto vrsrc = [&](int64_t pg) { return page_rsrc(vbase + pg * page_stride, page_bytes); };
-
-      f32x4 acc[NJ];
+    }
+    c.b = -1;
+    return c;
+  };
+  auto same_run = [](const StreamPos& a, const StreamPos& c) { return a.b == c.b && a.hk == c.hk; };
+  // wave-uniform reads of metadata the kernel never writes, as scalar loads
+  using c64p = const __attribute__((address_space(4))) int64_t*;
+  using cf32p = const __attribute__((address_space(4))) float*;
+  auto q_row_of = [&](int b) { return ((c64p)p.qsl)[b]; };
+  auto run_scales = [&](int h, float& ls, float& os) {
+    ls = p.scale * kLog2e;
+    os = 1.0f;
+    if constexpr (ESZ == 1) {
+      ls *= ((cf32p)p.k_scale)[h];
+      os = ((cf32p)p.v_scale)[h];
+    }
+  };
+  auto bt_row = [&](int b) {
+    return (const __attribute__((address_space(4))) int64_t*)(p.block_table + (int64_t)b * p.max_blocks +
+                                                               base / kPageSize);
+  };
+  auto last_page = [&](int64_t L) { return ((L + 15) >> 4) - 1 - base / kPageSize; };
+  auto pages_of = [&](const StreamPos& c, int64_t L) {
+    if (c.b < 0) return UnitPages{0, 0};
+    return unit_pages(bt_row(c.b), c.j, last_page(L));
+  };
+  auto head_of = [&](const StreamPos& c) { return wave + c.hk * waves; };
+  auto krsrc = [&](int h, int64_t pg) {
+    return page_rsrc((const char*)p.key_pool + (int64_t)h * D * ESZ + pg * page_stride, page_bytes);
+  };
+  auto vrsrc = [&](int h, int64_t pg) {
+    return page_rsrc((const char*)p.value_pool + (int64_t)h * D * ESZ + pg * page_stride, page_bytes);
+  };
+  // query operand of (row q_row, KV head h): head col of the group (zero for padding columns)
+  auto load_q = [&](bf16x8(&qb)[NKK], int64_t q_row, int h) {
+    const __bf16* qrow = (const __bf16*)p.q + (q_row * p.Hq + h * p.G + col) * D;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      float m_run = -INFINITY, l_run = 0.f;
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (col < p.G) x = *(const u32x4*)(qrow + 32 * kk + 8 * grp);
+      qb[kk] = __builtin_bit_cast(bf16x8, x);
+    }
+  };
 
-      // One unit of registers: as soon as unit j is staged into LDS, unit j+1's
-      // loads are issued into them, so each load has a whole unit of compute to
-      // land.  Page ids are fetched one unit further ahead.
-      UnitRegs<ESZ, D> u;
-      const UnitPages first = unit_pages(bt_row, j0, last_page);
-      UnitPages nxt = unit_pages(bt_row, j0 + 1, last_page);
-      issue_k<ESZ, D>(u, krsrc(first.p0), krsrc(first.p1), off);
-      issue_v<ESZ, D>(u, vrsrc(first.p0), vrsrc(first.p1), off);
-      // the loop issues unconditionally (straight-line load order, so each wait
-      // covers exactly the loads it needs); the last unit is peeled
-      for (int j = j0; j < j1 - 1; ++j) {
-        consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, base + (int64_t)j * kUnit, L, lane, [&] {
-          issue_k<ESZ, D>(u, krsrc(nxt.p0), krsrc(nxt.p1), off);
-          issue_v<ESZ, D>(u, vrsrc(nxt.p0), vrsrc(nxt.p1), off);
-        });
-        nxt = unit_pages(bt_row, j + 2, last_page);
-      }
-      consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, base + (int64_t)(j1 - 1) * kUnit, L,
-                           lane, [] {});
+  StreamPos c0;
+  {
+    const int lo = uniform(s_first);  // the sequence holding unit u0
+    const int32_t cb = uniform(s_cum[lo]), ce = uniform(s_cum[lo + 1]);
+    c0 = StreamPos{lo, 0, uniform(u0 - cb), uniform(min(u1, ce) - cb)};
+  }
+  int64_t L0 = seq_len(c0.b), q_row0 = q_row_of(c0.b);
+  bf16x8 qb[NKK];
+  load_q(qb, q_row0, head_of(c0));
+  StreamPos c1 = advance(c0);
+  int64_t L1 = same_run(c0, c1) || c1.b < 0 ? L0 : seq_len(c1.b);
+  int64_t q_row1 = c1.b == c0.b || c1.b < 0 ? q_row0 : q_row_of(c1.b);
+  UnitRegs<ESZ, D> u;
+  {
+    const UnitPages first = pages_of(c0, L0);
+    const int h = head_of(c0);
+    issue_k<ESZ, D>(u, krsrc(h, first.p0), krsrc(h, first.p1), off);
+    issue_v<ESZ, D>(u, vrsrc(h, first.p0), vrsrc(h, first.p1), off);
+  }
+  UnitPages pg1 = pages_of(c1, L1);
 
+  f32x4 acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  float logit_scale, out_scale;
+  run_scales(head_of(c0), logit_scale, out_scale);
+
+  while (true) {
+    // the unit after c1 (page ids fetched below, loads issued while c1 is computed)
+    const StreamPos c2 = advance(c1);
+    const int64_t L2 = c2.b == c1.b || c2.b < 0 ? L1 : seq_len(c2.b);
+    const int64_t q_row2 = c2.b == c1.b || c2.b < 0 ? q_row1 : q_row_of(c2.b);
+    const bool run_ends = !same_run(c0, c1);
+
+    const int h0 = head_of(c0);
+    const int h1 = head_of(c1);
+    consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, base + (int64_t)c0.j * kUnit, L0, lane,
+                         [&] {
+                           if (c1.b >= 0) {
+                             issue_k<ESZ, D>(u, krsrc(h1, pg1.p0), krsrc(h1, pg1.p1), off);
+                             issue_v<ESZ, D>(u, vrsrc(h1, pg1.p0), vrsrc(h1, pg1.p1), off);
+                           }
+                         });
+    const UnitPages pg2 = pages_of(c2, L2);
+
+    if (run_ends) {
+      // the next run's query (its latency overlaps the write-out below)
+      if (c1.b >= 0) load_q(qb, q_row1, head_of(c1));
       // the four lane groups hold partial sums of the same head (same max)
       l_run += xor_shuffle(l_run, 16);
       l_run += xor_shuffle(l_run, 32);
-      float out_scale = 1.0f;
-      if constexpr (ESZ == 1) out_scale = p.v_scale[h];
+      // (with a shared prefix, its partial joins in the merge: never whole)
+      const int32_t cb = s_cum[c0.b], ce = s_cum[c0.b + 1];
+      const bool whole = u0 <= cb && ce <= u1 && p.prefix_len == 0;
       if (col < p.G) {
-        const int hq = h * p.G + col;
+        const int hq = h0 * p.G + col;
         // acc[t][i] = O^T[dim 16t + 4*grp + i][head col]
         if (whole) {
           const float inv = out_scale / l_run;
-          __bf16* orow = (__bf16*)p.out + (q_row * p.Hq + hq) * D;
+          __bf16* orow = (__bf16*)p.out + (q_row0 * p.Hq + hq) * D;
 #pragma unroll
           for (int t = 0; t < NJ; ++t)
             *(u32x2*)(orow + 16 * t + 4 * grp) =
                 u32x2{pack_bf16x2(acc[t][0] * inv, acc[t][1] * inv), pack_bf16x2(acc[t][2] * inv, acc[t][3] * inv)};
         } else {
-          const int64_t slot = ((int64_t)b + wg) * p.Hq + hq;
+          const int64_t slot = ((int64_t)c0.b + wg) * p.Hq + hq;
           float* orow = p.ws_o + slot * D;
 #pragma unroll
           for (int t = 0; t < NJ; ++t) *(f32x4*)(orow + 16 * t + 4 * grp) = acc[t] * out_scale;
@@ -494,7 +559,20 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
           }
         }
       }
+      if (c1.b < 0) break;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run = -INFINITY;
+      l_run = 0.f;
+      run_scales(head_of(c1), logit_scale, out_scale);
     }
+    c0 = c1;
+    L0 = L1;
+    q_row0 = q_row1;
+    c1 = c2;
+    L1 = L2;
+    q_row1 = q_row2;
+    pg1 = pg2;
   }
 }
 
