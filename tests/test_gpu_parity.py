@@ -138,6 +138,25 @@ def test_other_geometries(gpu, g, d, kv, mode):
     assert_close(out, ref, kv, f"G={g} D={d} {kv} {mode}")
 
 
+@pytest.mark.parametrize("hkv,kv", [(9, "bf16"), (16, "bf16"), (12, "fp8_e4m3fn")])
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_more_kv_heads_than_waves(gpu, hkv, kv, mode):
+    """More KV heads than the decode workgroup's 8 waves: each wave runs
+    several heads of every segment (9 heads: 5 waves, the last with one head),
+    and with 64-position partitions a workgroup's range crosses sequences."""
+    note(f"{hkv} KV heads {kv} {mode}")
+    if mode == "decode":  # about 380 units over the 256 workgroups: ranges of 1-2 units cross sequences
+        base = dataclasses.replace(W.SMALL[2], batch=8, old_min=2000, old_max=3000, num_pages=2048)
+    else:
+        base = W.SMALL[3]
+    cfg = dataclasses.replace(base, hq=2 * hkv, hkv=hkv, head_dim=64, kv_dtype=kv, q_dtype="bf16",
+                              split_tokens=64 if mode == "decode" else 0)
+    w = W.generate(cfg, DEV, seed=11)
+    kp, vp, out = gpu_step(gpu, w)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, kv, f"Hkv={hkv} {kv} {mode}")
+
+
 def test_ragged_prefill_with_empty_and_single_row_sequences(gpu):
     """A mixed batch through the prefill kernel: sequences with 0, 1 and many
     query rows, empty and long old contexts."""
