@@ -157,6 +157,20 @@ def test_more_kv_heads_than_waves(gpu, hkv, kv, mode):
     assert_close(out, ref, kv, f"Hkv={hkv} {kv} {mode}")
 
 
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+def test_decode_at_the_sequence_limit(gpu, kv):
+    """4096 sequences, the most one decode call takes: each scan thread sums 8
+    sequences, and every workgroup's range crosses a dozen or more sequences
+    (lengths 0..80: a third of a page up to three units)."""
+    note(f"decode with 4096 sequences {kv}")
+    cfg = dataclasses.replace(W.SMALL[2], batch=4096, hq=4, hkv=2, head_dim=64, kv_dtype=kv, q_dtype="bf16",
+                              old_min=0, old_max=80, num_pages=32768)
+    w = W.generate(cfg, DEV, seed=5)
+    kp, vp, out = gpu_step(gpu, w)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, kv, f"4096 sequences {kv}")
+
+
 def test_ragged_prefill_with_empty_and_single_row_sequences(gpu):
     """A mixed batch through the prefill kernel: sequences with 0, 1 and many
     query rows, empty and long old contexts."""
