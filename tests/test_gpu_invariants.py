@@ -166,3 +166,36 @@ def test_timing_events_bracket_the_main_kernel(gpu, cid):
     assert np.array_equal(_bits(out), _bits(ref))
     kernel_ms, call_ms = ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
     assert 0.0 < kernel_ms <= call_ms
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 5])
+@pytest.mark.parametrize("how", ["zero", "negative"])
+def test_degenerate_logit_scales(gpu, cid, how):
+    """scale = 0 weighs every visible key the same, so query row p of a
+    sequence is the mean of its value rows 0..p (closed form, checked on the
+    written pool directly); a negative scale reverses the order of the logits
+    (the kernels move its sign into q).  Both against the oracle on all rows."""
+    note(f"degenerate scale {how}, small config {cid}")
+    w = W.generate(W.SMALL[cid], DEV)
+    scale = 0.0 if how == "zero" else -2.0 * w.scale
+    kp, vp = gpu_write(gpu, w)
+    out = gpu_attend(gpu, w, kp, vp, scale=scale)
+    ref = H.oracle_attend(w, S(kp).copy(), S(vp).copy(), scale=scale)
+    assert_close(out, ref, w.kv_dtype, f"scale {scale:g}, small config {cid}")
+    if how != "zero":
+        return
+    vs = None if w.v_scale is None else S(w.v_scale)
+    V = H.pool_to_f64(S(vp), w.kv_dtype, vs).numpy()  # [pages, 16, Hkv, D]
+    G = w.cfg.hq // w.cfg.hkv
+    qsl, lens, bt = S(w.query_start_loc), S(w.seq_lens), S(w.block_table)
+    got = as_f64(out)
+    for b in range(w.cfg.batch):
+        n, L = int(qsl[b + 1] - qsl[b]), int(lens[b])
+        if n == 0:
+            continue
+        pos = np.arange(L)
+        rows = V[bt[b, pos // 16], pos % 16]            # [L, Hkv, D] in position order
+        prefix_mean = np.cumsum(rows, axis=0) / (pos + 1)[:, None, None]
+        want = np.repeat(prefix_mean[L - n:], G, axis=1)  # query i sits at position L - n + i
+        err = np.max(np.abs(got[qsl[b]:qsl[b + 1]] - want))
+        assert err <= TOL[w.kv_dtype], (b, err)
