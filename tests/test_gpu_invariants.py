@@ -199,3 +199,34 @@ def test_degenerate_logit_scales(gpu, cid, how):
         want = np.repeat(prefix_mean[L - n:], G, axis=1)  # query i sits at position L - n + i
         err = np.max(np.abs(got[qsl[b]:qsl[b + 1]] - want))
         assert err <= TOL[w.kv_dtype], (b, err)
+
+
+@pytest.mark.parametrize("cid", [2, 3, 4, 5])
+def test_device_metadata_validation(gpu, cid):
+    """paged_validate_metadata on device-resident metadata: the workloads'
+    own (full size) pass; a duplicated slot, a page id past the pool, a
+    length past the row and a query count above the length are each
+    reported as PKV_ERR_INDEX, and the device tensors are left unchanged."""
+    note(f"device metadata validation, config {cid}")
+    w = W.generate(cid, DEV)
+    num_pages, T = w.key_pool.shape[0], w.q.shape[0]
+    args = (w.slot_mapping, w.block_table, w.seq_lens, w.query_start_loc)
+    assert gpu.paged_validate_metadata(*args, num_pages, 16, T) == (0, "")
+    keep = [a.clone() for a in args]
+
+    def bad(i, idx, value, needle):
+        t = [a.clone() for a in args]
+        t[i][idx] = value
+        st, msg = gpu.paged_validate_metadata(*t, num_pages, 16, T)
+        assert st == -8 and needle in msg, (st, msg)
+
+    if w.slot_mapping.shape[0] > 1:
+        bad(0, 1, int(w.slot_mapping[0]), "twice")
+    bad(0, 0, num_pages * 16, "out of range")
+    bad(1, (0, 0), num_pages, "page")
+    bad(2, 0, w.block_table.shape[1] * 16 + 1, "exceeds")
+    n0 = int(w.query_start_loc[1] - w.query_start_loc[0])
+    if n0 > 0:
+        bad(2, 0, n0 - 1, "more query rows")
+    for a, k in zip(args, keep):
+        assert torch.equal(a, k)
