@@ -12,13 +12,17 @@
 // Mapping onto gfx950:
 //  * Stream-K work split.  The work is the list of (sequence, unit) pairs, a
 //    unit being 32 consecutive positions (two pages) of one sequence for all KV
-//    heads.  The grid has one 8-wave workgroup per CU (or a multiple of the CU
-//    count when the caller asks for smaller partitions); workgroup w takes the
-//    w-th of gridDim.x equal contiguous ranges, so every CU streams the same
-//    number of bytes whatever the length mix.  Wave k of a workgroup handles KV
-//    head k (or heads k, k + 8, ...): the waves of a workgroup read the same
-//    pages together, so HBM sees whole 2 KiB rows.  Every K/V byte of (b, h) is
-//    read from HBM once and serves all G query heads.
+//    heads.  It is cut into equal contiguous ranges (parts), so every CU
+//    streams the same number of bytes whatever the length mix.  A part is run
+//    by a group of waves, wave k of the group handling KV head k (or heads k,
+//    k + 8, ...): the waves of a group read the same pages together, so HBM
+//    sees whole rows of all heads.  A workgroup holds up to 8 waves: one group
+//    when there are 8 or more KV heads, else several groups side by side (8 of
+//    one wave each for a single KV head, as on a tensor-parallel shard), so
+//    every CU keeps 8 waves' loads in flight.  The grid has one workgroup per
+//    CU, or a multiple of the CU count when the caller asks for smaller
+//    partitions.  Every K/V byte of (b, h) is read from HBM once and serves
+//    all G query heads.
 //  * Page ids come from block_table through wave-uniform scalar loads, two
 //    units ahead.  K and V are read with buffer loads (page base in a scalar
 //    descriptor, 32-bit lane offsets), non-temporal, in whole-row runs: each
@@ -60,10 +64,21 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kStreamAux = 2;
 constexpr int kMaxWaves = 8;   // waves per workgroup
 
+#ifndef PKV_DECODE_MAX_GROUPS
+#define PKV_DECODE_MAX_GROUPS 8
+#endif
+
 __host__ __device__ inline int decode_heads_per_wave(int Hkv) { return (Hkv + kMaxWaves - 1) / kMaxWaves; }
+// waves of one group: together they cover every KV head of a part
 __host__ __device__ inline int decode_waves(int Hkv) {
   const int hpw = decode_heads_per_wave(Hkv);
   return (Hkv + hpw - 1) / hpw;
+}
+// groups (parts) per workgroup: with fewer KV heads than waves, the workgroup
+// runs several parts side by side, so the CU keeps 8 waves' loads in flight
+__host__ __device__ inline int decode_groups(int Hkv) {
+  const int g = kMaxWaves / decode_waves(Hkv);
+  return g < PKV_DECODE_MAX_GROUPS ? g : PKV_DECODE_MAX_GROUPS;
 }
 
 // Units of sequence b: its 32-position blocks past the shared prefix (if
@@ -303,12 +318,14 @@ struct Partition {
 };
 
 // Stream-K decode.  The flattened list of (sequence, unit) pairs is cut into
-// gridDim.x equal contiguous ranges, one per workgroup; a workgroup walks the
-// sequences its range overlaps (segments).  Wave w handles KV heads w, w +
-// waves, ... of every segment.  A segment that covers a whole sequence writes
+// grid_parts = gridDim.x * R equal contiguous ranges (parts), group gi of
+// workgroup w running part w * R + gi; a group walks the sequences its range
+// overlaps (segments).  Wave k of a group handles KV heads k, k + (waves per
+// group), ... of every segment.  A segment that covers a whole sequence writes
 // the normalised output; otherwise it writes an unnormalised partial to slot
-// (b + workgroup), which merge_kernel combines.  Slots are unique because the
-// ranges are ordered: a later sequence only meets later workgroups.
+// (b + part), which merge_kernel combines.  Slots are unique because the
+// ranges are ordered: a later sequence only meets later parts.  After the
+// scan the groups share no barrier, so a group whose range is empty leaves.
 //
 // Each wave processes its work as one stream of units: a run is one KV head of
 // one segment, runs follow segment by segment (heads inside a segment), and
@@ -332,7 +349,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   // positions of each sequence's last unit (1..32), to rebuild its length
   __shared__ uint8_t s_tail[kDecodeMaxSeqs];
   __shared__ int32_t s_wave_units[kMaxWaves];
-  __shared__ int32_t s_first;      // the sequence holding this workgroup's first unit
+  __shared__ int32_t s_first[kMaxWaves];  // the sequence holding each group's first unit
   __shared__ __bf16 s_ktile[kMaxWaves][kUnit * D];
   __shared__ __bf16 s_vtile[kMaxWaves][kUnit * D];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -345,7 +362,11 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   // sequences, inclusive within the wave by lane shuffles, then over the wave
   // totals (one barrier).  The thread whose run holds the workgroup's first
   // unit also publishes that sequence.
-  const int W = gridDim.x, wg = blockIdx.x;
+  // parts: R groups of wpg waves per workgroup, group gi running part wg
+  const int wpg = decode_waves(p.Hkv);
+  const int R = (nthreads >> 6) / wpg;
+  const int gi = wave / wpg, wig = wave - gi * wpg;
+  const int W = gridDim.x * R, wg = blockIdx.x * R + gi;
   int32_t U;
   {
     const int per = (B + nthreads - 1) / nthreads;
@@ -372,13 +393,15 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
       U += t;
     }
     const Partition part0(U, W);
-    const int32_t first_unit = part0.start(wg);
     if (tid == 0) s_cum[0] = 0;
     for (int i = 0; i < per; ++i) {
       const int b = b_lo + i;
       if (b < B) {
         const int32_t n = seq_units(p, b, len);
-        if (n > 0 && acc_units <= first_unit && first_unit < acc_units + n) s_first = b;
+        for (int r = 0; r < R; ++r) {
+          const int32_t first_unit = part0.start((int)blockIdx.x * R + r);
+          if (n > 0 && acc_units <= first_unit && first_unit < acc_units + n) s_first[r] = b;
+        }
         // len = prefix_len + 32 (n - 1) + tail with tail in [1, 32]
         s_tail[b] = (uint8_t)(n > 0 ? len - p.prefix_len - (int64_t)kUnit * (n - 1) : 0);
         acc_units += n;
@@ -387,7 +410,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     }
     __syncthreads();
   }
-  if (wg == 0)
+  if (blockIdx.x == 0)
     for (int b = tid; b <= B; b += nthreads) p.ws_cum[b] = s_cum[b];
   // (the wave totals come through LDS: keep the range in scalar registers)
   U = (int32_t)__builtin_amdgcn_readfirstlane(U);
@@ -398,7 +421,6 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   if (u0 >= u1) return;
 
   const int hpw = decode_heads_per_wave(p.Hkv);
-  const int waves = nthreads >> 6;
   const uint32_t row_stride = (uint32_t)p.Hkv * D * ESZ;
   const int64_t page_stride = (int64_t)row_stride * kPageSize;
   const uint32_t page_bytes = (uint32_t)page_stride;
@@ -422,7 +444,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   auto advance = [&](StreamPos c) {
     if (c.b < 0) return c;
     if (++c.j < c.j1) return c;
-    if (c.hk + 1 < hpw && wave + (c.hk + 1) * waves < p.Hkv) {  // next head of the segment
+    if (c.hk + 1 < hpw && wig + (c.hk + 1) * wpg < p.Hkv) {  // next head of the segment
       ++c.hk;
       const int32_t cb = uniform(s_cum[c.b]);
       c.j = uniform(max(u0, cb) - cb);
@@ -465,7 +487,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     if (c.b < 0) return UnitPages{0, 0};
     return unit_pages(bt_row(c.b), c.j, last_page(L));
   };
-  auto head_of = [&](const StreamPos& c) { return wave + c.hk * waves; };
+  auto head_of = [&](const StreamPos& c) { return wig + c.hk * wpg; };
   auto krsrc = [&](int h, int64_t pg) {
     return page_rsrc((const char*)p.key_pool + (int64_t)h * D * ESZ + pg * page_stride, page_bytes);
   };
@@ -485,7 +507,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
 
   StreamPos c0;
   {
-    const int lo = uniform(s_first);  // the sequence holding unit u0
+    const int lo = uniform(s_first[gi]);  // the sequence holding unit u0
     const int32_t cb = uniform(s_cum[lo]), ce = uniform(s_cum[lo + 1]);
     c0 = StreamPos{lo, 0, uniform(u0 - cb), uniform(min(u1, ce) - cb)};
   }
@@ -577,26 +599,42 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
 }
 
 // Log-sum-exp merge of the partials of a sequence whose units span several
-// workgroups (and, with a shared prefix, of the prefix chunks' partials):
+// parts (and, with a shared prefix, of the prefix chunks' partials):
 //   M = max_w m_w,  out = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w.
-// One wave per (query head, sequence).  Partials are taken in chunks of 8:
-// every (m, l) and O load of a chunk is issued before any of them is used, so
-// a chunk costs one memory round trip.
+// One workgroup of nw waves (1 .. kMergeWaves, by the partials a sequence
+// has) per (query head, sequence).  Wave k takes the chunks k, k + nw, ... of
+// 8 consecutive partials (wave 0 also the prefix chunks'); every (m, l) and O
+// load of a chunk is issued before any of them is used, so a chunk costs one
+// memory round trip and the waves' round trips overlap.  With several waves
+// their (m, l, O) are then combined through LDS in wave order.
+constexpr int kMergeWaves = 4;
+
+// merge waves for a grid of `parts` parts over B sequences: one per 8 partials
+// a sequence holds on average, at most kMergeWaves
+static int merge_waves(int parts, int64_t B) {
+  const int64_t per_seq = parts / std::max<int64_t>(B, 1) + 1;
+  return (int)std::min<int64_t>(kMergeWaves, (per_seq + 7) / 8);
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
   constexpr int PER = D / 64;
   constexpr int CHUNK = 8;
+  __shared__ float s_ml[kMergeWaves][2];
+  __shared__ float s_o[kMergeWaves][D];
   const int hq = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
-  // every index this wave needs, loaded together (one memory round trip before
-  // the partials' own)
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  // every index this workgroup needs, loaded together (one memory round trip
+  // before the partials' own)
   const int64_t q_row = p.qsl[b], q_end = p.qsl[b + 1];
   const int32_t cb = p.ws_cum[b], ce = p.ws_cum[b + 1], units = p.ws_cum[p.B];
   const bool prefix = p.prefix_len > 0;
   const bool has_units = ce > cb && units > 0;
   if (q_end == q_row || (!prefix && !has_units)) return;
   const Partition part(units, p.grid_parts);
-  int32_t wa = 0, wz = -1;  // workgroups holding the sequence's units (none: wz < wa)
+  int32_t wa = 0, wz = -1;  // parts holding the sequence's units (none: wz < wa)
   if (has_units) {
     wa = part.owner(cb);
     wz = part.owner(ce - 1);
@@ -607,7 +645,7 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
   float o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
-  if (prefix) {
+  if (prefix && wave == 0) {
     // the prefix chunks' partials (at most kMaxPrefixChunks), all loads first
     const f32x2* pml = (const f32x2*)p.ws_pre_ml;
     f32x2 mlc[kMaxPrefixChunks];
@@ -632,7 +670,7 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
       for (int i = 0; i < PER; ++i) o[i] += f * oc[c][i];
     }
   }
-  for (int32_t w0 = wa; w0 <= wz; w0 += CHUNK) {
+  for (int32_t w0 = wa + wave * CHUNK; w0 <= wz; w0 += nw * CHUNK) {
     f32x2 mlw[CHUNK];
     float ow[CHUNK][PER];
 #pragma unroll
@@ -665,6 +703,32 @@ __global__ __launch_bounds__(64) void merge_kernel(AttnParams p) {
     }
     M = Mc;
   }
+  if (nw > 1) {
+    // combine the waves' (M, l, O); a wave that took no partial has M = -inf,
+    // l = 0, O = 0 and weight 0 (wave 0 holds at least one live partial)
+    if (lane == 0) {
+      s_ml[wave][0] = M;
+      s_ml[wave][1] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) s_o[wave][lane + 64 * i] = o[i];
+    __syncthreads();
+    if (wave != 0) return;
+    float Mt = -INFINITY;
+    for (int k = 0; k < nw; ++k) Mt = fmaxf(Mt, s_ml[k][0]);
+    float lt = 0.f, ot[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) ot[i] = 0.f;
+    for (int k = 0; k < nw; ++k) {
+      const float f = s_ml[k][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_ml[k][0] - Mt);
+      lt += f * s_ml[k][1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ot[i] += f * s_o[k][lane + 64 * i];
+    }
+    l = lt;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = ot[i];
+  }
   const float inv = 1.0f / l;
 #pragma unroll
   for (int i = 0; i < PER; ++i)
@@ -692,24 +756,26 @@ void decode_workspace_carve(AttnParams& p, void* workspace) {
 // Workgroups of the decode grid: one per CU (one 8-wave workgroup fits a CU),
 // or, when the caller asks for partitions of split_tokens positions, about
 // B * max_len / 2 / split_tokens of them rounded to a multiple of the CU count.
-int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu) {
+int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu, int Hkv) {
   int64_t parts = n_cu;
   if (split_tokens > 0) {
     const int64_t want = (B * max_len / 2 + split_tokens - 1) / split_tokens;
     const int64_t rounds = std::max<int64_t>(1, (want + n_cu / 2) / n_cu);
     parts = rounds * n_cu;
   }
-  return (int)std::min<int64_t>(parts, kDecodeMaxParts);
+  const int R = decode_groups(Hkv);
+  return (int)(std::min<int64_t>(parts * R, kDecodeMaxParts) / R * R);
 }
 
 template <int ESZ, int D>
 static void launch_decode_t(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
-  const int threads = 64 * decode_waves(p.Hkv);
+  const int R = decode_groups(p.Hkv);
+  const int threads = 64 * decode_waves(p.Hkv) * R;
   if (p.prefix_len > 0) (void)launch_prefix_partials(p, stream);
   if (ev.begin) (void)hipEventRecord(ev.begin, stream);
-  hipLaunchKernelGGL((decode_kernel<ESZ, D>), dim3((unsigned)p.grid_parts), dim3(threads), 0, stream, p);
+  hipLaunchKernelGGL((decode_kernel<ESZ, D>), dim3((unsigned)(p.grid_parts / R)), dim3(threads), 0, stream, p);
   if (ev.end) (void)hipEventRecord(ev.end, stream);
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)p.Hq, (unsigned)p.B), dim3(64), 0, stream, p);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)p.Hq, (unsigned)p.B), dim3(64 * merge_waves(p.grid_parts, p.B)), 0, stream, p);
 }
 
 hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {

@@ -48,7 +48,7 @@ struct AttnParams {
   int max_query_len;   // grid sizing hint (>= true max n_b)
   // decode: stream-K over (sequence, 32-position block) units
   int split_tokens;    // requested positions per partition (0 = library choice)
-  int grid_parts;      // workgroups of the decode grid = partition ranges
+  int grid_parts;      // partition ranges (parts) of the decode work, a multiple of the parts per workgroup
   int32_t* ws_cum;     // [B + 1] units before each sequence (written by workgroup 0)
   float* ws_ml;        // [B + grid_parts, Hq, 2] partial (max in log2 units, sum)
   float* ws_o;         // [B + grid_parts, Hq, D] unnormalised partial outputs
@@ -82,7 +82,8 @@ hipError_t launch_csr_to_block_table(const int64_t* indptr, const int64_t* indic
 
 // workspace helpers shared by the ABI layer and the launchers
 size_t decode_workspace_bytes(int64_t B, int Hq, int D);
-int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu);
+// partition ranges of the decode work: a multiple of the parts one workgroup runs
+int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu, int Hkv);
 void decode_workspace_carve(AttnParams& p, void* workspace);
 constexpr int kDecodeMaxParts = 2048;
 constexpr int kDecodeMaxSeqs = 4096;

@@ -355,7 +355,8 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
       pkv::decode_workspace_carve(p, opts->workspace);
       if (p.prefix_len > 0)
         pkv::prefix_workspace_carve(p, (char*)opts->workspace + pkv::decode_workspace_bytes(p.B, p.Hq, p.D));
-      p.grid_parts = pkv::decode_grid_parts(p.B, p.max_blocks * kPageSize, p.split_tokens, device_cu_count());
+      p.grid_parts = pkv::decode_grid_parts(p.B, p.max_blocks * kPageSize, p.split_tokens, device_cu_count(),
+                                            (int)p.Hkv);
       err = pkv::launch_decode(p, s, ev);
       break;
     case AttnPlan::kPrefill:

@@ -157,6 +157,36 @@ def test_more_kv_heads_than_waves(gpu, hkv, kv, mode):
     assert_close(out, ref, kv, f"Hkv={hkv} {kv} {mode}")
 
 
+@pytest.mark.parametrize("hkv,kv,split", [(1, "bf16", 0), (1, "fp8_e4m3fn", 64), (1, "bf16", 64), (3, "bf16", 64),
+                                          (4, "fp8_e4m3fn", 0), (4, "bf16", 64)])
+def test_fewer_kv_heads_than_waves(gpu, hkv, kv, split):
+    """Fewer KV heads than the decode workgroup's 8 waves, as on a
+    tensor-parallel shard: a workgroup runs several parts side by side (one
+    KV head: 8 one-wave groups; 3 heads: 2 groups, 6 waves; 4 heads: 2
+    groups), each with its own range, and the ranges cross sequences."""
+    note(f"{hkv} KV heads {kv} split {split}")
+    base = dataclasses.replace(W.SMALL[2], batch=24, old_min=0, old_max=3000, num_pages=8192)
+    cfg = dataclasses.replace(base, hq=4 * hkv, hkv=hkv, head_dim=128, kv_dtype=kv, q_dtype="bf16",
+                              split_tokens=split)
+    w = W.generate(cfg, DEV, seed=13)
+    kp, vp, out = gpu_step(gpu, w)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, kv, f"Hkv={hkv} {kv} split {split}")
+
+
+def test_single_kv_head_shard_of_the_decode_workload(gpu):
+    """The decode workload at its 8-way tensor-parallel shard (4 query heads
+    on 1 KV head, 64 sequences of 512..4096 positions), in the launch
+    configuration of the full call; sampled rows against the oracle."""
+    note("decode workload, 1-KV-head shard")
+    w = W.generate(dataclasses.replace(W.CONFIGS[2], hq=4, hkv=1), DEV)
+    kp, vp, out = gpu_step(gpu, w)
+    rows = sample_rows(w, 1)
+    okp, ovp = H.oracle_write(w)
+    ref = H.oracle_attend(w, okp, ovp, sel_tokens=rows)
+    assert_close(as_f64(out)[rows], ref, "bf16", "1-KV-head shard of the decode workload")
+
+
 @pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
 def test_decode_at_the_sequence_limit(gpu, kv):
     """4096 sequences, the most one decode call takes: each scan thread sums 8

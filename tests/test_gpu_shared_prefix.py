@@ -38,6 +38,19 @@ def test_shared_prefix_small(gpu, kv, split):
     assert_close(out, ref, kv, f"shared prefix small kv={kv} split={split}")
 
 
+@pytest.mark.parametrize("split", [0, 64])
+def test_shared_prefix_single_kv_head(gpu, split):
+    """One KV head (8 query heads): the private decode runs 8 one-wave parts per
+    workgroup, their partials merged with the prefix chunks'."""
+    note(f"shared prefix, one KV head, split={split}")
+    cfg = dataclasses.replace(W.SMALL[4], hq=8, hkv=1, name="shared-prefix-1kv-small")
+    w = W.generate(cfg, DEV)
+    kp, vp = gpu_write(gpu, w)
+    out = attend_shared(gpu, w, kp, vp, cfg.shared_prefix_tokens // 16, split)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, "bf16", f"shared prefix one KV head split={split}")
+
+
 def test_shared_prefix_full(gpu):
     """256 sequences on 128 shared pages, in the launch configuration the
     benchmark times; every row against the oracle."""
