@@ -234,6 +234,13 @@ def traffic_from_profile(kernel: str):
     return None if entry is None else entry.get("traffic_bytes_per_launch")
 
 
+def tp_shard(W, cid: int, tp: int):
+    """Config `cid` with the heads one GPU holds under a `tp`-way head split."""
+    import dataclasses
+    c = W.CONFIGS[cid]
+    return dataclasses.replace(c, name=f"{c.name}-tp{tp}-shard", hq=c.hq // tp, hkv=c.hkv // tp)
+
+
 def cpu_baseline(w):
     """The oracle as it stands (fp64, OpenMP) on the whole decode step of the
     same workload: write of the 64 new tokens + attention of all 64 rows."""
@@ -338,7 +345,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--profile-workload",
-                    choices=["decode", "prefill", "shared", "sharedplain", "fp8", "fp8write", "csr"],
+                    choices=["decode", "prefill", "shared", "sharedplain", "fp8", "fp8write", "csr",
+                             "decode_tp8", "fp8_tp8"],
                     help="time one workload only and print its median times (for profiler runs)")
     args = ap.parse_args(argv)
 
@@ -370,8 +378,9 @@ def main(argv=None) -> int:
                           "write_ms_mean": statistics.fmean(t.write)}), flush=True)
         return 0
     if args.profile_workload:
-        cid = {"decode": 2, "prefill": 3, "shared": 4, "sharedplain": 4, "fp8": 5}[args.profile_workload]
-        w = W.generate(cid, dev)
+        cid = {"decode": 2, "prefill": 3, "shared": 4, "sharedplain": 4, "fp8": 5,
+               "decode_tp8": 2, "fp8_tp8": 5}[args.profile_workload]
+        w = W.generate(tp_shard(W, cid, 8) if args.profile_workload.endswith("_tp8") else cid, dev)
         # calibration for hardware byte counters: a plain device copy of known
         # size (256 MiB read + 256 MiB written), launched once
         calib = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
@@ -543,6 +552,32 @@ def main(argv=None) -> int:
         }
         del r5, w5
         torch.cuda.empty_cache()
+        # the two decode workloads at their 8-way tensor-parallel shard: one KV
+        # head (and its query heads) per GPU, all sequences and positions
+        shards = {}
+        for cid in (2, 5):
+            log(f"generating the 8-way shard of config {cid}")
+            ws = W.generate(tp_shard(W, cid, 8), dev)
+            rs = Runner(pkv, ws, torch)
+            ts, kts = time_workload(rs, torch, args.steps, args.warmup, flush, f"config {cid}, 8-way shard")
+            ks = statistics.fmean(kts.kernel)
+            kbs = decode_kernel_bytes(ws)
+            shards[f"config{cid}"] = {
+                "q_heads": ws.cfg.hq, "kv_heads": ws.cfg.hkv, "kv_dtype": ws.cfg.kv_dtype,
+                "algorithmic_bytes_per_launch": kbs,
+                "launch_ms_mean": round(ks, 5),
+                "achieved_GBps": round(kbs / (ks * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(kbs / (ks * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "call_ms_median": round(statistics.median(ts.attn), 5),
+            }
+            del rs, ws
+            torch.cuda.empty_cache()
+        extra["tp8_shard_decode"] = {
+            "workload": "the decode workload (config 2) and the long-context fp8 decode (config 5) with the "
+                        "query and KV heads of one GPU of an 8-way head split (1 KV head); not the headline",
+            "kernel": "decode_kernel (one-wave parts, 8 per workgroup)",
+            **shards,
+        }
         result.update(extra)
 
     if not args.no_extra:
