@@ -17,7 +17,8 @@ The printed JSON line carries:
                alone with HIP events the library records around it, against
                the 8 TB/s HBM peak; decode_call has the whole attention call,
   prefill, ... the other workloads (chunked prefill TFLOP/s against the bf16
-               MFMA peak, shared-prefix decode, fp8 long-context decode),
+               MFMA peak, shared-prefix decode, fp8 long-context decode, and
+               both decode workloads at their 8-way head shard: 1 KV head),
   cpu_baseline the CPU oracle on the same decode workload.
 Algorithmic bytes count each sequence's K and V rows once per KV head, plus q,
 out and the block_table entries read; flops count causally visible (query,
