@@ -347,7 +347,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--profile-workload",
                     choices=["decode", "prefill", "shared", "sharedplain", "fp8", "fp8write", "csr",
-                             "decode_tp8", "fp8_tp8"],
+                             "decode_tp8", "fp8_tp8", "prefill_tp8"],
                     help="time one workload only and print its median times (for profiler runs)")
     args = ap.parse_args(argv)
 
@@ -380,7 +380,7 @@ def main(argv=None) -> int:
         return 0
     if args.profile_workload:
         cid = {"decode": 2, "prefill": 3, "shared": 4, "sharedplain": 4, "fp8": 5,
-               "decode_tp8": 2, "fp8_tp8": 5}[args.profile_workload]
+               "decode_tp8": 2, "fp8_tp8": 5, "prefill_tp8": 3}[args.profile_workload]
         w = W.generate(tp_shard(W, cid, 8) if args.profile_workload.endswith("_tp8") else cid, dev)
         # calibration for hardware byte counters: a plain device copy of known
         # size (256 MiB read + 256 MiB written), launched once

@@ -52,8 +52,18 @@ struct AttnParams {
   int32_t* ws_cum;     // [B + 1] units before each sequence (written by workgroup 0)
   float* ws_ml;        // [B + grid_parts, Hq, 2] partial (max in log2 units, sum)
   float* ws_o;         // [B + grid_parts, Hq, D] unnormalised partial outputs
-  // prefill work list
-  int32_t* ws_plan;    // prefill tile schedule
+  // prefill work list: [0] item count, [1] tile count, then 2 words per item
+  // (b << 16 | query tile, tile index * split_max_chunks + chunk), then the
+  // (b << 16 | query tile) of every tile
+  int32_t* ws_plan;
+  int64_t plan_tiles_cap;  // bound on the (sequence, query tile) count
+  // prefill key split (0 = off): an item's keys run as chunks of split_keys
+  // keys (a multiple of 32), each writing (m, l, O) partials per row, which
+  // prefill_split_merge_kernel combines
+  int split_keys;
+  int split_max_chunks;    // chunks an item may have (1 without the split)
+  float* ws_split_ml;      // [plan_tiles_cap, Hkv, split_max_chunks, 256 rows, 2]
+  float* ws_split_o;       // [plan_tiles_cap, Hkv, split_max_chunks, 256 rows, D]
   // shared-prefix decode: the first prefix_len positions of every sequence
   // are the same pages; their attention runs as MFMA items of (prefix_tiles
   // groups of sequences) x (prefix_chunks chunks of prefix_chunk_len keys)
@@ -87,7 +97,11 @@ int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu, in
 void decode_workspace_carve(AttnParams& p, void* workspace);
 constexpr int kDecodeMaxParts = 2048;
 constexpr int kDecodeMaxSeqs = 4096;
+// decides the prefill key split (fills plan_tiles_cap, split_keys,
+// split_max_chunks); then the workspace size and its carving
+void prefill_split_plan(AttnParams& p);
 size_t prefill_workspace_bytes(const AttnParams& p);
+void prefill_workspace_carve(AttnParams& p, void* workspace);
 constexpr int kMaxPrefixChunks = 8;
 // groups of decode sequences, chunks and chunk length of a shared prefix of
 // prefix_len positions (fills p.prefix_*), and the partials' workspace bytes

@@ -199,6 +199,7 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
     const int64_t tpt = pkv::prefill_tokens_per_tile((int)G);
     if (max_blocks * kPageSize > INT32_MAX) return PKV_ERR_UNSUPPORTED;
     if ((T + tpt - 1) / tpt > 65535) return PKV_ERR_UNSUPPORTED;
+    pkv::prefill_split_plan(p);
     plan.workspace = pkv::prefill_workspace_bytes(p);
   }
 
@@ -360,7 +361,7 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
       err = pkv::launch_decode(p, s, ev);
       break;
     case AttnPlan::kPrefill:
-      p.ws_plan = plan.workspace > 0 ? (int32_t*)opts->workspace : nullptr;
+      pkv::prefill_workspace_carve(p, opts->workspace);
       err = pkv::launch_prefill(p, s, ev);
       break;
   }

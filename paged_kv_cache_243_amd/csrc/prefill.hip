@@ -71,65 +71,152 @@ int64_t prefill_max_items(int64_t T, int64_t B, int G) {
   return (T + tpt - 1) / tpt + B;
 }
 
+// Key split.  When the items (query tiles x KV heads) make fewer than
+// kSplitRounds rounds of workgroups on kSplitCUs CUs, as with one to four KV
+// heads per GPU, the longest item alone would set the kernel's time; the keys
+// are then cut into chunks so that about kSplitRounds rounds of workgroups
+// fill the CUs (if every sequence had max_blocks pages), each chunk at least
+// kSplitMinKeys keys.  The CU count is MI355X's, fixed so that
+// the workspace size does not depend on the device.
+constexpr int kSplitCUs = 256;
+constexpr int kSplitRounds = 2;
+constexpr int kSplitMinKeys = 512;
+
+void prefill_split_plan(AttnParams& p) {
+  const int64_t tiles = prefill_max_items(p.T, p.B, p.G);
+  p.plan_tiles_cap = tiles;
+  p.split_keys = 0;
+  p.split_max_chunks = 1;
+  const int64_t wgs = tiles * p.Hkv;
+  const int64_t max_kv = p.max_blocks * kPageSize;
+  if (wgs >= kSplitRounds * kSplitCUs || max_kv <= 2 * kSplitMinKeys) return;
+  const int64_t per_item = (kSplitRounds * kSplitCUs + wgs - 1) / wgs;
+  int64_t c = std::max<int64_t>((max_kv + per_item - 1) / per_item, kSplitMinKeys);
+  c = (c + kKeyTile - 1) / kKeyTile * kKeyTile;
+  p.split_keys = (int)c;
+  p.split_max_chunks = (int)((max_kv + c - 1) / c);
+}
+
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+static size_t plan_bytes(const AttnParams& p) {
+  const int64_t items = p.plan_tiles_cap * p.split_max_chunks;
+  return align256((size_t)(2 + 2 * items + p.plan_tiles_cap) * sizeof(int32_t));
+}
+
+static size_t split_rows(const AttnParams& p) {
+  return p.split_keys > 0 ? (size_t)p.plan_tiles_cap * p.Hkv * p.split_max_chunks * kPrefillRows : 0;
+}
+
 size_t prefill_workspace_bytes(const AttnParams& p) {
-  return (size_t)(prefill_max_items(p.T, p.B, p.G) + 1) * sizeof(uint32_t);
+  const size_t rows = split_rows(p);
+  return plan_bytes(p) + (rows ? align256(rows * 2 * sizeof(float)) + rows * p.D * sizeof(float) : 0);
+}
+
+void prefill_workspace_carve(AttnParams& p, void* workspace) {
+  char* w = (char*)workspace;
+  p.ws_plan = (int32_t*)w;
+  const size_t rows = split_rows(p);
+  p.ws_split_ml = rows ? (float*)(w + plan_bytes(p)) : nullptr;
+  p.ws_split_o = rows ? (float*)(w + plan_bytes(p) + align256(rows * 2 * sizeof(float))) : nullptr;
+}
+
+// chunks of an item whose rows see kv keys (1 without the key split); kv <
+// max_blocks * 16 < 2^31, so the division is a 32-bit one
+__device__ __forceinline__ int item_chunks(const AttnParams& p, int64_t kv) {
+  if (p.split_keys == 0) return 1;
+  const uint32_t c = ((uint32_t)kv + (uint32_t)p.split_keys - 1u) / (uint32_t)p.split_keys;
+  return (int)min(c, (uint32_t)p.split_max_chunks);
 }
 
 // ---------------------------------------------------------------------------
-// Plan: enumerate the (sequence, query tile) items, longest KV range first.
-// ws_plan[0] = item count, ws_plan[1 + rank] = b << 16 | tile.  Above
-// kPlanSortMax items the natural order is kept.
+// Plan: enumerate the (sequence, query tile, key chunk) items, longest key
+// range first, and the (sequence, query tile) pairs.  Layout in ws_plan:
+//   [0] item count, [1] tile count,
+//   [2 + 2 rank] = b << 16 | tile, [3 + 2 rank] = tile index * split_max_chunks + chunk,
+//   [2 + 2 items_cap + tile index] = b << 16 | tile.
+// Above kPlanSortMax items the natural order is kept.
 
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(AttnParams p) {
   __shared__ uint32_t s_item[kPlanSortMax];
+  __shared__ int32_t s_tc[kPlanSortMax];
   __shared__ int32_t s_work[kPlanSortMax];
-  __shared__ int32_t s_scan[1024];
+  __shared__ int32_t s_scan[1024];   // items (inclusive scan over threads)
+  __shared__ int32_t s_tscan[1024];  // tiles
   const int tid = threadIdx.x;
   const int B = (int)p.B;
   const int tpt = kPrefillRows / p.G;
+  const int MC = p.split_max_chunks;
+  const int64_t tiles_cap = p.plan_tiles_cap, items_cap = tiles_cap * MC;
+  int32_t* const list = p.ws_plan + 2;
+  int32_t* const tiles = p.ws_plan + 2 + 2 * items_cap;
   const int per = (B + 1023) / 1024;  // sequences per thread
-  int32_t mine = 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = tid * per + i;
-    if (b < B) mine += (int32_t)((p.qsl[b + 1] - p.qsl[b] + tpt - 1) / tpt);
-  }
-  s_scan[tid] = mine;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan
-    const int32_t v = tid >= off ? s_scan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    __syncthreads();
-  }
-  const int32_t total = s_scan[1023];
-  const bool sort = total <= kPlanSortMax;
-  int32_t at = tid ? s_scan[tid - 1] : 0;
+  int32_t mine = 0, mine_t = 0;
   for (int i = 0; i < per; ++i) {
     const int b = tid * per + i;
     if (b >= B) continue;
     const int64_t n = p.qsl[b + 1] - p.qsl[b];
     const int64_t P = p.seq_lens[b] - n;
     const int nt = (int)((n + tpt - 1) / tpt);
-    for (int t = 0; t < nt; ++t, ++at) {
+    mine_t += nt;
+    for (int t = 0; t < nt; ++t) mine += item_chunks(p, P + min((int64_t)(t + 1) * tpt, n));
+  }
+  s_scan[tid] = mine;
+  s_tscan[tid] = mine_t;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scans
+    const int32_t v = tid >= off ? s_scan[tid - off] : 0;
+    const int32_t vt = tid >= off ? s_tscan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    s_tscan[tid] += vt;
+    __syncthreads();
+  }
+  const int32_t total = (int32_t)min((int64_t)s_scan[1023], items_cap);
+  const bool sort = total <= kPlanSortMax;
+  int32_t at = tid ? s_scan[tid - 1] : 0;
+  int32_t gt = tid ? s_tscan[tid - 1] : 0;
+  for (int i = 0; i < per; ++i) {
+    const int b = tid * per + i;
+    if (b >= B) continue;
+    const int64_t n = p.qsl[b + 1] - p.qsl[b];
+    const int64_t P = p.seq_lens[b] - n;
+    const int nt = (int)((n + tpt - 1) / tpt);
+    for (int t = 0; t < nt; ++t, ++gt) {
       const uint32_t item = ((uint32_t)b << 16) | (uint32_t)t;
-      if (sort) {
-        const int64_t w = P + min((int64_t)(t + 1) * tpt, n);
-        s_item[at] = item;
-        s_work[at] = (int32_t)min(w, (int64_t)INT32_MAX);
-      } else {
-        p.ws_plan[1 + at] = (int32_t)item;
+      if (gt < tiles_cap) tiles[gt] = (int32_t)item;
+      const int64_t kv = P + min((int64_t)(t + 1) * tpt, n);
+      const int nch = item_chunks(p, kv);
+      for (int ch = 0; ch < nch; ++ch, ++at) {
+        if (at >= total) continue;
+        const int32_t tc = gt * MC + ch;
+        if (sort) {
+          const int64_t w = nch == 1 ? kv : (ch + 1 < nch ? (int64_t)p.split_keys : kv - (int64_t)ch * p.split_keys);
+          s_item[at] = item;
+          s_tc[at] = tc;
+          s_work[at] = (int32_t)min(w, (int64_t)INT32_MAX);
+        } else {
+          list[2 * at] = (int32_t)item;
+          list[2 * at + 1] = tc;
+        }
       }
     }
   }
-  if (tid == 0) p.ws_plan[0] = total;
+  if (tid == 0) {
+    p.ws_plan[0] = total;
+    p.ws_plan[1] = (int32_t)min((int64_t)s_tscan[1023], tiles_cap);
+  }
   if (!sort) return;
   __syncthreads();
   // rank = items that go first: longer, or as long and listed earlier
   for (int i = tid; i < total; i += 1024) {
     const int32_t w = s_work[i];
     int32_t rank = 0;
+    // (unrolled so that several LDS reads are in flight at once)
+#pragma unroll 8
     for (int j = 0; j < total; ++j) rank += (s_work[j] > w) | ((s_work[j] == w) & (j < i));
-    p.ws_plan[1 + rank] = (int32_t)s_item[i];
+    list[2 * rank] = (int32_t)s_item[i];
+    list[2 * rank + 1] = s_tc[i];
   }
 }
 
@@ -346,6 +433,11 @@ void prefill_kernel(AttnParams p) {
   // position, so that every key of the chunk and none past it is visible)
   int b, chunk = 0;
   int64_t q0, n, L, P, tok0, tok_end;
+  // key split: this item runs keys k0 .. k1 - 1 of the tile (all of them
+  // unless the tile's keys are cut into n_chunks chunks); gtile = the tile's
+  // index in the plan
+  int64_t k0 = 0, k1 = 0;
+  int n_chunks = 1, gtile = 0;
   if constexpr (PREFIX) {
     if (rank >= p.prefix_tiles * p.prefix_chunks) return;
     const int tile = rank / p.prefix_chunks;
@@ -360,7 +452,8 @@ void prefill_kernel(AttnParams p) {
     P = L - 1;
   } else {
     if (rank >= p.ws_plan[0]) return;
-    const uint32_t item = (uint32_t)p.ws_plan[1 + rank];
+    const uint32_t item = (uint32_t)p.ws_plan[2 + 2 * rank];
+    const int32_t tc = p.ws_plan[3 + 2 * rank];
     b = (int)(item >> 16);
     const int tile = (int)(item & 0xFFFF);
     q0 = p.qsl[b];
@@ -369,12 +462,25 @@ void prefill_kernel(AttnParams p) {
     P = L - n;
     tok0 = (int64_t)tile * tpt;
     tok_end = min(tok0 + (int64_t)tpt, n);
+    gtile = tc / p.split_max_chunks;
+    chunk = tc - gtile * p.split_max_chunks;
+    const int64_t kv_all = P + tok_end;
+    n_chunks = item_chunks(p, kv_all);
+    k0 = (int64_t)chunk * p.split_keys;
+    k1 = chunk + 1 < n_chunks ? k0 + p.split_keys : kv_all;
   }
-  const int64_t kv_len = PREFIX ? L : P + tok_end;  // keys some row of this tile sees
+  // keys some row of this item sees, counted from k0 (chunks before the last
+  // end on a tile boundary, so no key past k1 enters a tile)
+  const int64_t kv_len = PREFIX ? L : k1 - k0;
   const int n_tiles = (int)((kv_len + kKeyTile - 1) / kKeyTile);
-  const int64_t first_pos = P + tok0;  // position of the tile's first token
-  // first key tile that reaches past first_pos, i.e. needs the causal mask
-  const int t_diag = first_pos >= kKeyTile - 1 ? (int)((first_pos - (kKeyTile - 1)) / kKeyTile) + 1 : 0;
+  const int64_t first_pos = P + tok0 - k0;  // position of the tile's first token, from k0
+  // the last key this item may use (a row past it, in a chunk before the
+  // last, still stops there: the keys after it are the next chunks')
+  const int64_t last_key = kv_len - 1;
+  // first key tile that reaches past min(first_pos, last_key), i.e. needs the
+  // mask; tiles past the item's keys are always masked
+  const int64_t diag_pos = min(first_pos, last_key);
+  const int t_diag = diag_pos >= kKeyTile - 1 ? (int)((diag_pos - (kKeyTile - 1)) / kKeyTile) + 1 : 0;
 
   TileSrc c;
   c.row_stride = (uint32_t)p.Hkv * D * ESZ;
@@ -383,9 +489,9 @@ void prefill_kernel(AttnParams p) {
   c.vbase = (const char*)p.value_pool + (int64_t)h * D * ESZ;
   // (PREFIX: the chunk's pages, from the row of the item's first sequence)
   c.bt = (const_i64_ptr)(p.block_table + (int64_t)b * p.max_blocks +
-                         (PREFIX ? (int64_t)chunk * p.prefix_chunk_len / kPageSize : 0));
-  c.L = (int)L;
-  c.last_page = (int)((L + 15) >> 4) - 1;
+                         (PREFIX ? (int64_t)chunk * p.prefix_chunk_len / kPageSize : k0 / kPageSize));
+  c.L = (int)(L - k0);  // positions from k0 on
+  c.last_page = (int)((L - k0 + 15) >> 4) - 1;
 
   // logit scale in log2 units; its sign goes into q so maxima are taken on raw scores
   float cs = p.scale * kLog2e;
@@ -399,7 +505,7 @@ void prefill_kernel(AttnParams p) {
   // nb, dims [16 ks + 8 (l >> 5), +8)
   const int qcol = lane & 31, qgrp = lane >> 5;
   bf16x8 qb[NB][NKS];
-  int32_t qrel[NB];  // row position - first_pos - 4 qgrp
+  int32_t qrel[NB];  // min(row position, last_key) - first_pos - 4 qgrp
   bool row_live[NB];
   // (called once the first tile fetches are in flight; every lane loads, rows
   // past the tile from the sequence's first token, so that the loads issue
@@ -420,7 +526,7 @@ void prefill_kernel(AttnParams p) {
         qrel[nb] = -4 * qgrp;
       } else {
         qidx = q0 + (live ? tok : 0);
-        qrel[nb] = (int32_t)((live ? tok : tok_end - 1) - tok0) - 4 * qgrp;
+        qrel[nb] = (int32_t)min((live ? tok : tok_end - 1) - tok0, last_key - first_pos) - 4 * qgrp;
       }
       row_live[nb] = live;
       const __bf16* qrow = (const __bf16*)p.q + (qidx * p.Hq + h * G + r % G) * D;
@@ -616,8 +722,8 @@ void prefill_kernel(AttnParams p) {
   int64_t page_k[2] = {0, 0}, page_v[2] = {0, 0};
   Fp8Tile<D, THREADS> fk, fv;  // fp8 staging: iteration t fetches K(t+2) and V(t)
   auto store8 = [&](int t, int slot) __attribute__((always_inline)) {
-    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[slot], t + 2, L, tid);
-    fp8_store<D, THREADS, true>(fv, (__bf16*)sv[slot], t, L, tid);
+    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[slot], t + 2, c.L, tid);
+    fp8_store<D, THREADS, true>(fv, (__bf16*)sv[slot], t, c.L, tid);
   };
 
   bf16x8 pb_prev[2][NB];
@@ -736,9 +842,9 @@ void prefill_kernel(AttnParams p) {
     // slots that K(t) and V(t-2) held; a barrier per iteration
     load_q();
     fp8_fetch<D, THREADS>(fk, c, c.kbase, 0, tid);
-    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[0], 0, L, tid);
+    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[0], 0, c.L, tid);
     fp8_fetch<D, THREADS>(fk, c, c.kbase, 1, tid);
-    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[1], 1, L, tid);
+    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[1], 1, c.L, tid);
     for (int i = tid; i < TB / 16; i += THREADS) ((u32x4*)sv[1])[i] = u32x4{0u, 0u, 0u, 0u};
     barrier_lds();
     {
@@ -797,6 +903,33 @@ void prefill_kernel(AttnParams p) {
     }
     return;
   }
+  if (n_chunks > 1) {
+    // one chunk of a split item: its partial per row, combined by
+    // prefill_split_merge_kernel (plans past the bound write nothing)
+    if (gtile >= p.plan_tiles_cap) return;
+    const int64_t item_slot = ((int64_t)gtile * p.Hkv + h) * p.split_max_chunks + chunk;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float l = sum_pair(l_run[nb]);
+      const int r = wave * 32 * NB + nb * 32 + qcol;
+      const int64_t slot = item_slot * kPrefillRows + r;
+      float* orow = p.ws_split_o + slot * D;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          f32x4 o;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = acc[d][nb][4 * i4 + e] * out_scale;
+          *(f32x4*)(orow + d * 32 + 8 * i4 + 4 * qgrp) = o;
+        }
+      if (qgrp == 0) {
+        p.ws_split_ml[2 * slot] = m_ref[nb];
+        p.ws_split_ml[2 * slot + 1] = l;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const float l = sum_pair(l_run[nb]);
@@ -815,6 +948,71 @@ void prefill_kernel(AttnParams p) {
         *(u32x2*)(orow + d * 32 + 8 * i4 + 4 * qgrp) = w;
       }
   }
+}
+
+// Key-split prefill: combine the chunks' partials of every row of a split
+// (sequence, query tile, KV head) with a log-sum-exp merge,
+//   M = max_c m_c,  out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,
+// one wave per row (4 per workgroup), the lanes over the head dimension.
+// Chunk 0 starts at key 0, which every row sees, so M is finite; a chunk that
+// lies wholly past a row's position left m = -1e30 and l = 0 there (weight 0).
+template <int D>
+__global__ __launch_bounds__(256) void prefill_split_merge_kernel(AttnParams p) {
+  constexpr int PER = D / 64;
+  const int g = (int)(blockIdx.x / (unsigned)p.Hkv), h = (int)(blockIdx.x % (unsigned)p.Hkv);
+  if (g >= p.ws_plan[1]) return;
+  const int64_t items_cap = p.plan_tiles_cap * p.split_max_chunks;
+  const uint32_t item = (uint32_t)p.ws_plan[2 + 2 * items_cap + g];
+  const int b = (int)(item >> 16), tile = (int)(item & 0xFFFF);
+  const int G = p.G, tpt = kPrefillRows / G;
+  const int64_t q0 = p.qsl[b], n = p.qsl[b + 1] - q0, P = p.seq_lens[b] - n;
+  const int64_t tok0 = (int64_t)tile * tpt, tok_end = min(tok0 + (int64_t)tpt, n);
+  const int nch = item_chunks(p, P + tok_end);
+  if (nch <= 1) return;  // written directly by prefill_kernel
+  const int wave = (int)(threadIdx.x >> 6), lane = (int)(threadIdx.x & 63);
+  const int r = (int)blockIdx.y * 4 + wave;
+  const int64_t tok = tok0 + r / G;
+  if (r >= tpt * G || tok >= tok_end) return;
+  const int64_t base = ((int64_t)g * p.Hkv + h) * p.split_max_chunks;
+  const f32x2* ml = (const f32x2*)p.ws_split_ml;
+  // chunks in groups of 8, every load of a group issued before any is used
+  constexpr int CH = 8;
+  float M = -INFINITY, l = 0.f, o[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += CH) {
+    f32x2 x[CH];
+    float oc[CH][PER];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const int64_t slot = (base + min(c0 + k, nch - 1)) * kPrefillRows + r;
+      x[k] = ml[slot];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) oc[k][i] = p.ws_split_o[slot * D + lane + 64 * i];
+    }
+    float Mc = M;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      x[k][0] = c0 + k < nch ? x[k][0] : -INFINITY;  // repeats of the last chunk weigh 0
+      Mc = fmaxf(Mc, x[k][0]);
+    }
+    const float alpha = M == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mc);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] *= alpha;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+      const float f = __builtin_amdgcn_exp2f(x[k][0] - Mc);
+      l += f * x[k][1];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[i] += f * oc[k][i];
+    }
+    M = Mc;
+  }
+  const float inv = 1.0f / l;
+  __bf16* orow = (__bf16*)p.out + ((q0 + tok) * p.Hq + h * G + r % G) * D;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) orow[lane + 64 * i] = (__bf16)(o[i] * inv);
 }
 
 // Shared-prefix decode, prefix part: one item per (group of prefill_tokens_per_tile
@@ -860,7 +1058,8 @@ hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchE
   if (p.T == 0 || p.B == 0) return hipSuccess;
   hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(1024), 0, stream, p);
   if (ev.begin) (void)hipEventRecord(ev.begin, stream);
-  const dim3 grid((unsigned)(prefill_max_items(p.T, p.B, p.G) * p.Hkv));
+  // one workgroup per (item, KV head): at most plan_tiles_cap * split_max_chunks items
+  const dim3 grid((unsigned)(p.plan_tiles_cap * p.split_max_chunks * p.Hkv));
   constexpr int NB = kPrefillRowBlocks;
   const dim3 block(512 / NB);
   const bool fp8 = p.kv_type == KV_FP8;
@@ -872,6 +1071,11 @@ hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchE
     else hipLaunchKernelGGL((prefill_kernel<2, 64, NB>), grid, block, 0, stream, p);
   }
   if (ev.end) (void)hipEventRecord(ev.end, stream);
+  if (p.split_keys > 0) {
+    const dim3 mgrid((unsigned)(p.plan_tiles_cap * p.Hkv), kPrefillRows / 4);
+    if (p.D == 128) hipLaunchKernelGGL(prefill_split_merge_kernel<128>, mgrid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(prefill_split_merge_kernel<64>, mgrid, dim3(256), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -272,11 +272,36 @@ def test_workspace_size():
     want = align(65 * 4) + align(slots * 2 * 4) + slots * 128 * 4
     assert ws(opts(max_query_len=1, split_tokens=512)) == want
     assert ws(opts(max_query_len=1, split_tokens=0)) == want
-    # prefill: the tile work list, one count plus at most ceil(T / tile) + B
-    # items of 4 bytes (tile = 256 / G query tokens, G = 4 here)
-    assert ws(opts(max_query_len=7)) == (1 + 64 + (64 + 63) // 64) * 4
+    # prefill: the work list, two counts, two words per item and one per
+    # (sequence, query tile); at most ceil(T / tile) + B tiles (tile = 256 / G
+    # query tokens, G = 4 here).  520 workgroups make two rounds on the 256 CUs: no key split
+    tiles = (64 + 63) // 64 + 64
+    assert ws(opts(max_query_len=7)) == align((2 + 2 * tiles + tiles) * 4)
     # invalid arguments
     assert ws(opts(max_query_len=1, split_tokens=20)) == ctypes.c_size_t(-1).value
+
+
+def test_prefill_key_split_workspace():
+    """One 512-token chunk of one sequence on one KV head (G = 4), 8704-key
+    rows: 9 tiles at most, far fewer workgroups than the 256 CUs, so the keys
+    are cut into chunks of max(ceil(8704 / ceil(512 / 9)), 512) = 512 keys, 17
+    per item; the workspace adds (m, l) and D floats per row for every (tile,
+    head, chunk) beside the work list."""
+    lib = pkv.load()
+    q, kp = T([512, 4, 128], B.PKV_BF16), T([65536, 16, 1, 128], B.PKV_BF16)
+    bt = T([1, 544], B.PKV_I64)
+    o = opts(max_query_len=512)
+    n = lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt), ctypes.byref(o))
+    align = lambda v: (v + 255) // 256 * 256
+    tiles, chunks = 512 // 64 + 1, 17
+    rows = tiles * 1 * chunks * 256
+    assert n == align((2 + 2 * tiles * chunks + tiles) * 4) + align(rows * 2 * 4) + rows * 128 * 4
+    # 8 KV heads: 72 workgroups, still short of the CUs -> chunks of
+    # max(ceil(8704 / ceil(512 / 72)), 512) = 1088 keys, 8 per item
+    kp8, q8 = T([65536, 16, 8, 128], B.PKV_BF16), T([512, 32, 128], B.PKV_BF16)
+    n8 = lib.paged_attention_workspace_size(ctypes.byref(q8), ctypes.byref(kp8), ctypes.byref(bt), ctypes.byref(o))
+    rows8 = tiles * 8 * 8 * 256
+    assert n8 == align((2 + 2 * tiles * 8 + tiles) * 4) + align(rows8 * 2 * 4) + rows8 * 128 * 4
 
 
 @pytest.mark.parametrize("pages,max_q,status", [

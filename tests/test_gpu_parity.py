@@ -174,6 +174,51 @@ def test_fewer_kv_heads_than_waves(gpu, hkv, kv, split):
     assert_close(out, ref, kv, f"Hkv={hkv} {kv} split {split}")
 
 
+@pytest.mark.parametrize("hkv,kv,d", [(1, "bf16", 128), (2, "bf16", 128), (1, "fp8_e4m3fn", 128),
+                                      (1, "bf16", 64), (2, "fp8_e4m3fn", 64)])
+def test_key_split_prefill(gpu, hkv, kv, d):
+    """Few workgroups for the CUs (2 sequences, 1-2 KV heads): the prefill
+    cuts every item's keys into 512-key chunks and merges their partials.  The
+    100 new rows sit at positions 3500..3599, across the chunk boundary at
+    3584: for the query tile of rows 3564..3599, the chunk [3072, 3584) is
+    partly masked for some rows although it is not the last, and the last
+    chunk [3584, 3600) lies wholly past the rows before 3584 (weight 0)."""
+    note(f"key-split prefill Hkv={hkv} {kv} D={d}")
+    base = dataclasses.replace(W.SMALL[3], batch=2, n_new=100, old_min=3500, old_max=3500, num_pages=2048)
+    cfg = dataclasses.replace(base, hq=4 * hkv, hkv=hkv, head_dim=d, kv_dtype=kv, q_dtype="bf16")
+    w = W.generate(cfg, DEV, seed=17)
+    kp, vp, out = gpu_step(gpu, w)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, kv, f"key-split prefill Hkv={hkv} {kv} D={d}")
+
+
+def test_key_split_prefill_is_deterministic_and_page_invariant(gpu):
+    """The split path's partials and merge keep the two bitwise invariants:
+    two runs agree, and relabelling the physical pages changes nothing."""
+    note("key-split prefill invariants")
+    base = dataclasses.replace(W.SMALL[3], batch=2, n_new=100, old_min=1500, old_max=4000, num_pages=2048)
+    w = W.generate(dataclasses.replace(base, hq=4, hkv=1), DEV, seed=19)
+    kp, vp, out1 = gpu_step(gpu, w)
+    out2 = gpu_attend(gpu, w, kp, vp)
+    assert torch.equal(out1, out2)
+    wp = W.permute_pages(w, seed=3)
+    _, _, out3 = gpu_step(gpu, wp)
+    assert torch.equal(out1, out3)
+
+
+def test_prefill_shard_of_the_chunked_prefill_workload(gpu):
+    """The chunked-prefill workload at its 8-way head shard (4 query heads on
+    1 KV head: 72 workgroups at most, keys cut into 1088-key chunks) in the
+    launch configuration of the full call; sampled rows against the oracle."""
+    note("chunked prefill workload, 1-KV-head shard")
+    w = W.generate(dataclasses.replace(W.CONFIGS[3], hq=4, hkv=1), DEV)
+    kp, vp, out = gpu_step(gpu, w)
+    rows = sample_rows(w, 24, seed=3)
+    okp, ovp = H.oracle_write(w)
+    ref = H.oracle_attend(w, okp, ovp, sel_tokens=rows)
+    assert_close(as_f64(out)[rows], ref, "bf16", "1-KV-head shard of the chunked prefill workload")
+
+
 def test_single_kv_head_shard_of_the_decode_workload(gpu):
     """The decode workload at its 8-way tensor-parallel shard (4 query heads
     on 1 KV head, 64 sequences of 512..4096 positions), in the launch
