@@ -13,8 +13,11 @@
 //    head-of-group) pairs, row = token * G + g, 256 / G tokens, so the G heads
 //    that share a KV head share every K/V tile.  One workgroup of 8 waves per
 //    item (two per SIMD), each wave owning 32 rows.  A one-workgroup plan
-//    kernel lists the tiles longest first (their KV length sets their cost),
-//    so in-order dispatch fills the CUs greedily.
+//    kernel lists the items longest first (their KV length sets their cost),
+//    so in-order dispatch fills the CUs greedily.  When the items make fewer
+//    than two rounds of workgroups (few KV heads per GPU), every item's keys
+//    are cut into chunks that run as items of their own, each writing (m, l,
+//    O) partials per row, which prefill_split_merge_kernel combines.
 //  * Keys stream in tiles of 32 positions (2 pages) through LDS rings (K and
 //    V).  bf16 tiles go from global memory straight into LDS (buffer_load ...
 //    lds), 6 slots deep, two K and two V tiles behind each barrier; every page
