@@ -237,9 +237,7 @@ def traffic_from_profile(kernel: str):
 
 def tp_shard(W, cid: int, tp: int):
     """Config `cid` with the heads one GPU holds under a `tp`-way head split."""
-    import dataclasses
-    c = W.CONFIGS[cid]
-    return dataclasses.replace(c, name=f"{c.name}-tp{tp}-shard", hq=c.hq // tp, hkv=c.hkv // tp)
+    return W.head_shard(W.CONFIGS[cid], tp)
 
 
 def cpu_baseline(w):

@@ -94,12 +94,17 @@ typedef struct {
                              device->host copy.  A value below the true maximum is
                              undefined behaviour; 0 means "T" (always safe). */
   int32_t split_tokens;   /* decode only: approximate KV positions per split-K partition (a
-                             multiple of the page size, at most 4096).  The decode work is
-                             cut into equal contiguous ranges of (sequence, 32-position)
-                             units, one per workgroup; split_tokens sets how many ranges
-                             (about B * max_blocks * page_size / 2 / split_tokens, rounded
-                             to a multiple of the CU count).  0 = one range per CU.  The
-                             result does not depend on it beyond rounding. */
+                             multiple of the page size, at most 4096).  The decode work, the
+                             list of (sequence, 32-position unit) pairs of all sequences, is
+                             cut into equal contiguous ranges (stream-K; a range may cross
+                             sequence boundaries, and each sequence's pieces are merged by
+                             log-sum-exp).  split_tokens sets how many ranges: about
+                             B * max_blocks * page_size / 2 / split_tokens (half the table's
+                             capacity, the host's estimate of the positions without reading
+                             seq_lens), rounded to a multiple of the CU count and capped at
+                             2048 ranges.  0 = one range per CU (per parallel wave group
+                             when Hkv < 8).  The result does not depend on it beyond
+                             floating-point rounding. */
   void* timing_events[2]; /* optional pair of hipEvent_t (created by the caller), recorded on
                              `stream` immediately before and after the call's main attention
                              kernel: the split-K decode kernel, the prefill kernel or the fp32
@@ -209,8 +214,12 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
 
 /*
  * paged_attention_workspace_size -- bytes of workspace paged_attention needs
- * for these shapes and options (0 if none).  Depends only on shapes, dtypes,
- * opts->max_query_len and opts->split_tokens.  Returns (size_t)-1 if the
+ * for these shapes and options (0 if none).  Depends only on the shapes and
+ * dtypes of q, key_pool and block_table, on opts->max_query_len (decode or
+ * prefill; for prefill the work list grows with the query rows, and with few
+ * KV heads the key split's partials with max_blocks) and on
+ * opts->shared_prefix_pages; opts->split_tokens does not change it.  The
+ * workspace holds no state between calls.  Returns (size_t)-1 if the
  * arguments are invalid (the same ones paged_attention would reject).
  */
 size_t paged_attention_workspace_size(const pkv_tensor* q, const pkv_tensor* key_pool,
@@ -255,26 +264,32 @@ int paged_block_table_from_csr(const pkv_tensor* kv_indptr, const pkv_tensor* kv
  * every slot in [-1 .. num_pages*page_size), no duplicate non-negative slot,
  * query_start_loc non-decreasing from 0 to T, n_b <= L_b, L_b <= max_blocks *
  * page_size, and every block_table entry a sequence reaches in [0, num_pages).
- * slot_mapping may be NULL (attention-only check).  Returns PKV_OK,
- * PKV_ERR_INDEX on the first bad value (and, if `message` is non-NULL, writes
- * a NUL-terminated description of at most `message_len` bytes), or another
- * negative status for bad arguments.
+ * With shared_prefix_pages = N > 0 it also checks the statement a decode call
+ * makes through pkv_attn_opts.shared_prefix_pages: N <= max_blocks, every
+ * sequence with a query row holds more than N * page_size positions, and the
+ * first N entries of all those sequences' rows are the same pages (0 = no
+ * statement).  slot_mapping may be NULL (attention-only check).  Returns
+ * PKV_OK, PKV_ERR_INDEX on the first bad value (and, if `message` is
+ * non-NULL, writes a NUL-terminated description of at most `message_len`
+ * bytes), or another negative status for bad arguments.
  */
 int paged_validate_metadata(const pkv_tensor* slot_mapping, const pkv_tensor* block_table,
                             const pkv_tensor* seq_lens, const pkv_tensor* query_start_loc,
                             int64_t num_pages, int64_t page_size, int64_t num_query_rows,
-                            void* stream, char* message, size_t message_len);
+                            int64_t shared_prefix_pages, void* stream, char* message,
+                            size_t message_len);
 
 /*
  * pkv_check_metadata_host -- the checks of paged_validate_metadata on index
  * arrays already in host memory (all int64, row-major: slots [n_slots] or NULL,
  * block_table [B, max_blocks], seq_lens [B], query_start_loc [B+1]).  Same
- * return values and message convention.
+ * arguments, return values and message convention.
  */
 int pkv_check_metadata_host(const int64_t* slots, int64_t n_slots, const int64_t* block_table,
                             int64_t B, int64_t max_blocks, const int64_t* seq_lens,
                             const int64_t* query_start_loc, int64_t num_pages, int64_t page_size,
-                            int64_t num_query_rows, char* message, size_t message_len);
+                            int64_t num_query_rows, int64_t shared_prefix_pages, char* message,
+                            size_t message_len);
 
 /* Human-readable name of a status code (static string). */
 const char* pkv_status_string(int status);

@@ -73,9 +73,9 @@ def load() -> ctypes.CDLL:
         lib.paged_attention.restype = i32
         lib.paged_attention_workspace_size.argtypes = [P, P, P, ctypes.POINTER(PkvAttnOpts)]
         lib.paged_attention_workspace_size.restype = sz
-        lib.paged_validate_metadata.argtypes = [P, P, P, P, i64, i64, i64, vp, ctypes.c_char_p, sz]
+        lib.paged_validate_metadata.argtypes = [P, P, P, P, i64, i64, i64, i64, vp, ctypes.c_char_p, sz]
         lib.paged_validate_metadata.restype = i32
-        lib.pkv_check_metadata_host.argtypes = [vp, i64, vp, i64, i64, vp, vp, i64, i64, i64,
+        lib.pkv_check_metadata_host.argtypes = [vp, i64, vp, i64, i64, vp, vp, i64, i64, i64, i64,
                                                 ctypes.c_char_p, sz]
         lib.pkv_check_metadata_host.restype = i32
         lib.pkv_status_string.argtypes = [i32]
@@ -107,8 +107,36 @@ def describe(t: torch.Tensor) -> PkvTensor:
     return d
 
 
-def _stream(t: torch.Tensor):
-    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+def _on_one_gpu(what: str, *tensors) -> torch.device:
+    """The GPU every tensor of a call lives on.  A host tensor's pointer would
+    reach the kernels as a device address, so host tensors, and tensors on
+    different GPUs, are refused before anything is launched."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise PagedKVError(-4, f"{what}: every tensor must be in GPU memory (got one on {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise PagedKVError(-4, f"{what}: tensors on {dev} and {t.device}; all must be on one GPU")
+    return dev
+
+
+def _check_scales(what: str, k_scale, v_scale, key_pool) -> None:
+    """Per-KV-head fp8 scales: contiguous float32 [Hkv] on the pool's GPU."""
+    for s_ in (k_scale, v_scale):
+        if s_ is None:
+            continue
+        if s_.dtype != torch.float32 or not s_.is_contiguous() or s_.device != key_pool.device:
+            raise PagedKVError(-5, f"{what}: scales must be contiguous float32 tensors on the pool's device")
+        if s_.dim() != 1 or s_.numel() != key_pool.shape[2]:
+            raise PagedKVError(-2, f"{what}: scales need one entry per KV head")
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
 def _check(status: int, what: str):
@@ -120,8 +148,9 @@ def _check(status: int, what: str):
 def paged_kv_write(k, v, slot_mapping, key_pool, value_pool) -> None:
     """Scatter k/v [T, Hkv, D] into the pools [num_pages, 16, Hkv, D] in place."""
     lib = load()
+    dev = _on_one_gpu("paged_kv_write", k, v, slot_mapping, key_pool, value_pool)
     st = lib.paged_kv_write(describe(k), describe(v), describe(slot_mapping), describe(key_pool),
-                            describe(value_pool), _stream(key_pool))
+                            describe(value_pool), _stream(dev))
     _check(st, "paged_kv_write")
 
 
@@ -130,13 +159,12 @@ def paged_kv_write_fp8(k, v, slot_mapping, key_pool, value_pool, k_scale, v_scal
     scatter them into the fp8 pools [num_pages, 16, Hkv, D] in place;
     k_scale, v_scale: [Hkv] float32 device tensors."""
     lib = load()
-    for s_ in (k_scale, v_scale):
-        if s_ is None or s_.dtype != torch.float32 or s_.device != key_pool.device or not s_.is_contiguous():
-            raise PagedKVError(-5, "paged_kv_write_fp8: scales must be contiguous float32 tensors on the pool's device")
-        if s_.numel() != key_pool.shape[2]:
-            raise PagedKVError(-2, "paged_kv_write_fp8: scales need one entry per KV head")
+    if k_scale is None or v_scale is None:
+        raise PagedKVError(-5, "paged_kv_write_fp8: k_scale and v_scale are required")
+    dev = _on_one_gpu("paged_kv_write_fp8", k, v, slot_mapping, key_pool, value_pool, k_scale, v_scale)
+    _check_scales("paged_kv_write_fp8", k_scale, v_scale, key_pool)
     st = lib.paged_kv_write_fp8(describe(k), describe(v), describe(slot_mapping), describe(key_pool),
-                                describe(value_pool), k_scale.data_ptr(), v_scale.data_ptr(), _stream(key_pool))
+                                describe(value_pool), k_scale.data_ptr(), v_scale.data_ptr(), _stream(dev))
     _check(st, "paged_kv_write_fp8")
 
 
@@ -145,9 +173,10 @@ def paged_block_table_from_csr(kv_indptr, kv_indices, kv_last_page_len, block_ta
     """Fill block_table [B, max_blocks] and seq_lens [B] (int64 device tensors)
     from the packed page-list form of the metadata."""
     lib = load()
+    dev = _on_one_gpu("paged_block_table_from_csr", kv_indptr, kv_indices, kv_last_page_len, block_table, seq_lens)
     st = lib.paged_block_table_from_csr(describe(kv_indptr), describe(kv_indices), describe(kv_last_page_len),
                                         int(page_size), int(pad_page), describe(block_table), describe(seq_lens),
-                                        _stream(block_table))
+                                        _stream(dev))
     _check(st, "paged_block_table_from_csr")
 
 
@@ -195,6 +224,11 @@ def paged_attention(q, key_pool, value_pool, block_table, seq_lens, query_start_
     ``timing_events`` = (begin, end) torch.cuda.Event pair recorded around the
     call's main attention kernel."""
     lib = load()
+    dev = _on_one_gpu("paged_attention", q, key_pool, value_pool, block_table, seq_lens, query_start_loc, out,
+                      k_scale, v_scale, workspace)
+    _check_scales("paged_attention", k_scale, v_scale, key_pool)
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise PagedKVError(-6, "paged_attention: the workspace must be a contiguous uint8 tensor")
     if workspace is None:
         need = paged_attention_workspace_size(q, key_pool, block_table, max_query_len=max_query_len,
                                               split_tokens=split_tokens, shared_prefix_pages=shared_prefix_pages)
@@ -202,23 +236,26 @@ def paged_attention(q, key_pool, value_pool, block_table, seq_lens, query_start_
     opts = _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_events, shared_prefix_pages)
     st = lib.paged_attention(describe(q), describe(key_pool), describe(value_pool), describe(block_table),
                              describe(seq_lens), describe(query_start_loc), ctypes.c_float(scale),
-                             describe(out), ctypes.byref(opts), _stream(q))
+                             describe(out), ctypes.byref(opts), _stream(dev))
     _check(st, "paged_attention")
     return out
 
 
 def paged_validate_metadata(slot_mapping, block_table, seq_lens, query_start_loc, num_pages,
-                            page_size, num_query_rows) -> tuple[int, str]:
+                            page_size, num_query_rows, shared_prefix_pages=0) -> tuple[int, str]:
+    """Synchronous device-metadata check (see the header); returns (status, message)."""
     lib = load()
+    dev = _on_one_gpu("paged_validate_metadata", slot_mapping, block_table, seq_lens, query_start_loc)
     buf = ctypes.create_string_buffer(256)
     st = lib.paged_validate_metadata(describe(slot_mapping) if slot_mapping is not None else None,
                                      describe(block_table), describe(seq_lens), describe(query_start_loc),
-                                     num_pages, page_size, num_query_rows, _stream(block_table), buf, 256)
+                                     num_pages, page_size, num_query_rows, int(shared_prefix_pages),
+                                     _stream(dev), buf, 256)
     return st, buf.value.decode()
 
 
 def check_metadata_host(slot_mapping, block_table, seq_lens, query_start_loc, num_pages, page_size,
-                        num_query_rows) -> tuple[int, str]:
+                        num_query_rows, shared_prefix_pages=0) -> tuple[int, str]:
     """Host-memory metadata check (numpy int64 arrays; slot_mapping may be None)."""
     lib = load()
     buf = ctypes.create_string_buffer(256)
@@ -228,5 +265,5 @@ def check_metadata_host(slot_mapping, block_table, seq_lens, query_start_loc, nu
     st = lib.pkv_check_metadata_host(sm.ctypes.data if sm is not None else None,
                                      sm.shape[0] if sm is not None else 0,
                                      bt.ctypes.data, bt.shape[0], bt.shape[1], sl.ctypes.data, qs.ctypes.data,
-                                     num_pages, page_size, num_query_rows, buf, 256)
+                                     num_pages, page_size, num_query_rows, int(shared_prefix_pages), buf, 256)
     return st, buf.value.decode()

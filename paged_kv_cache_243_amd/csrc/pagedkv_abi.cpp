@@ -215,7 +215,7 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
 
 extern "C" {
 
-int pkv_abi_version(void) { return 3; }
+int pkv_abi_version(void) { return 4; }
 
 const char* pkv_status_string(int status) {
   switch (status) {
@@ -373,12 +373,13 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
 int pkv_check_metadata_host(const int64_t* slots, int64_t n_slots, const int64_t* block_table,
                             int64_t B, int64_t max_blocks, const int64_t* seq_lens,
                             const int64_t* qsl, int64_t num_pages, int64_t page_size,
-                            int64_t num_query_rows, char* message, size_t message_len) {
+                            int64_t num_query_rows, int64_t shared_prefix_pages, char* message,
+                            size_t message_len) {
   auto fail = [&](const char* fmt, long long a, long long b) {
     if (message && message_len) snprintf(message, message_len, fmt, a, b);
     return PKV_ERR_INDEX;
   };
-  if (page_size <= 0 || num_pages < 0) return PKV_ERR_SHAPE;
+  if (page_size <= 0 || num_pages < 0 || shared_prefix_pages < 0) return PKV_ERR_SHAPE;
   const int64_t capacity = num_pages * page_size;
   if (slots) {
     std::vector<int64_t> seen;
@@ -408,13 +409,35 @@ int pkv_check_metadata_host(const int64_t* slots, int64_t n_slots, const int64_t
         return fail("block_table[%lld] names page %lld, out of range", (long long)(b * max_blocks + j), (long long)pg);
     }
   }
+  // a shared-prefix statement: every sequence with a query row holds more
+  // positions than the prefix, and its row starts with the same pages as the
+  // first such sequence's row
+  if (shared_prefix_pages > 0) {
+    if (shared_prefix_pages > max_blocks)
+      return fail("shared_prefix_pages = %lld exceeds the block table width %lld", (long long)shared_prefix_pages,
+                  (long long)max_blocks);
+    int64_t b0 = -1;
+    for (int64_t b = 0; b < B; ++b) {
+      if (qsl[b + 1] == qsl[b]) continue;
+      if (seq_lens[b] <= shared_prefix_pages * page_size)
+        return fail("sequence %lld holds %lld positions, not more than the shared prefix", (long long)b,
+                    (long long)seq_lens[b]);
+      if (b0 < 0) {
+        b0 = b;
+        continue;
+      }
+      for (int64_t j = 0; j < shared_prefix_pages; ++j)
+        if (block_table[b * max_blocks + j] != block_table[b0 * max_blocks + j])
+          return fail("sequence %lld does not share prefix page %lld", (long long)b, (long long)j);
+    }
+  }
   return PKV_OK;
 }
 
 int paged_validate_metadata(const pkv_tensor* slot_mapping, const pkv_tensor* block_table,
                             const pkv_tensor* seq_lens, const pkv_tensor* query_start_loc,
                             int64_t num_pages, int64_t page_size, int64_t num_query_rows,
-                            void* stream, char* message, size_t message_len) {
+                            int64_t shared_prefix_pages, void* stream, char* message, size_t message_len) {
   if (slot_mapping) PKV_TRY(check_tensor(slot_mapping, 1, 8));
   PKV_TRY(check_tensor(block_table, 2, 8));
   PKV_TRY(check_tensor(seq_lens, 1, 8));
@@ -438,7 +461,7 @@ int paged_validate_metadata(const pkv_tensor* slot_mapping, const pkv_tensor* bl
   if (hipStreamSynchronize(s) != hipSuccess) return PKV_ERR_HIP;
   return pkv_check_metadata_host(slot_mapping ? sm.data() : nullptr, (int64_t)sm.size(), bt.data(), B,
                                  block_table->shape[1], sl.data(), qs.data(), num_pages, page_size,
-                                 num_query_rows, message, message_len);
+                                 num_query_rows, shared_prefix_pages, message, message_len);
 }
 
 }  // extern "C"

@@ -100,6 +100,27 @@ SMALL = {
 }
 
 
+def head_shard(cfg: Config, tp: int) -> Config:
+    """The shape one GPU holds when the heads are split ``tp`` ways: Hq / tp
+    query heads and the KV heads they read, max(1, Hkv / tp) of them.  Pages
+    are not split, so page ids and every metadata tensor stay the same.  When
+    tp exceeds Hkv each GPU holds one KV head and the heads are copied
+    tp / Hkv times (page "[Draft] kv paged kernels", ROCm/maxtext #93: the
+    heads_per_shard fix, one KV head per shard at TP=8 on 8 KV heads, the
+    number of copies growing above that)."""
+    if tp < 1 or cfg.hq % tp != 0:
+        raise ValueError(f"{cfg.name}: {cfg.hq} query heads do not split {tp} ways")
+    hkv = max(1, cfg.hkv // tp)
+    if cfg.hkv >= tp and cfg.hkv % tp != 0:
+        raise ValueError(f"{cfg.name}: {cfg.hkv} KV heads do not split {tp} ways")
+    return dataclasses.replace(cfg, name=f"{cfg.name}-tp{tp}-shard", hq=cfg.hq // tp, hkv=hkv)
+
+
+def kv_head_copies(cfg: Config, tp: int) -> int:
+    """How many GPUs hold each KV head under a ``tp``-way head split."""
+    return max(1, tp // cfg.hkv)
+
+
 @dataclass
 class Workload:
     cfg: Config

@@ -127,3 +127,74 @@ def brute_force(q_rows, kv_dtype, kp, vp, block_table_row, L, n, scale, G, ps):
 
 def max_abs(a, b):
     return float(np.max(np.abs(np.asarray(a, dtype=np.float64) - np.asarray(b, dtype=np.float64))))
+
+
+# --------------------------------------------------------------------------
+# special values through the quantising fp8 write, with the code the OCP
+# E4M3FN definition gives for each (1 sign, 4 exponent bits of bias 7, 3
+# mantissa bits; S.1111.111 is NaN, S.1111.110 = 448 the largest finite value,
+# no infinities): NaN keeps its sign, magnitudes past 448 and infinities
+# saturate to +-448, zero keeps its sign, exact ties round to the even code.
+# One row of 2 KV heads x 16 elements; k_scale = [1, 1e-3], v_scale = [1, 0.5].
+
+FP8_SPECIAL_K_SCALE = (1.0, 1e-3)
+FP8_SPECIAL_V_SCALE = (1.0, 0.5)
+# (bf16 bits of x, code of x / k_scale[h], code of x / v_scale[h])
+FP8_SPECIAL_ROW = (
+    # head 0: scale 1 on both pools
+    ((0x7FC0, 0x7F, 0x7F),   # +quiet NaN
+     (0x7FC1, 0x7F, 0x7F),   # +NaN with a payload
+     (0x7F81, 0x7F, 0x7F),   # +signalling NaN
+     (0xFFC0, 0xFF, 0xFF),   # -quiet NaN
+     (0xFF81, 0xFF, 0xFF),   # -NaN with a payload
+     (0xFFFF, 0xFF, 0xFF),   # -NaN, all payload bits set
+     (0x7F80, 0x7E, 0x7E),   # +inf saturates
+     (0xFF80, 0xFE, 0xFE),   # -inf saturates
+     (0x447A, 0x7E, 0x7E),   # 1000 > 448 saturates
+     (0xC47A, 0xFE, 0xFE),   # -1000
+     (0x43E6, 0x7E, 0x7E),   # 460: nearest finite value is 448
+     (0x43E0, 0x7E, 0x7E),   # 448 exactly
+     (0x0DA2, 0x00, 0x00),   # about 1e-30: underflows to +0
+     (0x8DA2, 0x80, 0x80),   # about -1e-30: underflows to -0
+     (0x3A80, 0x00, 0x00),   # 2^-10: half the smallest subnormal 2^-9, a tie, to the even code 0
+     (0x3F00, 0x30, 0x30)),  # 0.5 = 2^(6-7)
+    # head 1: k divided by 1e-3, v by 0.5
+    ((0x7F62, 0x7E, 0x7E),   # about 3.0e38: both quotients overflow binary32 to +inf, saturate
+     (0xFF62, 0xFE, 0xFE),
+     (0x7FC1, 0x7F, 0x7F),   # NaN, either sign, whatever the scale
+     (0xFF81, 0xFF, 0xFF),
+     (0x3F00, 0x7E, 0x38),   # 0.5: k 500 saturates; v 1.0
+     (0x3E80, 0x78, 0x30),   # 0.25: k 250 is nearest 256; v 0.5
+     (0xBE80, 0xF8, 0xB0),   # -0.25
+     (0x7F80, 0x7E, 0x7E),   # +inf
+     (0x0000, 0x00, 0x00),   # +0
+     (0x8000, 0x80, 0x80),   # -0
+     (0x3A80, 0x38, 0x01),   # 2^-10: k 0.97656 is nearest 1.0; v 2^-9 the smallest subnormal
+     (0x3B00, 0x40, 0x02),   # 2^-9: k 1.95312 is nearest 2.0; v 2^-8
+     (0x43E0, 0x7E, 0x7E),   # 448: k 448000 and v 896 saturate
+     (0xC3E0, 0xFE, 0xFE),
+     (0x3C00, 0x50, 0x08),   # 2^-7: k 7.8125 is nearest 8; v 2^-6 the smallest normal
+     (0x3A00, 0x30, 0x00)),  # 2^-11: k 0.48828 is nearest 0.5; v 2^-10 ties to 0
+)
+
+
+def fp8_write_special_values(write_fp8):
+    """Run the special-value row through ``write_fp8(k, v, slots, k_scale,
+    v_scale, key_pool, value_pool)`` (numpy: bf16 bits as uint16, codes as
+    uint8) at slot 19 of a 2-page pool; returns (got_k, want_k, got_v, want_v,
+    untouched) where untouched says every other pool byte kept its 0x5A fill."""
+    Hkv, D = len(FP8_SPECIAL_ROW), len(FP8_SPECIAL_ROW[0])
+    bits = np.array([[c[0] for c in head] for head in FP8_SPECIAL_ROW], dtype=np.uint16)[None]
+    want_k = np.array([[c[1] for c in head] for head in FP8_SPECIAL_ROW], dtype=np.uint8)
+    want_v = np.array([[c[2] for c in head] for head in FP8_SPECIAL_ROW], dtype=np.uint8)
+    kp = np.full((2, 16, Hkv, D), 0x5A, dtype=np.uint8)
+    vp = kp.copy()
+    slot = 19
+    write_fp8(bits, bits.copy(), np.array([slot], dtype=np.int64),
+              np.array(FP8_SPECIAL_K_SCALE, dtype=np.float32), np.array(FP8_SPECIAL_V_SCALE, dtype=np.float32),
+              kp, vp)
+    got_k, got_v = kp[slot // 16, slot % 16].copy(), vp[slot // 16, slot % 16].copy()
+    kp[slot // 16, slot % 16] = 0x5A
+    vp[slot // 16, slot % 16] = 0x5A
+    untouched = bool((kp == 0x5A).all() and (vp == 0x5A).all())
+    return got_k, want_k, got_v, want_v, untouched

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     for n in names:
         assert hasattr(lib, n), n
     assert set(B.EXPORTS) == names
-    assert lib.pkv_abi_version() == 3
+    assert lib.pkv_abi_version() == 4
 
 
 def T(shape, dtype, ptr=FAKE):
@@ -430,7 +430,71 @@ def test_metadata_check_rejects(mutate, needle):
     assert st == -8 and needle in msg, msg
 
 
+def _shared_meta():
+    """Three decode sequences sharing their first two pages (positions 0..31);
+    the middle one has no query row this step."""
+    bt = np.array([[5, 6, 1, 9], [5, 6, 9, 9], [5, 6, 2, 3]], dtype=np.int64)
+    sl = np.array([40, 20, 64], dtype=np.int64)
+    qsl = np.array([0, 1, 1, 2], dtype=np.int64)
+    return bt, sl, qsl
+
+
+def test_shared_prefix_statement_check_accepts_valid():
+    bt, sl, qsl = _shared_meta()
+    # the sequence without a query row may differ and may be shorter
+    bt[1, 1] = 7
+    assert pkv.check_metadata_host(None, bt, sl, qsl, 10, 16, 2, shared_prefix_pages=2) == (0, "")
+    assert pkv.check_metadata_host(None, bt, sl, qsl, 10, 16, 2, shared_prefix_pages=0) == (0, "")
+
+
+@pytest.mark.parametrize("mutate,pages,needle", [
+    (lambda bt, sl, qsl: bt.__setitem__((2, 1), 4), 2, "does not share prefix page 1"),
+    (lambda bt, sl, qsl: bt.__setitem__((2, 0), 4), 2, "does not share prefix page 0"),
+    (lambda bt, sl, qsl: sl.__setitem__(0, 32), 2, "not more than the shared prefix"),
+    (lambda bt, sl, qsl: None, 3, "not more than the shared prefix"),
+    (lambda bt, sl, qsl: None, 6, "exceeds the block table width"),
+])
+def test_shared_prefix_statement_check_rejects(mutate, pages, needle):
+    bt, sl, qsl = _shared_meta()
+    mutate(bt, sl, qsl)
+    st, msg = pkv.check_metadata_host(None, bt, sl, qsl, 10, 16, 2, shared_prefix_pages=pages)
+    assert st == -8 and needle in msg, msg
+
+
 def test_padding_entries_past_the_length_are_not_checked():
     sm, bt, sl, qsl = _meta()
     bt[:, 2:] = 10 ** 9  # never reached by lengths 20 and 17
     assert pkv.check_metadata_host(sm, bt, sl, qsl, 8, 16, 2)[0] == 0
+
+
+def test_binding_refuses_host_tensors_before_any_launch():
+    """A host tensor's pointer must never reach a kernel: the binding refuses
+    tensors that are not in GPU memory (queries, pools, metadata, scales,
+    workspace) with PagedKVError before calling the library."""
+    import torch
+    from paged_kv_cache_243_amd import workloads as W
+    w = W.generate(W.SMALL[2], "cpu")
+    out = torch.empty_like(w.q)
+    attn = lambda **kw: pkv.paged_attention(kw.get("q", w.q), kw.get("kp", w.key_pool), w.value_pool,
+                                            w.block_table, w.seq_lens, w.query_start_loc, w.scale, out,
+                                            max_query_len=1, workspace=torch.empty(16, dtype=torch.uint8))
+    for call in (lambda: attn(),
+                 lambda: pkv.paged_kv_write(w.k_new, w.v_new, w.slot_mapping, w.key_pool, w.value_pool),
+                 lambda: pkv.paged_validate_metadata(w.slot_mapping, w.block_table, w.seq_lens,
+                                                     w.query_start_loc, 512, 16, int(w.q.shape[0])),
+                 lambda: pkv.paged_block_table_from_csr(w.seq_lens, w.seq_lens, w.seq_lens,
+                                                        w.block_table, w.seq_lens)):
+        with pytest.raises(pkv.PagedKVError, match="GPU memory") as e:
+            call()
+        assert e.value.status == -4
+    w5 = W.generate(W.SMALL[5], "cpu")
+    bf = torch.zeros(w5.k_new.shape, dtype=torch.bfloat16)
+    with pytest.raises(pkv.PagedKVError, match="GPU memory"):
+        pkv.paged_kv_write_fp8(bf, bf, w5.slot_mapping, w5.key_pool, w5.value_pool, w5.k_scale, w5.v_scale)
+    with pytest.raises(pkv.PagedKVError) as e:
+        pkv.paged_kv_write_fp8(bf, bf, w5.slot_mapping, w5.key_pool, w5.value_pool, None, w5.v_scale)
+    assert e.value.status == -5
+    # tensors on the meta device carry no memory at all: refused the same way
+    meta_q = torch.empty(w.q.shape, dtype=w.q.dtype, device="meta")
+    with pytest.raises(pkv.PagedKVError, match="GPU memory"):
+        attn(q=meta_q)

@@ -228,5 +228,17 @@ def test_device_metadata_validation(gpu, cid):
     n0 = int(w.query_start_loc[1] - w.query_start_loc[0])
     if n0 > 0:
         bad(2, 0, n0 - 1, "more query rows")
+    shared = w.cfg.shared_prefix_tokens // 16
+    if shared:
+        # the workload's shared-prefix statement holds; a row that stops
+        # sharing a prefix page, and a sequence no longer than the prefix, do not
+        assert gpu.paged_validate_metadata(*args, num_pages, 16, T, shared) == (0, "")
+        other = (int(w.block_table[0, shared - 1]) + 1) % num_pages
+        for i, idx, value, needle in ((1, (3, shared - 1), other, "does not share prefix page"),
+                                      (2, 5, shared * 16, "not more than the shared prefix")):
+            t = [a.clone() for a in args]
+            t[i][idx] = value
+            st, msg = gpu.paged_validate_metadata(*t, num_pages, 16, T, shared)
+            assert st == -8 and needle in msg, (st, msg)
     for a, k in zip(args, keep):
         assert torch.equal(a, k)

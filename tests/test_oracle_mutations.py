@@ -35,14 +35,22 @@ MUTATIONS = {
                                           "uint32_t u = (uint32_t)bits << 15;"),
     "page offset uses the head count": ("const int64_t base = ((page * page_size + o) * Hkv + h) * D;",
                                         "const int64_t base = ((page * Hkv + o) * Hkv + h) * D;"),
+    "fp8 write drops the sign of a NaN": ("isnan(xk) ? (uint8_t)(signbit(xk) ? 0xFF : 0x7F)",
+                                          "isnan(xk) ? (uint8_t)0x7F"),
+    "fp8 write stores infinity as NaN": ("if (isinf(a)) return sign | 0x7E;", "if (isinf(a)) return sign | 0x7F;"),
+    "fp8 write divides the values by the key scales": ("orc_e4m3fn_from_float(xv / v_scale[h])",
+                                                       "orc_e4m3fn_from_float(xv / k_scale[h])"),
 }
 
 
 def _pins_pass() -> bool:
     """A subset of the oracle pins: write vs numpy, codec tables vs torch,
-    paged vs dense SDPA on decode, prefill and fp8 workloads."""
-    import math
+    the quantising write's special values vs the format definition, paged vs
+    dense SDPA on decode, prefill and fp8 workloads."""
     import torch
+    got_k, want_k, got_v, want_v, untouched = H.fp8_write_special_values(oracle.paged_kv_write_fp8)
+    if not (untouched and np.array_equal(got_k, want_k) and np.array_equal(got_v, want_v)):
+        return False
     table = oracle.e4m3fn_table()
     ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).float().double().numpy()
     if not np.array_equal(np.nan_to_num(table, nan=1e9), np.nan_to_num(ref, nan=1e9)):

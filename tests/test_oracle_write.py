@@ -6,6 +6,7 @@ import torch
 
 import oracle
 from paged_kv_cache_243_amd import workloads as W
+from tests import helpers as H
 from tests.helpers import S
 
 
@@ -159,3 +160,14 @@ def test_csr_unpacking_edge_cases_and_rejections():
             oracle.block_table_from_csr(ip, indices, ll, 16, 0, 2)
     with pytest.raises(oracle.OracleError):                # more pages than the row holds
         oracle.block_table_from_csr(indptr, indices, last, 16, 0, 1)
+
+
+def test_quantising_write_special_values_follow_the_format_definition():
+    """NaN of either sign (payloads included) -> the NaN code of that sign;
+    infinities, values past 448 and quotients that overflow binary32 -> +-448;
+    underflow keeps the sign of zero; ties go to the even code.  Expected
+    codes are written out from the E4M3FN definition (tests/helpers.py)."""
+    got_k, want_k, got_v, want_v, untouched = H.fp8_write_special_values(oracle.paged_kv_write_fp8)
+    assert untouched
+    assert np.array_equal(got_k, want_k), (got_k, want_k)
+    assert np.array_equal(got_v, want_v), (got_v, want_v)

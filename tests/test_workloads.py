@@ -1,5 +1,6 @@
 """The seeded generators: determinism, structure, and the geometry facts the
 pages state (tests/golden/geometry.json)."""
+import dataclasses
 import json
 import os
 
@@ -24,6 +25,25 @@ def test_geometry_pins():
     s = g["slot_formula"]
     for page, off, slot in s["cases"]:
         assert W._slots(np.array([page]), np.array([off]), s["page_size"])[0] == slot
+
+
+def test_tensor_parallel_pool_shard_geometry():
+    """Per-GPU pool shape under a head split, against the shapes the maxtext
+    page prints (tests/golden/geometry.json "tp_pool_shard")."""
+    g = json.load(open(GOLDEN))["tp_pool_shard"]
+    pages, ps, hkv, d = g["pool"]
+    cfg = dataclasses.replace(W.CONFIGS[2], num_pages=pages, page_size=ps, hkv=hkv, head_dim=d, hq=4 * hkv)
+    shard = W.head_shard(cfg, g["tp"])
+    assert [shard.num_pages, shard.page_size, shard.hkv, shard.head_dim] == g["shard_pool"]
+    assert shard.hq == cfg.hq // g["tp"] and W.kv_head_copies(cfg, g["tp"]) == 1
+    rep = g["replicated"]
+    big = W.head_shard(cfg, rep["tp"])
+    assert big.hkv == rep["shard_kv_heads"] and W.kv_head_copies(cfg, rep["tp"]) == rep["copies"]
+    head_bytes = pages * ps * d * 2
+    # total pool bytes counted per device and per (head, copy) agree
+    for tp in (1, 2, 4, 8, rep["tp"]):
+        sh = W.head_shard(cfg, tp)
+        assert tp * sh.hkv * head_bytes == cfg.hkv * W.kv_head_copies(cfg, tp) * head_bytes
 
 
 @pytest.mark.parametrize("cid", [2, 3, 4, 5])
