@@ -537,7 +537,9 @@ def main(argv=None) -> int:
         kb5 = decode_kernel_bytes(w5)
         extra["fp8_long_decode"] = {
             "workload": "16 sequences, U{32768..131072} positions, fp8 E4M3FN KV with per-head scales, "
-                        "Hq 64, Hkv 8, split-K over 2048-position partitions",
+                        "Hq 64, Hkv 8, split_tokens 2048: the (sequence, 32-position unit) list cut into "
+                        "equal stream-K ranges (their count set by split_tokens), merged per sequence by "
+                        "log-sum-exp",
             "kernel": "decode_kernel<1,128>",
             "bound": "hbm", "unit": "GB/s",
             "achieved": round(kb5 / (k5 * 1e-3) / 1e9, 1),

@@ -1,0 +1,182 @@
+"""Index probes at full size on every attention path (closed form C4).
+
+A mis-mapped or dropped page moves a long-context output by far less than the
+tolerance (about 5e-4 at the long fp8 decode workload's lengths, against a
+6e-2 bar), so value parity alone cannot see it there.  These tests aim every
+(query row, query head) at one key (tests/probes.py) and check that the output
+is that key's value row.
+
+The targets are spread so that every page a run reads is near a probe: evenly
+spaced over each sequence (spacing at most 2048 positions, below the shortest
+split-K range of the long decode, about 2400 positions), plus the first and the
+last position, the edges of 32-key tiles (every key-split chunk edge is one),
+the old context and the new chunk of a prefill, and the shared prefix and the
+private suffix of a shared-prefix decode.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_243_amd import workloads as W
+from tests import helpers as H
+from tests.gpu_helpers import assert_close, gpu_write, note
+from tests.helpers import S
+from tests.probes import (assert_probes, decode_runs, decode_targets, prefill_runs, prefill_targets,
+                           probe_run, rows_of)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _attend_fn(pkv, w, kp, vp, **kw):
+    def run(q):
+        out = torch.empty_like(q)
+        pkv.paged_attention(q, kp, vp, w.block_table, w.seq_lens, w.query_start_loc, w.scale, out,
+                            k_scale=w.k_scale, v_scale=w.v_scale, max_query_len=w.max_query_len,
+                            split_tokens=w.split_tokens, **kw)
+        torch.cuda.synchronize()
+        return out
+    return run
+
+
+# ---------------------------------------------------------------------------
+# decode
+
+
+@pytest.mark.parametrize("case", ["long-fp8", "decode-bf16", "decode-tp8-shard", "long-fp8-tp8-shard"])
+def test_decode_index_probes_full_size(gpu, case):
+    """Full-size decode workloads in the launch configuration the benchmark
+    times, every page of every sequence probed: the long-context fp8 decode
+    (131072-page pool, page ids past 65535, split 2048), the bf16 decode, and
+    both at the 8-way head shard (one KV head: 8 one-wave parts per
+    workgroup)."""
+    cid = 5 if case.startswith("long") else 2
+    cfg = W.head_shard(W.CONFIGS[cid], 8) if case.endswith("shard") else W.CONFIGS[cid]
+    note(f"decode index probes {case}")
+    w = W.generate(cfg, DEV)
+    kp, vp = gpu_write(gpu, w)
+    rng = np.random.default_rng(11)
+    attend = _attend_fn(gpu, w, kp, vp)
+    runs = decode_runs(w)
+    high, worst = 0, 0.0
+    for run in range(runs):
+        got, want, pages = probe_run(w, kp, vp, decode_targets(w, run, rng), attend)
+        worst = max(worst, assert_probes(got, want, f"{case} run {run}", quiet=run > 0))
+        high += int((pages >= 65536).sum())
+    note(f"{case}: {runs} runs, every page probed, worst error / bound {worst:.3f}, "
+         f"{high} probes on page ids past 65535")
+    if cfg.num_pages > 65536:
+        assert high > 0, "no probe landed on a page id past 65535"
+
+
+def test_shared_prefix_decode_index_probes_full_size(gpu):
+    """The shared-prefix decode (256 sequences on one 128-page prefix, the
+    prefix run once as MFMA tiles and merged with each sequence's split-K
+    decode): even heads probe the shared prefix, odd heads the private
+    suffix (whose last key is the token this step wrote); the runs cover
+    every prefix page for every sequence and every suffix page."""
+    note("shared-prefix decode index probes")
+    w = W.generate(4, DEV)
+    kp, vp = gpu_write(gpu, w)
+    prefix = w.cfg.shared_prefix_tokens
+    n_pre = prefix // 16
+    attend = _attend_fn(gpu, w, kp, vp, shared_prefix_pages=n_pre)
+    lens = S(w.seq_lens)
+    rng = np.random.default_rng(12)
+    B, Hq = w.cfg.batch, w.cfg.hq
+    half = Hq // 2
+    n_suf = -(-(lens - prefix) // 16)
+    runs = max(-(-n_pre // half), int(-(-n_suf.max() // half)))
+    seen_pre = np.zeros((B, n_pre), dtype=bool)
+    seen_suf = [set() for _ in range(B)]
+    worst = 0.0
+    for run in range(runs):
+        t = np.empty((B, Hq), dtype=np.int64)
+        jp = (run * half + np.arange(half)) % n_pre
+        for b in range(B):
+            L = int(lens[b])
+            js = (run * half + np.arange(half)) % int(n_suf[b])
+            suf = prefix + js * 16 + rng.integers(0, 16, half)
+            suf = np.where(js == n_suf[b] - 1, L - 1, np.minimum(suf, L - 1))
+            t[b, 0::2] = jp * 16 + rng.integers(0, 16, half)
+            t[b, 1::2] = suf
+            seen_pre[b, jp] = True
+            seen_suf[b].update(((suf - prefix) // 16).tolist())
+        got, want, _ = probe_run(w, kp, vp, t, attend)
+        worst = max(worst, assert_probes(got, want, f"shared prefix run {run}", quiet=run > 0))
+    assert seen_pre.all() and all(seen_suf[b] == set(range(int(n_suf[b]))) for b in range(B))
+    note(f"shared prefix: {runs} runs, every prefix and suffix page probed, worst error / bound {worst:.3f}")
+
+
+# ---------------------------------------------------------------------------
+# prefill
+
+
+def _c3(kv="bf16", tp=1):
+    cfg = W.CONFIGS[3]
+    if kv != "bf16":
+        cfg = dataclasses.replace(cfg, kv_dtype=kv, name=cfg.name + "-fp8")
+    return W.head_shard(cfg, tp) if tp > 1 else cfg
+
+
+@pytest.mark.parametrize("kv,tp", [("bf16", 1), ("fp8_e4m3fn", 1), ("bf16", 8), ("bf16", 4), ("fp8_e4m3fn", 8)])
+def test_prefill_index_probes_every_row_full_size(gpu, kv, tp):
+    """Every query row and head of the chunked-prefill workload (8 sequences x
+    512 new tokens on contexts up to 8192), bf16 and fp8 pools; at the 8- and
+    4-way head shards (1 and 2 KV heads) the call cuts every item's keys into
+    chunks merged by log-sum-exp, and the probes at 32-key edges sit on every
+    chunk edge."""
+    cfg = _c3(kv, tp)
+    note(f"prefill index probes {cfg.name}")
+    w = W.generate(cfg, DEV)
+    kp, vp = gpu_write(gpu, w)
+    rng = np.random.default_rng(13)
+    attend = _attend_fn(gpu, w, kp, vp)
+    seq, _ = rows_of(w)
+    seen = set()
+    for run in range(prefill_runs(w)):
+        t = prefill_targets(w, rng, run)
+        got, want, _ = probe_run(w, kp, vp, t, attend)
+        assert_probes(got, want, f"{cfg.name} run {run}")
+        seen.update(zip(np.repeat(seq, t.shape[1]).tolist(), (t // 16).reshape(-1).tolist()))
+    lens = S(w.seq_lens)
+    assert all((b, j) in seen for b in range(len(lens)) for j in range(-(-int(lens[b]) // 16))), \
+        "a page no probe reached"
+
+
+@pytest.mark.parametrize("tp", [8, 4])
+def test_key_split_prefill_never_reads_unread_rows(gpu, tp):
+    """At the head shards the prefill runs as key chunks: NaN in every pool
+    row no sequence reads leaves the output finite and bit-identical to the
+    output with those rows refilled with finite bytes."""
+    cfg = _c3("bf16", tp)
+    note(f"key-split prefill poison {cfg.name}")
+    w = W.generate(cfg, DEV)
+    kp, vp = gpu_write(gpu, w)
+    out = _attend_fn(gpu, w, kp, vp)(w.q)
+    assert torch.isfinite(out.float()).all()
+    w2 = W.refill_unread_rows(dataclasses.replace(w, key_pool=kp, value_pool=vp), 0x3C)
+    out2 = _attend_fn(gpu, w2, w2.key_pool, w2.value_pool)(w.q)
+    assert np.array_equal(S(out).view(np.uint8), S(out2).view(np.uint8))
+
+
+def test_prefill_plan_beyond_the_sorted_list_and_1024_sequences(gpu):
+    """3000 sequences of 3 new tokens: more work items than the plan kernel
+    orders by length (it keeps their natural order) and more sequences than
+    its threads (each thread lists several), against the oracle on every row,
+    and against index probes."""
+    cfg = dataclasses.replace(W.SMALL[3], name="prefill-3000-short", batch=3000, hq=8, hkv=2, n_new=3,
+                              old_min=0, old_max=120, num_pages=30000)
+    note(f"prefill plan, {cfg.batch} sequences")
+    w = W.generate(cfg, DEV)
+    kp, vp = gpu_write(gpu, w)
+    attend = _attend_fn(gpu, w, kp, vp)
+    out = attend(w.q)
+    ref = H.oracle_attend(w, S(kp).copy(), S(vp).copy())
+    assert_close(out, ref, "bf16", "3000 short prefills")
+    rng = np.random.default_rng(14)
+    for run in range(prefill_runs(w)):
+        got, want, _ = probe_run(w, kp, vp, prefill_targets(w, rng, run), attend)
+        assert_probes(got, want, f"3000 short prefills run {run}")
