@@ -69,7 +69,9 @@ enum {
   PKV_ERR_SCALE = -5,       /* non-finite scale, or fp8 pool without k/v scales */
   PKV_ERR_WORKSPACE = -6,   /* workspace missing or smaller than required */
   PKV_ERR_HIP = -7,         /* the HIP runtime reported an error */
-  PKV_ERR_INDEX = -8        /* (validator only) an index value is out of range */
+  PKV_ERR_INDEX = -8,       /* (validator only) an index value is out of range */
+  PKV_ERR_SCRATCH = -9      /* (paged_attention_noalloc only) the call needs more than its
+                               fixed scratch of PKV_NOALLOC_SCRATCH_BYTES */
 };
 
 /* A dense row-major tensor in device memory. */
@@ -211,6 +213,35 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
                     const pkv_tensor* block_table, const pkv_tensor* seq_lens,
                     const pkv_tensor* query_start_loc, float scale, pkv_tensor* out,
                     const pkv_attn_opts* opts, void* stream);
+
+/*
+ * paged_attention_noalloc -- paged_attention for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, computation and results as
+ * paged_attention (the same kernels and launch shapes: bit-identical output),
+ * except that opts->workspace must be NULL and opts->workspace_bytes 0: the
+ * workspace is a fixed region of PKV_NOALLOC_SCRATCH_BYTES that the library
+ * holds in device memory of its own, one per GPU, from the first call on that
+ * GPU until the process ends.  The call allocates and frees nothing.
+ *
+ * The region is sized by this device's own decode grid (smaller than the
+ * device-independent size paged_attention_workspace_size reports); a call
+ * that needs more than PKV_NOALLOC_SCRATCH_BYTES returns PKV_ERR_SCRATCH
+ * before anything is enqueued (128 MiB holds every workload of the design
+ * notes, the largest being the key-split prefill of 8 sequences x 512 tokens
+ * on 8704-position contexts with 1 or 2 KV heads, about 77 MB).  Nothing in
+ * the region needs to start at zero: every kernel writes what a later kernel
+ * of the same call reads.  All calls on one GPU share its region, so calls
+ * that may overlap on one GPU (different streams without ordering between
+ * them) race and give unspecified output; order them on one stream.
+ * Returns PKV_OK, PKV_ERR_SCRATCH, PKV_ERR_WORKSPACE for a non-NULL
+ * opts->workspace, or any status paged_attention returns.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int paged_attention_noalloc(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_tensor* value_pool,
+                            const pkv_tensor* block_table, const pkv_tensor* seq_lens,
+                            const pkv_tensor* query_start_loc, float scale, pkv_tensor* out,
+                            const pkv_attn_opts* opts, void* stream);
 
 /*
  * paged_attention_workspace_size -- bytes of workspace paged_attention needs

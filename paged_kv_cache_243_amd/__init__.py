@@ -16,6 +16,7 @@ from ._binding import (  # noqa: F401
     check_metadata_host,
     load,
     paged_attention,
+    paged_attention_noalloc,
     paged_block_table_from_csr,
     paged_attention_workspace_size,
     paged_kv_write,

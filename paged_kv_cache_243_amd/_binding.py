@@ -21,13 +21,15 @@ PKV_F32, PKV_BF16, PKV_FP8_E4M3FN, PKV_I64 = 0, 1, 2, 3
 STATUS = {
     0: "PKV_OK", -1: "PKV_ERR_NULL", -2: "PKV_ERR_SHAPE", -3: "PKV_ERR_DTYPE",
     -4: "PKV_ERR_UNSUPPORTED", -5: "PKV_ERR_SCALE", -6: "PKV_ERR_WORKSPACE",
-    -7: "PKV_ERR_HIP", -8: "PKV_ERR_INDEX",
+    -7: "PKV_ERR_HIP", -8: "PKV_ERR_INDEX", -9: "PKV_ERR_SCRATCH",
     -20: "PKV_ERR_NO_PAGES", -21: "PKV_ERR_BAD_HANDLE", -22: "PKV_ERR_DIRTY",
 }
 # every symbol include/pagedkv.h declares
-EXPORTS = ("paged_kv_write", "paged_kv_write_fp8", "paged_block_table_from_csr", "paged_attention", "paged_attention_workspace_size",
-           "paged_validate_metadata", "pkv_check_metadata_host", "pkv_status_string",
-           "pkv_abi_version")
+EXPORTS = ("paged_kv_write", "paged_kv_write_fp8", "paged_block_table_from_csr", "paged_attention",
+           "paged_attention_noalloc", "paged_attention_workspace_size", "paged_validate_metadata",
+           "pkv_check_metadata_host", "pkv_status_string", "pkv_abi_version")
+# fixed scratch of paged_attention_noalloc (PKV_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class PkvTensor(ctypes.Structure):
@@ -71,6 +73,8 @@ def load() -> ctypes.CDLL:
         lib.paged_kv_write_fp8.restype = i32
         lib.paged_attention.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, ctypes.POINTER(PkvAttnOpts), vp]
         lib.paged_attention.restype = i32
+        lib.paged_attention_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, ctypes.POINTER(PkvAttnOpts), vp]
+        lib.paged_attention_noalloc.restype = i32
         lib.paged_attention_workspace_size.argtypes = [P, P, P, ctypes.POINTER(PkvAttnOpts)]
         lib.paged_attention_workspace_size.restype = sz
         lib.paged_validate_metadata.argtypes = [P, P, P, P, i64, i64, i64, i64, vp, ctypes.c_char_p, sz]
@@ -238,6 +242,24 @@ def paged_attention(q, key_pool, value_pool, block_table, seq_lens, query_start_
                              describe(seq_lens), describe(query_start_loc), ctypes.c_float(scale),
                              describe(out), ctypes.byref(opts), _stream(dev))
     _check(st, "paged_attention")
+    return out
+
+
+def paged_attention_noalloc(q, key_pool, value_pool, block_table, seq_lens, query_start_loc, scale, out, *,
+                            k_scale=None, v_scale=None, max_query_len=None, split_tokens=0,
+                            timing_events=None, shared_prefix_pages=0) -> torch.Tensor:
+    """paged_attention with the library's fixed per-GPU scratch as its
+    workspace: nothing is allocated, by the library or here.  Calls that may
+    overlap on one GPU share that scratch (order them on one stream)."""
+    lib = load()
+    dev = _on_one_gpu("paged_attention_noalloc", q, key_pool, value_pool, block_table, seq_lens,
+                      query_start_loc, out, k_scale, v_scale)
+    _check_scales("paged_attention_noalloc", k_scale, v_scale, key_pool)
+    opts = _opts(k_scale, v_scale, None, max_query_len, split_tokens, timing_events, shared_prefix_pages)
+    st = lib.paged_attention_noalloc(describe(q), describe(key_pool), describe(value_pool), describe(block_table),
+                                     describe(seq_lens), describe(query_start_loc), ctypes.c_float(scale),
+                                     describe(out), ctypes.byref(opts), _stream(dev))
+    _check(st, "paged_attention_noalloc")
     return out
 
 

@@ -737,15 +737,17 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 
-size_t decode_workspace_bytes(int64_t B, int Hq, int D) {
-  const size_t slots = (size_t)(B + kDecodeMaxParts) * Hq;
+// partial slots: one per (sequence + part, query head); a segment of sequence
+// b in part w writes slot b + w < B + parts
+size_t decode_workspace_bytes(int64_t B, int Hq, int D, int parts) {
+  const size_t slots = (size_t)(B + parts) * Hq;
   return align256((size_t)(B + 1) * sizeof(int32_t)) + align256(slots * 2 * sizeof(float)) +
-         slots * D * sizeof(float);
+         align256(slots * D * sizeof(float));
 }
 
-void decode_workspace_carve(AttnParams& p, void* workspace) {
+void decode_workspace_carve(AttnParams& p, void* workspace, int parts) {
   char* w = (char*)workspace;
-  const size_t slots = (size_t)(p.B + kDecodeMaxParts) * p.Hq;
+  const size_t slots = (size_t)(p.B + parts) * p.Hq;
   p.ws_cum = (int32_t*)w;
   w += align256((size_t)(p.B + 1) * sizeof(int32_t));
   p.ws_ml = (float*)w;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "pagedkv.h"
+
 namespace pkv {
 
 enum KvType { KV_F32 = 0, KV_BF16 = 1, KV_FP8 = 2 };
@@ -90,11 +92,13 @@ hipError_t launch_csr_to_block_table(const int64_t* indptr, const int64_t* indic
                                      int64_t pad_page, int64_t* block_table, int64_t* seq_lens,
                                      hipStream_t stream);
 
-// workspace helpers shared by the ABI layer and the launchers
-size_t decode_workspace_bytes(int64_t B, int Hq, int D);
+// workspace helpers shared by the ABI layer and the launchers.  The decode
+// partial slots are sized for `parts` partition ranges: kDecodeMaxParts for a
+// workspace that fits any device, or the grid's own count.
+size_t decode_workspace_bytes(int64_t B, int Hq, int D, int parts);
 // partition ranges of the decode work: a multiple of the parts one workgroup runs
 int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu, int Hkv);
-void decode_workspace_carve(AttnParams& p, void* workspace);
+void decode_workspace_carve(AttnParams& p, void* workspace, int parts);
 constexpr int kDecodeMaxParts = 2048;
 constexpr int kDecodeMaxSeqs = 4096;
 // decides the prefill key split (fills plan_tiles_cap, split_keys,
@@ -108,6 +112,16 @@ constexpr int kMaxPrefixChunks = 8;
 size_t prefix_plan(AttnParams& p, int64_t prefix_len);
 void prefix_workspace_carve(AttnParams& p, void* region);
 int prefill_tokens_per_tile(int G);
+
+// paged_attention whose workspace is a fixed region of region_bytes bytes on
+// each device, resolved by region(device) once the call is known to fit
+// (PKV_ERR_SCRATCH otherwise); decode partials are sized for the device's own
+// grid.  Implemented by the ABI layer.
+int attention_in_region(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_tensor* value_pool,
+                        const pkv_tensor* block_table, const pkv_tensor* seq_lens,
+                        const pkv_tensor* query_start_loc, float scale, pkv_tensor* out,
+                        const pkv_attn_opts* opts, size_t region_bytes, void* (*region)(int device),
+                        void* stream);
 int64_t prefill_max_items(int64_t T, int64_t B, int G);
 
 }  // namespace pkv

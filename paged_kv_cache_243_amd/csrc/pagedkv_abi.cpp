@@ -66,11 +66,25 @@ bool same_shape(const pkv_tensor* a, const pkv_tensor* b) {
     if (_st != PKV_OK) return _st; \
   } while (0)
 
-// Compute units of the current device (cached per device).
-int device_cu_count() {
-  static int cached[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+constexpr int kMaxDevices = 64;
+
+// The device `stream` runs on (the current device for the null stream), or -1.
+int stream_device(hipStream_t stream) {
+  int dev = -1;
+  if (stream != nullptr) {
+    hipDevice_t d;
+    if (hipStreamGetDevice(stream, &d) == hipSuccess) dev = (int)d;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    dev = -1;
+  }
+  return dev >= 0 && dev < kMaxDevices ? dev : -1;
+}
+
+// Compute units of device `dev` (cached per device); 256, MI355X's count, when
+// the device cannot be queried.
+int device_cu_count(int dev) {
+  static int cached[kMaxDevices] = {0};
+  if (dev < 0 || dev >= kMaxDevices) return 256;
   if (cached[dev] == 0) {
     int n = 0;
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
@@ -83,13 +97,18 @@ struct AttnPlan {
   AttnParams p;
   enum { kNone, kF32, kDecode, kPrefill } kernel;
   size_t workspace;
+  int slot_parts;  // decode: partition ranges the partial slots are sized for
 };
 
 // Validates the attention arguments and fills the launch plan (no HIP calls).
+// n_cu > 0 fixes the decode grid for a device of that many CUs (0: a size
+// query, no grid); `tight` sizes the decode partials for that grid instead of
+// for any device.
 int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_tensor* value_pool,
                    const pkv_tensor* block_table, const pkv_tensor* seq_lens,
                    const pkv_tensor* query_start_loc, float scale, const pkv_tensor* out,
-                   const pkv_attn_opts* opts, bool check_runtime_args, AttnPlan& plan) {
+                   const pkv_attn_opts* opts, bool check_runtime_args, int n_cu, bool tight,
+                   AttnPlan& plan) {
   PKV_TRY(check_tensor(q, 3, 16));
   PKV_TRY(check_tensor(key_pool, 4, 16));
   if (value_pool) PKV_TRY(check_tensor(value_pool, 4, 16));
@@ -189,7 +208,9 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
     // the decode kernel counts 32-position units of all sequences in 32 bits
     if (B * ((max_blocks * kPageSize + 31) / 32) > INT32_MAX) return PKV_ERR_UNSUPPORTED;
     p.split_tokens = split;
-    plan.workspace = pkv::decode_workspace_bytes(B, (int)Hq, (int)D);
+    if (n_cu > 0) p.grid_parts = pkv::decode_grid_parts(B, max_blocks * kPageSize, split, n_cu, (int)Hkv);
+    plan.slot_parts = tight ? p.grid_parts : pkv::kDecodeMaxParts;
+    plan.workspace = pkv::decode_workspace_bytes(B, (int)Hq, (int)D, plan.slot_parts);
     if (shared_pages > 0) plan.workspace += pkv::prefix_plan(p, shared_pages * kPageSize);
   } else {
     plan.kernel = AttnPlan::kPrefill;
@@ -202,16 +223,68 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
     pkv::prefill_split_plan(p);
     plan.workspace = pkv::prefill_workspace_bytes(p);
   }
-
-  if (check_runtime_args && plan.workspace > 0) {
-    if (!opts || !opts->workspace) return PKV_ERR_WORKSPACE;
-    if (opts->workspace_bytes < plan.workspace) return PKV_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(opts->workspace) % 16 != 0) return PKV_ERR_WORKSPACE;
-  }
   return PKV_OK;
 }
 
+// Enqueues the planned attention with its workspace at `ws`.
+int launch_attention(AttnPlan& plan, void* ws, const pkv_attn_opts* opts, hipStream_t s) {
+  AttnParams& p = plan.p;
+  hipError_t err = hipSuccess;
+  pkv::LaunchEvents ev;
+  if (opts) {
+    ev.begin = (hipEvent_t)opts->timing_events[0];
+    ev.end = (hipEvent_t)opts->timing_events[1];
+  }
+  switch (plan.kernel) {
+    case AttnPlan::kNone:
+      return PKV_OK;
+    case AttnPlan::kF32:
+      err = pkv::launch_attention_f32(p, s, ev);
+      break;
+    case AttnPlan::kDecode:
+      pkv::decode_workspace_carve(p, ws, plan.slot_parts);
+      if (p.prefix_len > 0)
+        pkv::prefix_workspace_carve(p, (char*)ws + pkv::decode_workspace_bytes(p.B, p.Hq, p.D, plan.slot_parts));
+      err = pkv::launch_decode(p, s, ev);
+      break;
+    case AttnPlan::kPrefill:
+      pkv::prefill_workspace_carve(p, ws);
+      err = pkv::launch_prefill(p, s, ev);
+      break;
+  }
+  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
 }  // namespace
+
+namespace pkv {
+
+// paged_attention with its workspace in a fixed region of `region_bytes`
+// bytes that `region(device)` resolves for the stream's device; the region is
+// resolved only once the arguments are known to fit in it.  The decode
+// partials are sized for this device's own grid.
+int attention_in_region(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_tensor* value_pool,
+                        const pkv_tensor* block_table, const pkv_tensor* seq_lens,
+                        const pkv_tensor* query_start_loc, float scale, pkv_tensor* out,
+                        const pkv_attn_opts* opts, size_t region_bytes, void* (*region)(int device),
+                        void* stream) {
+  if (opts && (opts->workspace || opts->workspace_bytes)) return PKV_ERR_WORKSPACE;
+  const hipStream_t s = (hipStream_t)stream;
+  const int dev = stream_device(s);
+  AttnPlan plan;
+  PKV_TRY(plan_attention(q, key_pool, value_pool, block_table, seq_lens, query_start_loc, scale, out, opts,
+                         true, device_cu_count(dev), true, plan));
+  if (plan.workspace > region_bytes) return PKV_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (plan.workspace > 0) {
+    if (dev < 0) return PKV_ERR_HIP;
+    ws = region(dev);
+    if (ws == nullptr) return PKV_ERR_HIP;
+  }
+  return launch_attention(plan, ws, opts, s);
+}
+
+}  // namespace pkv
 
 extern "C" {
 
@@ -228,6 +301,9 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE: return "workspace missing or too small";
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_INDEX: return "index value out of range";
+    case PKV_ERR_SCRATCH:
+      return "the call needs more workspace than the fixed scratch of paged_attention_noalloc "
+             "(PKV_NOALLOC_SCRATCH_BYTES); use paged_attention with a caller workspace";
     case PKV_ERR_NO_PAGES: return "too few free pages";
     case PKV_ERR_BAD_HANDLE: return "stale or unknown handle, or a page released more often than held";
     case PKV_ERR_DIRTY: return "a page to describe is dirty (not confirmed overwritten since it was freed)";
@@ -326,7 +402,7 @@ size_t paged_attention_workspace_size(const pkv_tensor* q, const pkv_tensor* key
                                       const pkv_tensor* block_table, const pkv_attn_opts* opts) {
   AttnPlan plan;
   if (plan_attention(q, key_pool, nullptr, block_table, nullptr, nullptr, 1.0f, nullptr, opts,
-                     false, plan) != PKV_OK)
+                     false, 0, false, plan) != PKV_OK)
     return (size_t)-1;
   return plan.workspace;
 }
@@ -335,37 +411,16 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
                     const pkv_tensor* block_table, const pkv_tensor* seq_lens,
                     const pkv_tensor* query_start_loc, float scale, pkv_tensor* out,
                     const pkv_attn_opts* opts, void* stream) {
+  const hipStream_t s = (hipStream_t)stream;
   AttnPlan plan;
   PKV_TRY(plan_attention(q, key_pool, value_pool, block_table, seq_lens, query_start_loc, scale,
-                         out, opts, true, plan));
-  AttnParams& p = plan.p;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t err = hipSuccess;
-  pkv::LaunchEvents ev;
-  if (opts) {
-    ev.begin = (hipEvent_t)opts->timing_events[0];
-    ev.end = (hipEvent_t)opts->timing_events[1];
+                         out, opts, true, device_cu_count(stream_device(s)), false, plan));
+  if (plan.workspace > 0) {
+    if (!opts || !opts->workspace) return PKV_ERR_WORKSPACE;
+    if (opts->workspace_bytes < plan.workspace) return PKV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(opts->workspace) % 16 != 0) return PKV_ERR_WORKSPACE;
   }
-  switch (plan.kernel) {
-    case AttnPlan::kNone:
-      return PKV_OK;
-    case AttnPlan::kF32:
-      err = pkv::launch_attention_f32(p, s, ev);
-      break;
-    case AttnPlan::kDecode:
-      pkv::decode_workspace_carve(p, opts->workspace);
-      if (p.prefix_len > 0)
-        pkv::prefix_workspace_carve(p, (char*)opts->workspace + pkv::decode_workspace_bytes(p.B, p.Hq, p.D));
-      p.grid_parts = pkv::decode_grid_parts(p.B, p.max_blocks * kPageSize, p.split_tokens, device_cu_count(),
-                                            (int)p.Hkv);
-      err = pkv::launch_decode(p, s, ev);
-      break;
-    case AttnPlan::kPrefill:
-      pkv::prefill_workspace_carve(p, opts->workspace);
-      err = pkv::launch_prefill(p, s, ev);
-      break;
-  }
-  return err == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+  return launch_attention(plan, opts ? opts->workspace : nullptr, opts, s);
 }
 
 // Host-memory form of the metadata check; paged_validate_metadata copies the

@@ -498,3 +498,26 @@ def test_binding_refuses_host_tensors_before_any_launch():
     meta_q = torch.empty(w.q.shape, dtype=w.q.dtype, device="meta")
     with pytest.raises(pkv.PagedKVError, match="GPU memory"):
         attn(q=meta_q)
+
+
+def test_noalloc_refuses_before_touching_a_device():
+    """paged_attention_noalloc checks its arguments and that the call fits in
+    its fixed scratch before it resolves the scratch or launches anything: a
+    caller workspace is refused, and so is a decode of 4096 sequences x 128
+    query heads (about 276 MiB of partials for 128 MiB of scratch)."""
+    lib = pkv.load()
+    B_, Hq, Hkv, D = 4096, 128, 8, 128
+    q, out = T([B_, Hq, D], B.PKV_BF16), T([B_, Hq, D], B.PKV_BF16)
+    kp, vp = T([8192, 16, Hkv, D], B.PKV_BF16), T([8192, 16, Hkv, D], B.PKV_BF16)
+    bt, sl, qsl = T([B_, 4], B.PKV_I64), T([B_], B.PKV_I64), T([B_ + 1], B.PKV_I64)
+    call = lambda o: lib.paged_attention_noalloc(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(vp),
+                                                 ctypes.byref(bt), ctypes.byref(sl), ctypes.byref(qsl),
+                                                 ctypes.c_float(0.1), ctypes.byref(out), ctypes.byref(o), None)
+    o = B.PkvAttnOpts()
+    o.max_query_len = 1
+    assert call(o) == -9
+    assert "PKV_NOALLOC_SCRATCH_BYTES" in lib.pkv_status_string(-9).decode()
+    o.workspace, o.workspace_bytes = FAKE, 1 << 30
+    assert call(o) == -6
+    assert B.NOALLOC_SCRATCH_BYTES == 128 << 20
+    assert "#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in open(HEADER).read()
