@@ -19,7 +19,10 @@ The printed JSON line carries:
   prefill, ... the other workloads (chunked prefill TFLOP/s against the bf16
                MFMA peak, shared-prefix decode, fp8 long-context decode, and
                both decode workloads at their 8-way head shard: 1 KV head),
-  cpu_baseline the CPU oracle on the same decode workload.
+  stream_ceiling  a plain read-only kernel over the same pages (context),
+  cpu_baseline the CPU oracle on the same decode workload (headline value),
+               and on sampled parts of the prefill and long fp8 decode
+               workloads, write and attention timed separately.
 Algorithmic bytes count each sequence's K and V rows once per KV head, plus q,
 out and the block_table entries read; flops count causally visible (query,
 key) pairs, 4 * D per pair per head.
@@ -213,6 +216,37 @@ def time_steps(runner, torch, steps, warmup, flush, progress="", kernel_events=T
     return t
 
 
+def time_graph_steps(runner, torch, steps, warmup, flush, progress=""):
+    """The same write + attention step captured once as a HIP graph (torch's
+    stream capture of the library's launches) and replayed: one replay per
+    step, the cache flush before each outside the timed region, HIP events
+    around each replay.  Returns the per-step times (ms)."""
+    for _ in range(warmup):
+        runner.write()
+        runner.attend()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        runner.write()
+        runner.attend()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        ev[i][0].record()
+        g.replay()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = [a.elapsed_time(b) for a, b in ev]
+    if progress:
+        log(f"{progress} (HIP graph): {steps} steps, median step {statistics.median(ms):.4f} ms")
+    del g
+    return ms
+
+
 def time_workload(runner, torch, steps, warmup, flush, progress):
     """Two timed passes: whole steps without in-call events, then the main
     kernel alone with them."""
@@ -240,40 +274,141 @@ def tp_shard(W, cid: int, tp: int):
     return W.head_shard(W.CONFIGS[cid], tp)
 
 
-def cpu_baseline(w):
-    """The oracle as it stands (fp64, OpenMP) on the whole decode step of the
-    same workload: write of the 64 new tokens + attention of all 64 rows."""
-    import numpy as np
-    import oracle
-    from paged_kv_cache_243_amd import workloads as W
-    S = W.to_numpy_storage
-    threads = len(os.sched_getaffinity(0))
-    os.environ.setdefault("OMP_NUM_THREADS", str(threads))
-    kp, vp = S(w.key_pool).copy(), S(w.value_pool).copy()
-    k, v, sm = S(w.k_new), S(w.v_new), S(w.slot_mapping)
-    q, bt, sl, qsl = S(w.q), S(w.block_table), S(w.seq_lens), S(w.query_start_loc)
-    times = []
-    for rep in range(3):
-        t0 = time.perf_counter()
-        oracle.paged_kv_write(k, v, sm, kp, vp)
-        oracle.paged_attention(q, w.q_dtype, kp, vp, w.kv_dtype, bt, sl, qsl, w.scale, threads=threads)
-        times.append(time.perf_counter() - t0)
-        if times[-1] > 10:
-            break
-    t = statistics.median(times)
-    cpu = "unknown"
+def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": round(decode_bytes(w) / t / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle", "ms_per_step": round(t * 1e3, 1), "cpu": cpu,
+    return "unknown"
+
+
+def _timed(fn, limit_s=10.0):
+    """Median of 3 wall-clock runs of fn(), or 1 run when it takes longer
+    than limit_s; returns (seconds, runs)."""
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+        if times[-1] > limit_s:
+            break
+    return statistics.median(times), len(times)
+
+
+def cpu_oracle_leg(w, sel_tokens=None):
+    """The oracle as it stands (fp64, OpenMP over (sequence, KV head)) on a
+    workload already resident in host copies: the write of all new tokens and
+    the attention of the selected query rows (all when None), timed
+    separately.  Returns (write_s, attention_s, threads, runs)."""
+    import oracle
+    from paged_kv_cache_243_amd import workloads as W
+    S = W.to_numpy_storage
+    threads = len(os.sched_getaffinity(0))
+    kp0, vp0 = S(w.key_pool), S(w.value_pool)
+    k, v, sm = S(w.k_new), S(w.v_new), S(w.slot_mapping)
+    q, bt, sl, qsl = S(w.q), S(w.block_table), S(w.seq_lens), S(w.query_start_loc)
+    ks = None if w.k_scale is None else S(w.k_scale)
+    vs = None if w.v_scale is None else S(w.v_scale)
+    kp, vp = kp0.copy(), vp0.copy()
+    t_write, runs_w = _timed(lambda: oracle.paged_kv_write(k, v, sm, kp, vp))
+    t_attn, runs_a = _timed(lambda: oracle.paged_attention(q, w.q_dtype, kp, vp, w.kv_dtype, bt, sl, qsl, w.scale,
+                                                           ks, vs, sel_tokens=sel_tokens, threads=threads))
+    return t_write, t_attn, threads, min(runs_w, runs_a)
+
+
+def cpu_baseline_decode(w):
+    """Headline CPU baseline: the whole decode step of the timed workload (the
+    write of its 64 tokens and the attention of all 64 rows)."""
+    tw, ta, threads, runs = cpu_oracle_leg(w)
+    return {"value": round(decode_bytes(w) / (tw + ta) / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "ms_per_step": round((tw + ta) * 1e3, 1), "write_ms": round(tw * 1e3, 2),
+            "attention_ms": round(ta * 1e3, 1), "cpu": _cpu_model(),
             "sample": f"the full decode step of the timed workload ({w.cfg.batch} sequences: write of "
-                      f"{w.k_new.shape[0]} tokens + attention of every row), fp64, median of {len(times)} runs"}
+                      f"{w.k_new.shape[0]} tokens, then attention of every row), fp64, write and attention "
+                      f"timed separately, median of {runs} runs"}
+
+
+def cpu_baseline_prefill(w, every: int = 8):
+    """Chunked prefill: the write of all 4096 new tokens, then attention of
+    every `every`-th query row (all heads), GFLOP/s over the sampled rows'
+    causally visible pairs."""
+    import numpy as np
+    sel = np.arange(0, w.q.shape[0], every, dtype=np.int64)
+    tw, ta, threads, runs = cpu_oracle_leg(w, sel)
+    lens = w.seq_lens.cpu().numpy().astype(np.int64)
+    qsl = w.query_start_loc.cpu().numpy().astype(np.int64)
+    seq = np.searchsorted(qsl, sel, side="right") - 1
+    pos = lens[seq] - (qsl[seq + 1] - qsl[seq]) + (sel - qsl[seq])
+    flops = int(4 * w.cfg.head_dim * w.cfg.hq * int((pos + 1).sum()))
+    return {"value": round(flops / ta / 1e9, 3), "unit": "GFLOP/s", "cores": threads, "kind": "oracle",
+            "attention_ms": round(ta * 1e3, 1), "write_ms": round(tw * 1e3, 2),
+            "write_GBps": round(write_bytes(w) / tw / 1e9, 3), "flop_sampled": flops,
+            "sample": f"the write of all {w.k_new.shape[0]} new tokens, then attention of every {every}th query "
+                      f"row ({len(sel)} of {w.q.shape[0]} rows, all heads), fp64, median of {runs} runs"}
+
+
+def cpu_baseline_long_decode(w, every: int = 2):
+    """Long-context fp8 decode: the write of the 16 new tokens, then attention
+    of every `every`-th sequence's row; GB/s over those sequences' K/V bytes."""
+    import numpy as np
+    sel = np.arange(0, w.q.shape[0], every, dtype=np.int64)
+    tw, ta, threads, runs = cpu_oracle_leg(w, sel)
+    lens = w.seq_lens.cpu().numpy().astype(np.int64)
+    kv_bytes = int(lens[sel].sum()) * w.cfg.hkv * w.cfg.head_dim * 2
+    return {"value": round(kv_bytes / ta / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "attention_ms": round(ta * 1e3, 1), "write_ms": round(tw * 1e3, 2), "kv_bytes_sampled": kv_bytes,
+            "sample": f"the write of all {w.k_new.shape[0]} new tokens, then attention of one sequence in {every} "
+                      f"({len(sel)} of {w.q.shape[0]}, {int(lens[sel].sum())} positions), fp64 on fp8 codes "
+                      f"dequantised exactly, median of {runs} runs"}
+
+
+def stream_ceiling(w, torch, flush, steps: int) -> dict:
+    """Practical HBM ceiling: a plain read-only kernel (bench_ceiling.hip)
+    streaming exactly the K and V pages the decode workload reads, in the
+    same order and access shape, with no compute; HIP events around each
+    call, the cache flushed before each."""
+    import ctypes
+    import numpy as np
+    from paged_kv_cache_243_amd import build as Bd
+    if not os.path.exists(Bd.CEILING_OUT):
+        Bd.build_ceiling()
+    lib = ctypes.CDLL(Bd.CEILING_OUT)
+    lib.stream_read_pages.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                              ctypes.c_void_p, ctypes.c_void_p]
+    lib.stream_read_pages.restype = ctypes.c_int
+    cfg = w.cfg
+    bt = w.block_table.cpu().numpy()
+    lens = w.seq_lens.cpu().numpy().astype(np.int64)
+    pages = np.concatenate([bt[b, :-(-int(lens[b]) // cfg.page_size)] for b in range(len(lens))])
+    pages_t = torch.as_tensor(pages, dtype=torch.int64, device=w.q.device)
+    page_bytes = cfg.page_size * cfg.hkv * cfg.head_dim * w.key_pool.element_size()
+    moved = int(len(pages)) * page_bytes * 2
+    out = {"kernel": "stream_read_kernel (bench_ceiling.hip)", "bytes": moved,
+           "pages": int(len(pages)), "page_bytes": page_bytes}
+    stream = torch.cuda.current_stream()
+    for wgs in (256, 1024):
+        sink = torch.empty(wgs * 8, dtype=torch.int32, device=w.q.device)
+        call = lambda: lib.stream_read_pages(w.key_pool.data_ptr(), w.value_pool.data_ptr(), pages_t.data_ptr(),
+                                             len(pages), page_bytes, wgs, sink.data_ptr(),
+                                             ctypes.c_void_p(stream.cuda_stream))
+        assert call() == 0
+        ms = []
+        for _ in range(steps):
+            if flush is not None:
+                flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            call()
+            b.record()
+            b.synchronize()
+            ms.append(a.elapsed_time(b))
+        med = statistics.median(ms)
+        out[f"workgroups_{wgs}"] = {"ms_median": round(med, 5), "GBps": round(moved / (med * 1e-3) / 1e9, 1),
+                                    "frac_of_hbm_peak": round(moved / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    return out
 
 
 def csr_unpack_timing(pkv, w, torch, steps: int) -> dict:
@@ -400,6 +535,7 @@ def main(argv=None) -> int:
     w2 = W.generate(2, dev)
     r2 = Runner(pkv, w2, torch)
     t2, k2 = time_workload(r2, torch, args.steps, args.warmup, flush, "decode bf16")
+    g2 = time_graph_steps(r2, torch, args.steps, args.warmup, flush, "decode bf16")
     bytes2 = decode_bytes(w2)
     kbytes2 = decode_kernel_bytes(w2)
     step_ms = statistics.median(t2.step)
@@ -451,11 +587,20 @@ def main(argv=None) -> int:
             "ms_warm_median": round(statistics.median(warm.attn), 5),
         },
         "write_ms_median": round(statistics.median(t2.write), 5),
+        "graph_step": {
+            "form": "the same write + attention step captured once as a HIP graph and replayed",
+            "ms_median": round(statistics.median(g2), 5),
+            "GBps": round(bytes2 / (statistics.median(g2) * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(bytes2 / (statistics.median(g2) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
         "timed_loop_wall_s": round(t2.wall, 4),
     }
     if not args.no_extra:
         result["csr_unpack"] = csr_unpack_timing(pkv, w2, torch, args.steps)
+        log("streaming-read ceiling over the decode workload's pages")
+        result["stream_ceiling"] = stream_ceiling(w2, torch, flush, args.steps)
     del r2
+    cpu = {}
 
     if not args.no_extra:
         extra = {}
@@ -499,7 +644,11 @@ def main(argv=None) -> int:
             "write_GBps": round(write_bytes(w3) / (statistics.median(t3.write) * 1e-3) / 1e9, 1),
             "step_ms_median": round(statistics.median(t3.step), 5),
         }
-        del r3, w3
+        del r3
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on the chunked-prefill workload (sampled rows)")
+            cpu["prefill"] = cpu_baseline_prefill(w3)
+        del w3
         torch.cuda.empty_cache()
         # shared-prefix decode
         log("generating shared-prefix decode workload (config 4)")
@@ -531,6 +680,7 @@ def main(argv=None) -> int:
         w5 = W.generate(5, dev)
         r5 = Runner(pkv, w5, torch)
         t5, kt5 = time_workload(r5, torch, args.steps, args.warmup, flush, "fp8 long decode")
+        g5 = time_graph_steps(r5, torch, args.steps, args.warmup, flush, "fp8 long decode")
         a5 = statistics.median(t5.attn)
         k5 = statistics.fmean(kt5.kernel)
         b5 = decode_bytes(w5)
@@ -550,8 +700,16 @@ def main(argv=None) -> int:
             "call_ms_median": round(a5, 5),
             "call_GBps": round(b5 / (a5 * 1e-3) / 1e9, 1),
             "step_ms_median": round(statistics.median(t5.step), 5),
+            "step_GBps": round(b5 / (statistics.median(t5.step) * 1e-3) / 1e9, 1),
+            "graph_step_ms_median": round(statistics.median(g5), 5),
+            "graph_step_GBps": round(b5 / (statistics.median(g5) * 1e-3) / 1e9, 1),
+            "graph_step_frac_of_hbm_peak": round(b5 / (statistics.median(g5) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         }
-        del r5, w5
+        del r5
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on the long-context fp8 decode workload (sampled sequences)")
+            cpu["long_fp8_decode"] = cpu_baseline_long_decode(w5)
+        del w5
         torch.cuda.empty_cache()
         # the two decode workloads at their 8-way tensor-parallel shard: one KV
         # head (and its query heads) per GPU, all sequences and positions
@@ -586,7 +744,7 @@ def main(argv=None) -> int:
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the decode workload")
-        result["cpu_baseline"] = cpu_baseline(w2)
+        result["cpu_baseline"] = {**cpu_baseline_decode(w2), **cpu}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -49,11 +49,29 @@ def _compile(src: str) -> str:
     return obj
 
 
+# The benchmark's streaming-read ceiling kernel: its own small library beside
+# bench.py, not part of libpagedkv.so.
+CEILING_SRC = os.path.join(ROOT, "bench_ceiling.hip")
+CEILING_OUT = os.path.join(ROOT, "libbenchceiling.so")
+
+
+def build_ceiling() -> str:
+    tmp = CEILING_OUT + ".tmp"
+    cmd = [HIPCC, *COMMON, "-shared", "-x", "hip", CEILING_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {CEILING_SRC}:\n{r.stderr}")
+    os.replace(tmp, CEILING_OUT)
+    return CEILING_OUT
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        ceiling = ex.submit(build_ceiling)
         objs = list(ex.map(_compile, srcs))
+        ceiling.result()
     tmp = OUT + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
