@@ -149,11 +149,14 @@ class Fp8WriteRunner:
 
 
 class Runner:
-    """Write + attention of one workload with preallocated buffers."""
+    """Write + attention of one workload with preallocated buffers: two calls
+    (paged_kv_write, then paged_attention), or with fused=True the one call
+    paged_kv_write_attention (write() then does nothing)."""
 
-    def __init__(self, pkv, w, torch, shared_prefix_pages=0):
+    def __init__(self, pkv, w, torch, shared_prefix_pages=0, fused=False):
         self.pkv, self.w, self.torch = pkv, w, torch
         self.shared = shared_prefix_pages
+        self.fused = fused
         self.kp, self.vp = w.key_pool, w.value_pool  # written in place each step (same rows)
         self.out = torch.empty_like(w.q)
         need = pkv.paged_attention_workspace_size(w.q, w.key_pool, w.block_table,
@@ -163,11 +166,21 @@ class Runner:
         self.ws = torch.empty(max(need, 1), dtype=torch.uint8, device=w.q.device)
 
     def write(self):
+        if self.fused:
+            return
         w = self.w
         self.pkv.paged_kv_write(w.k_new, w.v_new, w.slot_mapping, self.kp, self.vp)
 
     def attend(self, kernel_events=None):
         w = self.w
+        if self.fused:
+            self.pkv.paged_kv_write_attention(w.k_new, w.v_new, w.slot_mapping, self.kp, self.vp, w.q,
+                                              w.block_table, w.seq_lens, w.query_start_loc, w.scale, self.out,
+                                              k_scale=w.k_scale, v_scale=w.v_scale,
+                                              max_query_len=w.max_query_len, split_tokens=w.split_tokens,
+                                              workspace=self.ws, timing_events=kernel_events,
+                                              shared_prefix_pages=self.shared)
+            return
         self.pkv.paged_attention(w.q, self.kp, self.vp, w.block_table, w.seq_lens, w.query_start_loc,
                                  w.scale, self.out, k_scale=w.k_scale, v_scale=w.v_scale,
                                  max_query_len=w.max_query_len, split_tokens=w.split_tokens,
@@ -183,12 +196,14 @@ class Times:
         self.write, self.attn, self.kernel, self.step, self.wall = write, attn, kernel, step, wall
 
 
-def time_steps(runner, torch, steps, warmup, flush, progress="", kernel_events=True):
+def time_steps(runner, torch, steps, warmup, flush, progress="", kernel_events=True, mid_event=False):
     """Time `steps` steps after `warmup` untimed ones; the cache flush, when
     given, runs before each step outside its timed region.  With
     kernel_events the library also records a HIP event pair around the main
-    attention kernel (the two extra event packets lengthen the call by a few
-    microseconds, so whole-step figures come from a pass without them)."""
+    attention kernel, and with mid_event one more event separates the write
+    from the attention call (each event packet lengthens the step by a few
+    microseconds, so whole-step figures come from a pass with events at the
+    step's ends only)."""
     for _ in range(warmup):
         runner.write()
         runner.attend()
@@ -202,12 +217,14 @@ def time_steps(runner, torch, steps, warmup, flush, progress="", kernel_events=T
         e = ev[i]
         e[0].record()
         runner.write()
-        e[1].record()
+        if mid_event:
+            e[1].record()
         runner.attend(kernel_events=(e[3], e[4]) if kernel_events else None)
         e[2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t = Times(write=[e[0].elapsed_time(e[1]) for e in ev], attn=[e[1].elapsed_time(e[2]) for e in ev],
+    t = Times(write=[e[0].elapsed_time(e[1]) for e in ev] if mid_event else None,
+              attn=[e[1 if mid_event else 0].elapsed_time(e[2]) for e in ev],
               kernel=[e[3].elapsed_time(e[4]) for e in ev] if kernel_events else None,
               step=[e[0].elapsed_time(e[2]) for e in ev], wall=wall)
     if progress:
@@ -248,11 +265,16 @@ def time_graph_steps(runner, torch, steps, warmup, flush, progress=""):
 
 
 def time_workload(runner, torch, steps, warmup, flush, progress):
-    """Two timed passes: whole steps without in-call events, then the main
-    kernel alone with them."""
+    """Timed passes: whole steps with events at their ends only; for the
+    two-call form, the write and the attention call apart (an event between
+    them); the main kernel alone (events around it)."""
     plain = time_steps(runner, torch, steps, warmup, flush, progress + " (steps)", kernel_events=False)
+    split = None
+    if not getattr(runner, "fused", False):
+        split = time_steps(runner, torch, steps, 1, flush, progress + " (write | attention)", kernel_events=False,
+                           mid_event=True)
     kern = time_steps(runner, torch, steps, 1, flush, progress + " (main kernel)", kernel_events=True)
-    return plain, kern
+    return plain, split, kern
 
 
 def traffic_from_profile(kernel: str):
@@ -506,7 +528,7 @@ def main(argv=None) -> int:
     if args.profile_workload == "fp8write":
         w = W.generate(3, dev)
         t = time_steps(Fp8WriteRunner(pkv, w, torch), torch, args.steps, args.warmup, flush, "fp8 write",
-                       kernel_events=False)
+                       kernel_events=False, mid_event=True)
         print(json.dumps({"workload": "quantising fp8 write of 4096 bf16 K/V rows (Hkv 8, D 128)",
                           "write_ms_median": statistics.median(t.write),
                           "write_ms_mean": statistics.fmean(t.write)}), flush=True)
@@ -522,7 +544,7 @@ def main(argv=None) -> int:
         del calib
         pages = w.cfg.shared_prefix_tokens // w.cfg.page_size if args.profile_workload == "shared" else 0
         t = time_steps(Runner(pkv, w, torch, shared_prefix_pages=pages), torch, args.steps, args.warmup, flush,
-                       args.profile_workload)
+                       args.profile_workload, mid_event=True)
         print(json.dumps({"workload": w.cfg.name, "write_ms_median": statistics.median(t.write),
                           "attention_ms_median": statistics.median(t.attn),
                           "main_kernel_ms_median": statistics.median(t.kernel),
@@ -530,19 +552,23 @@ def main(argv=None) -> int:
                           "step_ms_median": statistics.median(t.step)}), flush=True)
         return 0
 
-    # ---- headline: decode workload, write + attention per step
+    # ---- headline: decode workload, write + attention per step, as the one
+    # call paged_kv_write_attention (one kernel pass writes and attends, then
+    # the merge); the two separate calls are timed beside it
     log("generating decode workload (config 2)")
     w2 = W.generate(2, dev)
-    r2 = Runner(pkv, w2, torch)
-    t2, k2 = time_workload(r2, torch, args.steps, args.warmup, flush, "decode bf16")
-    g2 = time_graph_steps(r2, torch, args.steps, args.warmup, flush, "decode bf16")
+    r2 = Runner(pkv, w2, torch, fused=True)
+    r2s = Runner(pkv, w2, torch)
+    t2, _, k2 = time_workload(r2, torch, args.steps, args.warmup, flush, "decode bf16, one call")
+    t2s, c2s, k2s = time_workload(r2s, torch, args.steps, args.warmup, flush, "decode bf16, two calls")
+    g2 = time_graph_steps(r2, torch, args.steps, args.warmup, flush, "decode bf16, one call")
     bytes2 = decode_bytes(w2)
-    kbytes2 = decode_kernel_bytes(w2)
+    kbytes2 = decode_kernel_bytes(w2) + write_bytes(w2)  # the fused kernel also moves the new rows
     step_ms = statistics.median(t2.step)
-    attn_ms = statistics.median(t2.attn)
+    attn_ms = statistics.median(c2s.attn)
     kern_ms = statistics.fmean(k2.kernel)
     achieved = kbytes2 / (kern_ms * 1e-3) / 1e9
-    warm = time_steps(r2, torch, max(5, args.steps // 3), 2, None, kernel_events=False)
+    warm = time_steps(r2s, torch, max(5, args.steps // 3), 2, None, kernel_events=False, mid_event=True)
     result = {
         "metric": METRIC,
         "value": round(bytes2 / (step_ms * 1e-3) / 1e9, 2),
@@ -559,13 +585,14 @@ def main(argv=None) -> int:
         "config": {
             "workload": "paged decode, bf16 KV: write 1 new token per sequence, then split-K decode "
                         "attention over each sequence's pages",
+            "form": "paged_kv_write_attention (the write and the attention as one call)",
             "batch": w2.cfg.batch, "q_heads": w2.cfg.hq, "kv_heads": w2.cfg.hkv,
             "head_dim": w2.cfg.head_dim, "page_size": w2.cfg.page_size, "num_pages": w2.cfg.num_pages,
             "context_lengths": "U{512..4096}", "kv_dtype": "bf16", "parallelism": "none (1 GPU)",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_kernel<2,128> (split-K decode pass)",
+            "kernel": "decode_kernel<2,128> (split-K decode pass, writing the new rows)",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -577,18 +604,26 @@ def main(argv=None) -> int:
             "launch_ms_min": round(min(k2.kernel), 5),
             "launches_timed": len(k2.kernel),
         },
+        "two_calls": {
+            "form": "paged_kv_write, then paged_attention",
+            "step_ms_median": round(statistics.median(t2s.step), 5),
+            "step_GBps": round(bytes2 / (statistics.median(t2s.step) * 1e-3) / 1e9, 1),
+            "step_frac_of_hbm_peak": round(bytes2 / (statistics.median(t2s.step) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "write_ms_median": round(statistics.median(c2s.write), 5),
+            "decode_kernel_ms_mean": round(statistics.fmean(k2s.kernel), 5),
+            "decode_kernel_GBps": round(decode_kernel_bytes(w2) / (statistics.fmean(k2s.kernel) * 1e-3) / 1e9, 1),
+        },
         "decode_call": {
-            "kernels": "decode_kernel + merge_kernel",
+            "kernels": "decode_kernel + merge_kernel (paged_attention)",
             "algorithmic_bytes": bytes2,
             "ms_median": round(attn_ms, 5),
-            "ms_min": round(min(t2.attn), 5),
+            "ms_min": round(min(c2s.attn), 5),
             "GBps": round(bytes2 / (attn_ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(bytes2 / (attn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "ms_warm_median": round(statistics.median(warm.attn), 5),
         },
-        "write_ms_median": round(statistics.median(t2.write), 5),
         "graph_step": {
-            "form": "the same write + attention step captured once as a HIP graph and replayed",
+            "form": "the same one-call step captured once as a HIP graph and replayed",
             "ms_median": round(statistics.median(g2), 5),
             "GBps": round(bytes2 / (statistics.median(g2) * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(bytes2 / (statistics.median(g2) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -599,7 +634,7 @@ def main(argv=None) -> int:
         result["csr_unpack"] = csr_unpack_timing(pkv, w2, torch, args.steps)
         log("streaming-read ceiling over the decode workload's pages")
         result["stream_ceiling"] = stream_ceiling(w2, torch, flush, args.steps)
-    del r2
+    del r2, r2s
     cpu = {}
 
     if not args.no_extra:
@@ -608,13 +643,13 @@ def main(argv=None) -> int:
         log("generating prefill workload (config 3)")
         w3 = W.generate(3, dev)
         r3 = Runner(pkv, w3, torch)
-        t3, kt3 = time_workload(r3, torch, max(5, args.steps // 2), args.warmup, flush, "prefill bf16")
+        t3, c3, kt3 = time_workload(r3, torch, max(5, args.steps // 2), args.warmup, flush, "prefill bf16")
         fl = prefill_flops(w3)
-        a3 = statistics.median(t3.attn)
+        a3 = statistics.median(c3.attn)
         k3 = statistics.fmean(kt3.kernel)
         # quantising fp8 write of the same 4096 new rows
         fw = time_steps(Fp8WriteRunner(pkv, w3, torch), torch, args.steps, args.warmup, flush,
-                        "fp8 quantising write", kernel_events=False)
+                        "fp8 quantising write", kernel_events=False, mid_event=True)
         fw_ms = statistics.median(fw.write)
         fw_bytes = fp8_write_bytes(w3.k_new.shape[0], w3.cfg.hkv, w3.cfg.head_dim)
         extra["fp8_quantising_write"] = {
@@ -640,8 +675,8 @@ def main(argv=None) -> int:
             "launch_ms_mean": round(k3, 5),
             "call_ms_median": round(a3, 5),
             "call_TFLOPs": round(fl / (a3 * 1e-3) / 1e12, 2),
-            "write_ms_median": round(statistics.median(t3.write), 5),
-            "write_GBps": round(write_bytes(w3) / (statistics.median(t3.write) * 1e-3) / 1e9, 1),
+            "write_ms_median": round(statistics.median(c3.write), 5),
+            "write_GBps": round(write_bytes(w3) / (statistics.median(c3.write) * 1e-3) / 1e9, 1),
             "step_ms_median": round(statistics.median(t3.step), 5),
         }
         del r3
@@ -655,10 +690,11 @@ def main(argv=None) -> int:
         w4 = W.generate(4, dev)
         pages4 = w4.cfg.shared_prefix_tokens // w4.cfg.page_size
         r4 = Runner(pkv, w4, torch, shared_prefix_pages=pages4)
-        t4 = time_steps(r4, torch, args.steps, args.warmup, flush, "shared-prefix decode", kernel_events=False)
+        t4 = time_steps(r4, torch, args.steps, args.warmup, flush, "shared-prefix decode", kernel_events=False,
+                        mid_event=True)
         r4p = Runner(pkv, w4, torch)
         t4p = time_steps(r4p, torch, args.steps, args.warmup, flush, "shared-prefix decode, plain call",
-                         kernel_events=False)
+                         kernel_events=False, mid_event=True)
         a4 = statistics.median(t4.attn)
         a4p = statistics.median(t4p.attn)
         extra["shared_prefix_decode"] = {
@@ -678,29 +714,28 @@ def main(argv=None) -> int:
         # long-context fp8 decode
         log("generating long-context fp8 decode workload (config 5)")
         w5 = W.generate(5, dev)
-        r5 = Runner(pkv, w5, torch)
-        t5, kt5 = time_workload(r5, torch, args.steps, args.warmup, flush, "fp8 long decode")
+        r5 = Runner(pkv, w5, torch, fused=True)
+        t5, _, kt5 = time_workload(r5, torch, args.steps, args.warmup, flush, "fp8 long decode")
         g5 = time_graph_steps(r5, torch, args.steps, args.warmup, flush, "fp8 long decode")
-        a5 = statistics.median(t5.attn)
         k5 = statistics.fmean(kt5.kernel)
         b5 = decode_bytes(w5)
-        kb5 = decode_kernel_bytes(w5)
+        kb5 = decode_kernel_bytes(w5) + write_bytes(w5)  # the fused kernel also moves the new rows
         extra["fp8_long_decode"] = {
             "workload": "16 sequences, U{32768..131072} positions, fp8 E4M3FN KV with per-head scales, "
                         "Hq 64, Hkv 8, split_tokens 2048: the (sequence, 32-position unit) list cut into "
                         "equal stream-K ranges (their count set by split_tokens), merged per sequence by "
                         "log-sum-exp",
-            "kernel": "decode_kernel<1,128>",
+            "form": "paged_kv_write_attention (the write and the attention as one call)",
+            "kernel": "decode_kernel<1,128> (split-K decode pass, writing the new rows)",
             "bound": "hbm", "unit": "GB/s",
             "achieved": round(kb5 / (k5 * 1e-3) / 1e9, 1),
             "peak": HBM_PEAK_GBS,
             "frac": round(kb5 / (k5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_launch": kb5,
             "launch_ms_mean": round(k5, 5),
-            "call_ms_median": round(a5, 5),
-            "call_GBps": round(b5 / (a5 * 1e-3) / 1e9, 1),
             "step_ms_median": round(statistics.median(t5.step), 5),
             "step_GBps": round(b5 / (statistics.median(t5.step) * 1e-3) / 1e9, 1),
+            "step_frac_of_hbm_peak": round(b5 / (statistics.median(t5.step) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "graph_step_ms_median": round(statistics.median(g5), 5),
             "graph_step_GBps": round(b5 / (statistics.median(g5) * 1e-3) / 1e9, 1),
             "graph_step_frac_of_hbm_peak": round(b5 / (statistics.median(g5) * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -718,7 +753,7 @@ def main(argv=None) -> int:
             log(f"generating the 8-way shard of config {cid}")
             ws = W.generate(tp_shard(W, cid, 8), dev)
             rs = Runner(pkv, ws, torch)
-            ts, kts = time_workload(rs, torch, args.steps, args.warmup, flush, f"config {cid}, 8-way shard")
+            ts, cs, kts = time_workload(rs, torch, args.steps, args.warmup, flush, f"config {cid}, 8-way shard")
             ks = statistics.fmean(kts.kernel)
             kbs = decode_kernel_bytes(ws)
             shards[f"config{cid}"] = {
@@ -727,7 +762,7 @@ def main(argv=None) -> int:
                 "launch_ms_mean": round(ks, 5),
                 "achieved_GBps": round(kbs / (ks * 1e-3) / 1e9, 1),
                 "frac_of_hbm_peak": round(kbs / (ks * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                "call_ms_median": round(statistics.median(ts.attn), 5),
+                "call_ms_median": round(statistics.median(cs.attn), 5),
             }
             del rs, ws
             torch.cuda.empty_cache()

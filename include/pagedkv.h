@@ -215,6 +215,37 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
                     const pkv_attn_opts* opts, void* stream);
 
 /*
+ * paged_kv_write_attention -- paged_kv_write followed by paged_attention, as
+ * one call: the whole step of the pages' graph (mobius #395, "How it works":
+ * the ScatterND of the new rows, then Attention over the pages they landed
+ * in).  Arguments are those of the two calls (k, v, slot_mapping and the pools
+ * as for paged_kv_write; q .. opts as for paged_attention, with the same
+ * workspace size), and so are the results.
+ *
+ * A decode step (opts->max_query_len 1) whose T_new equals T runs as one
+ * kernel pass that writes the new rows and attends (when the rows fit the
+ * pass's registers: up to 16 KiB of K and V rows per workgroup, e.g. 2048
+ * sequences of 8 KV heads x 128 bf16 dims on 256 CUs).  Such a call states that
+ * the new rows are the query rows' own keys: row t of k and v is the key of
+ * query row t, slot_mapping[t] is the slot of that row's position
+ * (block_table[b][p / page_size] * page_size + p % page_size with p =
+ * seq_lens[b] - 1), and no sequence reads a written slot at another position
+ * (the pages' step builds slot_mapping exactly so: the new tokens are the last
+ * ones of their sequences).  The kernel then takes each sequence's last key
+ * from k and v directly and writes the pools alongside, so no read waits for
+ * the write.  A statement that does not hold gives unspecified attention
+ * output (the pools are still written as paged_kv_write writes them);
+ * paged_validate_metadata with PKV_CHECK_NEW_ROWS_ARE_QUERY_ROWS checks it.
+ * Any other call (prefill, fp32 pools, T_new != T) enqueues the write and then
+ * the attention, exactly as the two calls do.
+ */
+int paged_kv_write_attention(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+                             pkv_tensor* key_pool, pkv_tensor* value_pool, const pkv_tensor* q,
+                             const pkv_tensor* block_table, const pkv_tensor* seq_lens,
+                             const pkv_tensor* query_start_loc, float scale, pkv_tensor* out,
+                             const pkv_attn_opts* opts, void* stream);
+
+/*
  * paged_attention_noalloc -- paged_attention for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  Same arguments, computation and results as
@@ -299,15 +330,20 @@ int paged_block_table_from_csr(const pkv_tensor* kv_indptr, const pkv_tensor* kv
  * makes through pkv_attn_opts.shared_prefix_pages: N <= max_blocks, every
  * sequence with a query row holds more than N * page_size positions, and the
  * first N entries of all those sequences' rows are the same pages (0 = no
- * statement).  slot_mapping may be NULL (attention-only check).  Returns
+ * statement).  `checks` selects further statements to check (0 = none):
+ * PKV_CHECK_NEW_ROWS_ARE_QUERY_ROWS, the statement of a fused decode step
+ * (paged_kv_write_attention): one slot per query row, each the slot of its
+ * row's position, and no sequence reading a written slot at an older
+ * position.  slot_mapping may be NULL (attention-only check).  Returns
  * PKV_OK, PKV_ERR_INDEX on the first bad value (and, if `message` is
  * non-NULL, writes a NUL-terminated description of at most `message_len`
  * bytes), or another negative status for bad arguments.
  */
+#define PKV_CHECK_NEW_ROWS_ARE_QUERY_ROWS 1u
 int paged_validate_metadata(const pkv_tensor* slot_mapping, const pkv_tensor* block_table,
                             const pkv_tensor* seq_lens, const pkv_tensor* query_start_loc,
                             int64_t num_pages, int64_t page_size, int64_t num_query_rows,
-                            int64_t shared_prefix_pages, void* stream, char* message,
+                            int64_t shared_prefix_pages, uint32_t checks, void* stream, char* message,
                             size_t message_len);
 
 /*
@@ -319,8 +355,8 @@ int paged_validate_metadata(const pkv_tensor* slot_mapping, const pkv_tensor* bl
 int pkv_check_metadata_host(const int64_t* slots, int64_t n_slots, const int64_t* block_table,
                             int64_t B, int64_t max_blocks, const int64_t* seq_lens,
                             const int64_t* query_start_loc, int64_t num_pages, int64_t page_size,
-                            int64_t num_query_rows, int64_t shared_prefix_pages, char* message,
-                            size_t message_len);
+                            int64_t num_query_rows, int64_t shared_prefix_pages, uint32_t checks,
+                            char* message, size_t message_len);
 
 /* Human-readable name of a status code (static string). */
 const char* pkv_status_string(int status);

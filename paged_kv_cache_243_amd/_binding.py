@@ -26,8 +26,9 @@ STATUS = {
 }
 # every symbol include/pagedkv.h declares
 EXPORTS = ("paged_kv_write", "paged_kv_write_fp8", "paged_block_table_from_csr", "paged_attention",
-           "paged_attention_noalloc", "paged_attention_workspace_size", "paged_validate_metadata",
-           "pkv_check_metadata_host", "pkv_status_string", "pkv_abi_version")
+           "paged_kv_write_attention", "paged_attention_noalloc", "paged_attention_workspace_size",
+           "paged_validate_metadata", "pkv_check_metadata_host", "pkv_status_string", "pkv_abi_version")
+CHECK_NEW_ROWS_ARE_QUERY_ROWS = 1
 # fixed scratch of paged_attention_noalloc (PKV_NOALLOC_SCRATCH_BYTES)
 NOALLOC_SCRATCH_BYTES = 128 << 20
 
@@ -73,14 +74,18 @@ def load() -> ctypes.CDLL:
         lib.paged_kv_write_fp8.restype = i32
         lib.paged_attention.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, ctypes.POINTER(PkvAttnOpts), vp]
         lib.paged_attention.restype = i32
+        lib.paged_kv_write_attention.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_float, P,
+                                                 ctypes.POINTER(PkvAttnOpts), vp]
+        lib.paged_kv_write_attention.restype = i32
         lib.paged_attention_noalloc.argtypes = [P, P, P, P, P, P, ctypes.c_float, P, ctypes.POINTER(PkvAttnOpts), vp]
         lib.paged_attention_noalloc.restype = i32
         lib.paged_attention_workspace_size.argtypes = [P, P, P, ctypes.POINTER(PkvAttnOpts)]
         lib.paged_attention_workspace_size.restype = sz
-        lib.paged_validate_metadata.argtypes = [P, P, P, P, i64, i64, i64, i64, vp, ctypes.c_char_p, sz]
+        lib.paged_validate_metadata.argtypes = [P, P, P, P, i64, i64, i64, i64, ctypes.c_uint32, vp,
+                                                ctypes.c_char_p, sz]
         lib.paged_validate_metadata.restype = i32
         lib.pkv_check_metadata_host.argtypes = [vp, i64, vp, i64, i64, vp, vp, i64, i64, i64, i64,
-                                                ctypes.c_char_p, sz]
+                                                ctypes.c_uint32, ctypes.c_char_p, sz]
         lib.pkv_check_metadata_host.restype = i32
         lib.pkv_status_string.argtypes = [i32]
         lib.pkv_status_string.restype = ctypes.c_char_p
@@ -263,21 +268,45 @@ def paged_attention_noalloc(q, key_pool, value_pool, block_table, seq_lens, quer
     return out
 
 
+def paged_kv_write_attention(k, v, slot_mapping, key_pool, value_pool, q, block_table, seq_lens, query_start_loc,
+                             scale, out, *, k_scale=None, v_scale=None, max_query_len=None, split_tokens=0,
+                             workspace=None, timing_events=None, shared_prefix_pages=0) -> torch.Tensor:
+    """paged_kv_write then paged_attention as one call (one kernel pass for a
+    decode step whose new rows are the query rows' keys; see the header)."""
+    lib = load()
+    dev = _on_one_gpu("paged_kv_write_attention", k, v, slot_mapping, key_pool, value_pool, q, block_table,
+                      seq_lens, query_start_loc, out, k_scale, v_scale, workspace)
+    _check_scales("paged_kv_write_attention", k_scale, v_scale, key_pool)
+    if workspace is not None and (workspace.dtype != torch.uint8 or not workspace.is_contiguous()):
+        raise PagedKVError(-6, "paged_kv_write_attention: the workspace must be a contiguous uint8 tensor")
+    if workspace is None:
+        need = paged_attention_workspace_size(q, key_pool, block_table, max_query_len=max_query_len,
+                                              split_tokens=split_tokens, shared_prefix_pages=shared_prefix_pages)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    opts = _opts(k_scale, v_scale, workspace, max_query_len, split_tokens, timing_events, shared_prefix_pages)
+    st = lib.paged_kv_write_attention(describe(k), describe(v), describe(slot_mapping), describe(key_pool),
+                                      describe(value_pool), describe(q), describe(block_table), describe(seq_lens),
+                                      describe(query_start_loc), ctypes.c_float(scale), describe(out),
+                                      ctypes.byref(opts), _stream(dev))
+    _check(st, "paged_kv_write_attention")
+    return out
+
+
 def paged_validate_metadata(slot_mapping, block_table, seq_lens, query_start_loc, num_pages,
-                            page_size, num_query_rows, shared_prefix_pages=0) -> tuple[int, str]:
+                            page_size, num_query_rows, shared_prefix_pages=0, checks=0) -> tuple[int, str]:
     """Synchronous device-metadata check (see the header); returns (status, message)."""
     lib = load()
     dev = _on_one_gpu("paged_validate_metadata", slot_mapping, block_table, seq_lens, query_start_loc)
     buf = ctypes.create_string_buffer(256)
     st = lib.paged_validate_metadata(describe(slot_mapping) if slot_mapping is not None else None,
                                      describe(block_table), describe(seq_lens), describe(query_start_loc),
-                                     num_pages, page_size, num_query_rows, int(shared_prefix_pages),
+                                     num_pages, page_size, num_query_rows, int(shared_prefix_pages), int(checks),
                                      _stream(dev), buf, 256)
     return st, buf.value.decode()
 
 
 def check_metadata_host(slot_mapping, block_table, seq_lens, query_start_loc, num_pages, page_size,
-                        num_query_rows, shared_prefix_pages=0) -> tuple[int, str]:
+                        num_query_rows, shared_prefix_pages=0, checks=0) -> tuple[int, str]:
     """Host-memory metadata check (numpy int64 arrays; slot_mapping may be None)."""
     lib = load()
     buf = ctypes.create_string_buffer(256)
@@ -287,5 +316,6 @@ def check_metadata_host(slot_mapping, block_table, seq_lens, query_start_loc, nu
     st = lib.pkv_check_metadata_host(sm.ctypes.data if sm is not None else None,
                                      sm.shape[0] if sm is not None else 0,
                                      bt.ctypes.data, bt.shape[0], bt.shape[1], sl.ctypes.data, qs.ctypes.data,
-                                     num_pages, page_size, num_query_rows, int(shared_prefix_pages), buf, 256)
+                                     num_pages, page_size, num_query_rows, int(shared_prefix_pages), int(checks),
+                                     buf, 256)
     return st, buf.value.decode()

@@ -64,6 +64,8 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kStreamAux = 2;
 constexpr int kMaxWaves = 8;   // waves per workgroup
 
+constexpr int kCopyRegs = 2;   // fused write: 16-byte chunks per thread and pool
+
 #ifndef PKV_DECODE_MAX_GROUPS
 #define PKV_DECODE_MAX_GROUPS 8
 #endif
@@ -239,23 +241,50 @@ __device__ __forceinline__ bf16x8 k_operand(const __bf16* __restrict__ tile, int
   return *(const bf16x8*)(tile + row * D + 8 * ((4 * kk + grp) ^ G::swz(row)));
 }
 
-// One unit of the online softmax for one KV head: scores for 32 keys, running
-// max/sum update, P.V accumulation.  pos0 = position of the unit's first key;
-// keys at positions >= len are masked.
+// Fused write: row `row` of the unit's K and V tiles replaced by the key the
+// step writes at the sequence's last position, held in registers (lane c <
+// D * ESZ / 16 holds bytes [16 c, 16 c + 16) of the K and V rows), laid out
+// as stage_k / stage_v lay out a pool row (same wave, so these LDS writes
+// land after the staged ones).
+template <int ESZ, int D>
+__device__ __forceinline__ void put_new_row(__bf16* __restrict__ ktile, __bf16* __restrict__ vtile, int row,
+                                            const u32x4& nk, const u32x4& nv, int lane) {
+  using G = KGeom<ESZ, D>;
+  constexpr int NCH = D * ESZ / 16;
+  if (lane >= NCH) return;
+  __bf16* kr = ktile + row * D;
+  __bf16* vr = vtile + row * D;
+  if constexpr (ESZ == 2) {
+    *(u32x4*)(kr + 8 * (lane ^ G::swz(row))) = nk;
+    *(u32x4*)(vr + 8 * (lane ^ G::swz_v(row))) = nv;
+  } else {
+    const u32x2 k0 = fp8x4_to_bf16x4(nk.x), k1 = fp8x4_to_bf16x4(nk.y);
+    const u32x2 k2 = fp8x4_to_bf16x4(nk.z), k3 = fp8x4_to_bf16x4(nk.w);
+    const u32x2 v0 = fp8x4_to_bf16x4(nv.x), v1 = fp8x4_to_bf16x4(nv.y);
+    const u32x2 v2 = fp8x4_to_bf16x4(nv.z), v3 = fp8x4_to_bf16x4(nv.w);
+    *(u32x4*)(kr + 8 * ((2 * lane) ^ G::swz(row))) = u32x4{k0.x, k0.y, k1.x, k1.y};
+    *(u32x4*)(kr + 8 * ((2 * lane + 1) ^ G::swz(row))) = u32x4{k2.x, k2.y, k3.x, k3.y};
+    *(u32x4*)(vr + 8 * ((2 * lane) ^ G::swz_v(row))) = u32x4{v0.x, v0.y, v1.x, v1.y};
+    *(u32x4*)(vr + 8 * ((2 * lane + 1) ^ G::swz_v(row))) = u32x4{v2.x, v2.y, v3.x, v3.y};
+  }
+}
+
 // One unit of the online softmax for one KV head: stage the unit's K and V
 // into the wave's LDS tiles, call next() (which issues the following unit's
 // loads into the now free registers), then scores for 32 keys, the running
 // max/sum update and the P.V accumulation.  pos0 = position of the unit's first
-// key; keys at positions >= len are masked.
+// key; keys at positions >= len are masked.  new_row >= 0 (fused write):
+// that row of the tiles is the step's new key, taken from nk / nv.
 template <int ESZ, int D, class Next>
 __device__ __forceinline__ void consume_unit(UnitRegs<ESZ, D>& u, __bf16* __restrict__ ktile, __bf16* __restrict__ vtile,
                                              const bf16x8 (&qb)[D / 32], f32x4 (&acc)[D / 16], float& m_run,
                                              float& l_run, float logit_scale, int64_t pos0, int64_t len, int lane,
-                                             Next next) {
+                                             int new_row, const u32x4& nk, const u32x4& nv, Next next) {
   constexpr int NKK = D / 32, NJ = D / 16;
   const int col = lane & 15, grp = lane >> 4;
   stage_k<ESZ, D>(u, ktile, lane);
   stage_v<ESZ, D>(u, vtile, lane, pos0, len);
+  if (new_row >= 0) put_new_row<ESZ, D>(ktile, vtile, new_row, nk, nv, lane);
   next();
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -358,6 +387,41 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   const int col = lane & 15, grp = lane >> 4;
   const int B = (int)p.B;
 
+  // ---- fused write: workgroup w writes new rows w, w + gridDim.x, ... to
+  // their pool rows (the host checks that they fit in kCopyRegs chunks per
+  // thread).  The rows are loaded here (their addresses do not depend on the
+  // slots) and stored when the workgroup's stream is done, so neither waits.
+  // No position this kernel reads is a written row (each is a sequence's
+  // last position, whose key the kernel takes from the new rows), so the
+  // stores need no ordering against the loads.
+  u32x4 cpk[kCopyRegs], cpv[kCopyRegs];
+  int64_t cpd[kCopyRegs];  // byte offset of the chunk in the pools, or -1
+  if (p.n_new > 0) {
+    const int64_t row_bytes = (int64_t)p.Hkv * D * ESZ;
+    const int rc = (int)(row_bytes / 16);
+#pragma unroll
+    for (int i = 0; i < kCopyRegs; ++i) {
+      const int f = tid + i * nthreads, k = f / rc, c = f - k * rc;
+      const int64_t t = blockIdx.x + (int64_t)k * gridDim.x;
+      cpd[i] = -1;
+      if (t < p.n_new) {
+        const int64_t slot = p.new_slots[t];
+        cpk[i] = ((const u32x4*)((const char*)p.new_k + t * row_bytes))[c];
+        cpv[i] = ((const u32x4*)((const char*)p.new_v + t * row_bytes))[c];
+        cpd[i] = slot >= 0 ? slot * row_bytes + 16 * c : -1;
+      }
+    }
+  }
+  auto finish_copy = [&]() {
+    if (p.n_new == 0) return;
+#pragma unroll
+    for (int i = 0; i < kCopyRegs; ++i)
+      if (cpd[i] >= 0) {
+        *(u32x4*)((char*)const_cast<void*>(p.key_pool) + cpd[i]) = cpk[i];
+        *(u32x4*)((char*)const_cast<void*>(p.value_pool) + cpd[i]) = cpv[i];
+      }
+  };
+
   // ---- units before each sequence: a scan of each thread's run of
   // sequences, inclusive within the wave by lane shuffles, then over the wave
   // totals (one barrier).  The thread whose run holds the workgroup's first
@@ -414,11 +478,17 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     for (int b = tid; b <= B; b += nthreads) p.ws_cum[b] = s_cum[b];
   // (the wave totals come through LDS: keep the range in scalar registers)
   U = (int32_t)__builtin_amdgcn_readfirstlane(U);
-  if (U == 0) return;
+  if (U == 0) {
+    finish_copy();
+    return;
+  }
   const Partition part(U, W);
   const int32_t u0 = (int32_t)__builtin_amdgcn_readfirstlane(part.start(wg));
   const int32_t u1 = (int32_t)__builtin_amdgcn_readfirstlane(part.start(wg + 1));
-  if (u0 >= u1) return;
+  if (u0 >= u1) {
+    finish_copy();
+    return;
+  }
 
   const int hpw = decode_heads_per_wave(p.Hkv);
   const uint32_t row_stride = (uint32_t)p.Hkv * D * ESZ;
@@ -505,6 +575,21 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
     }
   };
 
+  // fused write: the new key of the run's sequence (its query row's K and V
+  // rows of the run's head), for the run's last unit
+  u32x4 nk = {0u, 0u, 0u, 0u}, nv = {0u, 0u, 0u, 0u};
+  auto load_new = [&](int64_t q_row, int h) {
+    constexpr int NCH = D * ESZ / 16;
+    if (p.n_new > 0 && lane < NCH) {
+      const int64_t off = (q_row * p.Hkv + h) * (int64_t)(D * ESZ) + 16 * lane;
+      nk = *(const u32x4*)((const char*)p.new_k + off);
+      nv = *(const u32x4*)((const char*)p.new_v + off);
+    }
+  };
+  auto new_row_of = [&](int64_t pos0, int64_t len) {
+    return p.n_new > 0 && pos0 + kUnit >= len ? (int)(len - 1 - pos0) : -1;
+  };
+
   StreamPos c0;
   {
     const int lo = uniform(s_first[gi]);  // the sequence holding unit u0
@@ -514,6 +599,7 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
   int64_t L0 = seq_len(c0.b), q_row0 = q_row_of(c0.b);
   bf16x8 qb[NKK];
   load_q(qb, q_row0, head_of(c0));
+  load_new(q_row0, head_of(c0));
   StreamPos c1 = advance(c0);
   int64_t L1 = same_run(c0, c1) || c1.b < 0 ? L0 : seq_len(c1.b);
   int64_t q_row1 = c1.b == c0.b || c1.b < 0 ? q_row0 : q_row_of(c1.b);
@@ -542,8 +628,9 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
 
     const int h0 = head_of(c0);
     const int h1 = head_of(c1);
-    consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, base + (int64_t)c0.j * kUnit, L0, lane,
-                         [&] {
+    const int64_t pos0 = base + (int64_t)c0.j * kUnit;
+    consume_unit<ESZ, D>(u, ktile, vtile, qb, acc, m_run, l_run, logit_scale, pos0, L0, lane, new_row_of(pos0, L0),
+                         nk, nv, [&] {
                            if (c1.b >= 0) {
                              issue_k<ESZ, D>(u, krsrc(h1, pg1.p0), krsrc(h1, pg1.p1), off);
                              issue_v<ESZ, D>(u, vrsrc(h1, pg1.p0), vrsrc(h1, pg1.p1), off);
@@ -553,7 +640,10 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
 
     if (run_ends) {
       // the next run's query (its latency overlaps the write-out below)
-      if (c1.b >= 0) load_q(qb, q_row1, head_of(c1));
+      if (c1.b >= 0) {
+        load_q(qb, q_row1, head_of(c1));
+        load_new(q_row1, head_of(c1));
+      }
       // the four lane groups hold partial sums of the same head (same max)
       l_run += xor_shuffle(l_run, 16);
       l_run += xor_shuffle(l_run, 32);
@@ -581,7 +671,10 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
           }
         }
       }
-      if (c1.b < 0) break;
+      if (c1.b < 0) {
+        finish_copy();
+        break;
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
       m_run = -INFINITY;
@@ -767,6 +860,18 @@ int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu, in
   }
   const int R = decode_groups(Hkv);
   return (int)(std::min<int64_t>(parts * R, kDecodeMaxParts) / R * R);
+}
+
+// Whether the decode launch for p can carry the write of n_new rows of
+// row_bytes each: a workgroup holds kCopyRegs chunks of 16 bytes per thread
+// and pool, and takes every gridDim.x-th row.
+bool decode_can_fuse_write(const AttnParams& p, int64_t n_new, int64_t row_bytes) {
+  if (row_bytes <= 0 || row_bytes % 16 != 0) return false;
+  const int R = decode_groups(p.Hkv);
+  const int64_t wgs = p.grid_parts / R, threads = 64 * decode_waves(p.Hkv) * R;
+  if (wgs <= 0) return false;
+  const int64_t rows_per_wg = (n_new + wgs - 1) / wgs;
+  return rows_per_wg * (row_bytes / 16) <= kCopyRegs * threads;
 }
 
 template <int ESZ, int D>

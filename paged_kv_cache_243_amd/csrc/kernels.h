@@ -73,6 +73,16 @@ struct AttnParams {
   int prefix_tiles, prefix_chunks, prefix_chunk_len;
   float* ws_pre_ml;    // [prefix_chunks, B, Hq, 2] partial (max in log2 units, sum)
   float* ws_pre_o;     // [prefix_chunks, B, Hq, D] unnormalised partial outputs
+  // decode fused with the write (n_new > 0, n_new = T: the new rows are the
+  // query rows' own keys): decode_kernel takes the key at the last position
+  // of the sequence owning query row t from row t of new_k/new_v [n_new, Hkv,
+  // D] (pool dtype) instead of the pool, and writes each new row to its pool
+  // row new_slots[t] (negative: skipped)
+  const void* new_k;
+  const void* new_v;
+  const int64_t* new_slots;
+  int64_t n_new;
+  int kv_bytes;  // bytes per pool element (1 fp8, 2 bf16, 4 fp32)
 };
 
 // Optional events recorded around the main attention kernel of a launch.
@@ -98,6 +108,9 @@ hipError_t launch_csr_to_block_table(const int64_t* indptr, const int64_t* indic
 size_t decode_workspace_bytes(int64_t B, int Hq, int D, int parts);
 // partition ranges of the decode work: a multiple of the parts one workgroup runs
 int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu, int Hkv);
+// whether the decode launch planned in p (grid_parts set) can also write
+// n_new rows of row_bytes each (the fused write)
+bool decode_can_fuse_write(const AttnParams& p, int64_t n_new, int64_t row_bytes);
 void decode_workspace_carve(AttnParams& p, void* workspace, int parts);
 constexpr int kDecodeMaxParts = 2048;
 constexpr int kDecodeMaxSeqs = 4096;

@@ -194,6 +194,7 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
   p.G = (int)G;
   p.scale = scale;
   p.kv_type = kv == PKV_F32 ? pkv::KV_F32 : (fp8 ? pkv::KV_FP8 : pkv::KV_BF16);
+  p.kv_bytes = elem_bytes(kv);
   p.max_query_len = (int)std::min<int64_t>(max_q, INT32_MAX);
 
   plan.workspace = 0;
@@ -311,8 +312,13 @@ const char* pkv_status_string(int status) {
   }
 }
 
-int paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
-                   pkv_tensor* key_pool, pkv_tensor* value_pool, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the write; fills its launch parameters.
+int plan_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+               const pkv_tensor* key_pool, const pkv_tensor* value_pool, WriteParams& p) {
   PKV_TRY(check_tensor(k, 3, 16));
   PKV_TRY(check_tensor(v, 3, 16));
   PKV_TRY(check_tensor(slot_mapping, 1, 8));
@@ -327,7 +333,6 @@ int paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* s
   if (k->shape[1] != key_pool->shape[2] || k->shape[2] != key_pool->shape[3]) return PKV_ERR_SHAPE;
   const int64_t row_bytes = key_pool->shape[2] * key_pool->shape[3] * elem_bytes(kv);
   if (row_bytes <= 0 || row_bytes % 16 != 0) return PKV_ERR_UNSUPPORTED;
-  WriteParams p;
   p.k = k->data;
   p.v = v->data;
   p.slots = (const int64_t*)slot_mapping->data;
@@ -335,6 +340,17 @@ int paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* s
   p.value_pool = value_pool->data;
   p.n_tokens = k->shape[0];
   p.row_bytes = row_bytes;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_kv_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+                   pkv_tensor* key_pool, pkv_tensor* value_pool, void* stream) {
+  WriteParams p;
+  PKV_TRY(plan_write(k, v, slot_mapping, key_pool, value_pool, p));
   if (p.n_tokens == 0) return PKV_OK;
   return pkv::launch_write(p, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
@@ -423,13 +439,44 @@ int paged_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_t
   return launch_attention(plan, opts ? opts->workspace : nullptr, opts, s);
 }
 
+int paged_kv_write_attention(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_mapping,
+                             pkv_tensor* key_pool, pkv_tensor* value_pool, const pkv_tensor* q,
+                             const pkv_tensor* block_table, const pkv_tensor* seq_lens,
+                             const pkv_tensor* query_start_loc, float scale, pkv_tensor* out,
+                             const pkv_attn_opts* opts, void* stream) {
+  const hipStream_t s = (hipStream_t)stream;
+  WriteParams wp;
+  PKV_TRY(plan_write(k, v, slot_mapping, key_pool, value_pool, wp));
+  AttnPlan plan;
+  PKV_TRY(plan_attention(q, key_pool, value_pool, block_table, seq_lens, query_start_loc, scale, out, opts, true,
+                         device_cu_count(stream_device(s)), false, plan));
+  if (plan.workspace > 0) {
+    if (!opts || !opts->workspace) return PKV_ERR_WORKSPACE;
+    if (opts->workspace_bytes < plan.workspace) return PKV_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(opts->workspace) % 16 != 0) return PKV_ERR_WORKSPACE;
+  }
+  void* ws = opts ? opts->workspace : nullptr;
+  if (plan.kernel == AttnPlan::kDecode && wp.n_tokens == q->shape[0] &&
+      pkv::decode_can_fuse_write(plan.p, wp.n_tokens, wp.row_bytes)) {
+    // a decode step whose new rows are the query rows' keys: one kernel
+    // writes them and attends, taking each sequence's last key from them
+    plan.p.new_k = wp.k;
+    plan.p.new_v = wp.v;
+    plan.p.new_slots = wp.slots;
+    plan.p.n_new = wp.n_tokens;
+    return launch_attention(plan, ws, opts, s);
+  }
+  if (wp.n_tokens > 0 && pkv::launch_write(wp, s) != hipSuccess) return PKV_ERR_HIP;
+  return launch_attention(plan, ws, opts, s);
+}
+
 // Host-memory form of the metadata check; paged_validate_metadata copies the
 // device tensors and calls it.
 int pkv_check_metadata_host(const int64_t* slots, int64_t n_slots, const int64_t* block_table,
                             int64_t B, int64_t max_blocks, const int64_t* seq_lens,
                             const int64_t* qsl, int64_t num_pages, int64_t page_size,
-                            int64_t num_query_rows, int64_t shared_prefix_pages, char* message,
-                            size_t message_len) {
+                            int64_t num_query_rows, int64_t shared_prefix_pages, uint32_t checks,
+                            char* message, size_t message_len) {
   auto fail = [&](const char* fmt, long long a, long long b) {
     if (message && message_len) snprintf(message, message_len, fmt, a, b);
     return PKV_ERR_INDEX;
@@ -486,13 +533,43 @@ int pkv_check_metadata_host(const int64_t* slots, int64_t n_slots, const int64_t
           return fail("sequence %lld does not share prefix page %lld", (long long)b, (long long)j);
     }
   }
+  // the fused write + attention's statement: new row t is the key of query
+  // row t, stored at the slot of that row's position, and no sequence reads a
+  // slot this step writes at any other position
+  if (checks & PKV_CHECK_NEW_ROWS_ARE_QUERY_ROWS) {
+    if (!slots) return fail("the new-rows check needs slot_mapping (%lld, %lld)", 0, 0);
+    if (n_slots != num_query_rows)
+      return fail("slot_mapping has %lld rows, not the %lld query rows", (long long)n_slots, (long long)num_query_rows);
+    auto slot_of = [&](int64_t b, int64_t pos) {
+      return block_table[b * max_blocks + pos / page_size] * page_size + pos % page_size;
+    };
+    for (int64_t b = 0; b < B; ++b) {
+      const int64_t n = qsl[b + 1] - qsl[b], L = seq_lens[b];
+      for (int64_t i = 0; i < n; ++i)
+        if (slots[qsl[b] + i] != slot_of(b, L - n + i))
+          return fail("slot_mapping[%lld] = %lld is not the slot of its query row's position",
+                      (long long)(qsl[b] + i), (long long)slots[qsl[b] + i]);
+    }
+    std::vector<int64_t> written;
+    for (int64_t t = 0; t < n_slots; ++t)
+      if (slots[t] >= 0) written.push_back(slots[t]);
+    std::sort(written.begin(), written.end());
+    for (int64_t b = 0; b < B; ++b) {
+      const int64_t older = seq_lens[b] - (qsl[b + 1] - qsl[b]);
+      for (int64_t pos = 0; pos < older; ++pos)
+        if (std::binary_search(written.begin(), written.end(), slot_of(b, pos)))
+          return fail("sequence %lld reads slot %lld, which the step writes, at an older position", (long long)b,
+                      (long long)slot_of(b, pos));
+    }
+  }
   return PKV_OK;
 }
 
 int paged_validate_metadata(const pkv_tensor* slot_mapping, const pkv_tensor* block_table,
                             const pkv_tensor* seq_lens, const pkv_tensor* query_start_loc,
                             int64_t num_pages, int64_t page_size, int64_t num_query_rows,
-                            int64_t shared_prefix_pages, void* stream, char* message, size_t message_len) {
+                            int64_t shared_prefix_pages, uint32_t checks, void* stream, char* message,
+                            size_t message_len) {
   if (slot_mapping) PKV_TRY(check_tensor(slot_mapping, 1, 8));
   PKV_TRY(check_tensor(block_table, 2, 8));
   PKV_TRY(check_tensor(seq_lens, 1, 8));
@@ -516,7 +593,7 @@ int paged_validate_metadata(const pkv_tensor* slot_mapping, const pkv_tensor* bl
   if (hipStreamSynchronize(s) != hipSuccess) return PKV_ERR_HIP;
   return pkv_check_metadata_host(slot_mapping ? sm.data() : nullptr, (int64_t)sm.size(), bt.data(), B,
                                  block_table->shape[1], sl.data(), qs.data(), num_pages, page_size,
-                                 num_query_rows, shared_prefix_pages, message, message_len);
+                                 num_query_rows, shared_prefix_pages, checks, message, message_len);
 }
 
 }  // extern "C"

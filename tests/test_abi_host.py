@@ -521,3 +521,33 @@ def test_noalloc_refuses_before_touching_a_device():
     assert call(o) == -6
     assert B.NOALLOC_SCRATCH_BYTES == 128 << 20
     assert "#define PKV_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in open(HEADER).read()
+
+
+def test_new_rows_statement_check():
+    """PKV_CHECK_NEW_ROWS_ARE_QUERY_ROWS (the fused decode step's statement):
+    the workloads' own metadata pass; a slot that is not its row's position,
+    a missing row, and another sequence reading a written slot are reported."""
+    from paged_kv_cache_243_amd import workloads as W
+    from tests.helpers import S
+    for cid in (2, 3, 4, 5):
+        w = W.generate(W.SMALL[cid])
+        args = (S(w.slot_mapping), S(w.block_table), S(w.seq_lens), S(w.query_start_loc), w.cfg.num_pages, 16,
+                w.q.shape[0])
+        assert pkv.check_metadata_host(*args, checks=pkv.CHECK_NEW_ROWS_ARE_QUERY_ROWS) == (0, "")
+    w = W.generate(W.SMALL[2])
+    sm, bt, sl, qsl = S(w.slot_mapping).copy(), S(w.block_table).copy(), S(w.seq_lens), S(w.query_start_loc)
+    n_pages = w.cfg.num_pages
+    check = lambda sm_, bt_: pkv.check_metadata_host(sm_, bt_, sl, qsl, n_pages, 16, len(qsl) - 1, checks=1)
+    bad = sm.copy()
+    bad[2] = sm[2] - 1 if sm[2] % 16 else sm[2] + 1       # a neighbouring row of the same page
+    st, msg = check(bad, bt)
+    assert st == -8 and "not the slot of its query row" in msg, msg
+    st, msg = check(sm[:-1], bt)
+    assert st == -8 and "query rows" in msg, msg
+    # sequence 1's first page replaced by the page sequence 0's new token lands in
+    bt2 = bt.copy()
+    bt2[1, 0] = sm[0] // 16
+    st, msg = check(sm, bt2)
+    assert st == -8 and "which the step writes" in msg, msg
+    # without the flag the same metadata is fine for the separate calls
+    assert pkv.check_metadata_host(sm, bt2, sl, qsl, n_pages, 16, len(qsl) - 1)[0] == 0

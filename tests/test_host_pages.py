@@ -300,7 +300,7 @@ def test_metadata_from_the_control_plane_gives_dense_attention():
     T = int(qsl[-1])
     q = rng.standard_normal((T, Hq, D)).astype(np.float32)
     assert B.load().pkv_check_metadata_host(None, 0, bt.ctypes.data, len(seqs), max_blocks, sl.ctypes.data,
-                                            qsl.ctypes.data, num_pages, ps, T, 0, None, 0) == 0
+                                            qsl.ctypes.data, num_pages, ps, T, 0, 0, None, 0) == 0
     out = oracle.paged_attention(q, "f32", kpool, vpool, "f32", bt, sl, qsl, 0.125)
     for b, s in enumerate(seqs):
         k, v = rows(toks_of[s])
