@@ -291,6 +291,13 @@ def traffic_from_profile(kernel: str):
     return None if entry is None else entry.get("traffic_bytes_per_launch")
 
 
+def fp8_prefill_config(W):
+    """The chunked-prefill workload (config 3) with fp8 E4M3FN pools."""
+    import dataclasses
+    c = W.CONFIGS[3]
+    return dataclasses.replace(c, name=c.name + "-fp8", kv_dtype="fp8_e4m3fn")
+
+
 def tp_shard(W, cid: int, tp: int):
     """Config `cid` with the heads one GPU holds under a `tp`-way head split."""
     return W.head_shard(W.CONFIGS[cid], tp)
@@ -501,7 +508,7 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--profile-workload",
-                    choices=["decode", "prefill", "shared", "sharedplain", "fp8", "fp8write", "csr",
+                    choices=["decode", "prefill", "prefill_fp8", "shared", "sharedplain", "fp8", "fp8write", "csr",
                              "decode_tp8", "fp8_tp8", "prefill_tp8"],
                     help="time one workload only and print its median times (for profiler runs)")
     args = ap.parse_args(argv)
@@ -534,9 +541,12 @@ def main(argv=None) -> int:
                           "write_ms_mean": statistics.fmean(t.write)}), flush=True)
         return 0
     if args.profile_workload:
-        cid = {"decode": 2, "prefill": 3, "shared": 4, "sharedplain": 4, "fp8": 5,
+        cid = {"decode": 2, "prefill": 3, "prefill_fp8": 3, "shared": 4, "sharedplain": 4, "fp8": 5,
                "decode_tp8": 2, "fp8_tp8": 5, "prefill_tp8": 3}[args.profile_workload]
-        w = W.generate(tp_shard(W, cid, 8) if args.profile_workload.endswith("_tp8") else cid, dev)
+        if args.profile_workload == "prefill_fp8":
+            w = W.generate(fp8_prefill_config(W), dev)
+        else:
+            w = W.generate(tp_shard(W, cid, 8) if args.profile_workload.endswith("_tp8") else cid, dev)
         # calibration for hardware byte counters: a plain device copy of known
         # size (256 MiB read + 256 MiB written), launched once
         calib = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
@@ -684,6 +694,28 @@ def main(argv=None) -> int:
             log("timing the CPU oracle on the chunked-prefill workload (sampled rows)")
             cpu["prefill"] = cpu_baseline_prefill(w3)
         del w3
+        torch.cuda.empty_cache()
+        # the same chunked prefill over fp8 E4M3FN pools (per-head scales)
+        log("generating the chunked-prefill workload with fp8 KV")
+        w3f = W.generate(fp8_prefill_config(W), dev)
+        r3f = Runner(pkv, w3f, torch)
+        t3f, c3f, kt3f = time_workload(r3f, torch, max(5, args.steps // 2), args.warmup, flush, "prefill fp8 KV")
+        k3f = statistics.fmean(kt3f.kernel)
+        fl3f = prefill_flops(w3f)
+        extra["prefill_fp8_kv"] = {
+            "workload": "the chunked causal prefill over fp8 E4M3FN pools with per-head scales (codes widened "
+                        "exactly to bf16, bf16 MFMA)",
+            "kernel": "prefill_kernel<1,128,1>",
+            "bound": "mfma", "unit": "TFLOP/s",
+            "achieved": round(fl3f / (k3f * 1e-3) / 1e12, 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "frac": round(fl3f / (k3f * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "flop_per_launch": fl3f,
+            "launch_ms_mean": round(k3f, 5),
+            "call_ms_median": round(statistics.median(c3f.attn), 5),
+            "step_ms_median": round(statistics.median(t3f.step), 5),
+        }
+        del r3f, w3f
         torch.cuda.empty_cache()
         # shared-prefix decode
         log("generating shared-prefix decode workload (config 4)")

@@ -23,10 +23,11 @@
 //    lds), 6 slots deep, two K and two V tiles behind each barrier; every page
 //    gets a buffer descriptor whose range ends at the sequence's last valid
 //    row, so rows at positions >= seq_lens read as zeros whatever the pool
-//    holds.  fp8 tiles go through registers and are widened to bf16 (rows past
-//    seq_lens stored as zeros), two slots deep, one barrier per tile.  LDS rows
-//    keep their 16-byte chunks XOR-swizzled so the operand reads below are
-//    spread over the banks.
+//    holds.  fp8 codes take the same DMA path into code slots (half the
+//    bytes), two sets of four tiles, and every wave widens its share of them
+//    exactly to bf16 into 4-slot rings one hand-off later, with the same
+//    barrier cadence.  LDS rows keep their 16-byte chunks XOR-swizzled so the
+//    operand reads below are spread over the banks.
 //  * S^T = K . Q^T with v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from
 //    LDS, B = 16 dims x 32 query rows held in registers): each lane owns 16 keys
 //    of one query row, so a row max needs one cross-lane step.
@@ -321,50 +322,55 @@ __device__ __forceinline__ void dma_tile(const TileSrc& c, __bf16* tile, int t, 
   }
 }
 
-// fp8: a tile's codes through registers (one 16-byte chunk per thread and pass)
-template <int D, int THREADS>
-struct Fp8Tile {
-  static constexpr int CPR = D / 16;         // 16-byte code chunks per row
-  static constexpr int RPP = THREADS / CPR;  // rows per pass
-  static constexpr int PASSES = RPP >= kKeyTile ? 1 : kKeyTile / RPP;
-  u32x4 x[PASSES];
+// fp8: a tile's codes (32 rows x D bytes) go straight into an LDS code slot.
+// One load moves 1 KiB per wave (lane l -> LDS bytes 16 l after the wave's
+// base), i.e. 1024 / D whole rows of one page; the codes keep the pool's row
+// layout.  A hand-off fetches 4 tiles (two K, two V), its loads spread over
+// the waves.  Rows past seq_lens read as zeros and touch no memory.
+template <int D, int WAVES>
+struct Dma8 {
+  static constexpr int ROWS = 1024 / D;               // rows per load: 8 (D = 128) or 16 (D = 64)
+  static constexpr int PER_TILE = kKeyTile / ROWS;    // loads per tile: 4 or 2
+  static constexpr int PER_HANDOFF = 4 * PER_TILE;    // loads per hand-off: 16 or 8
+  static constexpr int LOADS = PER_HANDOFF / WAVES;   // per wave
+  static_assert(PER_HANDOFF % WAVES == 0 && kPageSize % ROWS == 0, "a load's rows share a page");
 };
 
-template <int D, int THREADS>
-__device__ __forceinline__ void fp8_fetch(Fp8Tile<D, THREADS>& st, const TileSrc& c, const char* base, int t,
-                                          int tid) {
-  using S = Fp8Tile<D, THREADS>;
-  const int chunk = tid % S::CPR, r0 = tid / S::CPR;
-#pragma unroll
-  for (int i = 0; i < S::PASSES; ++i) {
-    const int r = r0 + S::RPP * i;
-    if (r < kKeyTile) {
-      const int key = t * kKeyTile + r;
-      const int lp = key >> 4;
-      const int64_t page = c.bt[lp < c.last_page ? lp : c.last_page];
-      st.x[i] = *(const u32x4*)(base + page * c.page_stride + (key & 15) * c.row_stride + 16 * chunk);
-    }
-  }
+// Page holding rows part * ROWS .. of tile t (clamped into the sequence, as wave_page).
+template <int D, int WAVES>
+__device__ __forceinline__ int64_t page8(const TileSrc& c, int t, int part) {
+  const int lp = (t * kKeyTile + part * Dma8<D, WAVES>::ROWS) >> 4;
+  const int lpc = lp < 0 ? 0 : (lp < c.last_page ? lp : c.last_page);
+  return c.bt[lpc];
 }
 
-template <int D, int THREADS, bool IS_V>
-__device__ __forceinline__ void fp8_store(const Fp8Tile<D, THREADS>& st, __bf16* tile, int t, int64_t L, int tid) {
-  using S = Fp8Tile<D, THREADS>;
+template <int D, int WAVES>
+__device__ __forceinline__ void dma8_rows(const TileSrc& c, const char* base, char* ctile, int t, int part,
+                                          int64_t page, int lane) {
+  using M = Dma8<D, WAVES>;
+  constexpr int CPR = D / 16;  // 16-byte chunks per code row
+  const int r0 = part * M::ROWS;
+  const int lp = (t * kKeyTile + r0) >> 4;  // logical page (negative before position 0)
+  int valid = c.L - (lp << 4);
+  valid = lp < 0 || valid < 0 ? 0 : (valid > kPageSize ? kPageSize : valid);
+  const u32x4 r = uniform_rsrc(base + page * c.page_stride, (uint32_t)valid * c.row_stride);
+  const int row = r0 + lane / CPR;
+  const uint32_t voff = (uint32_t)(row & 15) * c.row_stride + 16u * (lane % CPR);
+  dma16(r, (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(ctile + r0 * D), voff);
+}
+
+// Widen one 16-code chunk (row r, chunk k of a code tile) into the bf16 tile
+// at `dst`, laid out and swizzled as the bf16 tiles the DMA path fills (exact:
+// every E4M3FN value is a bf16 value).
+template <int D>
+__device__ __forceinline__ void widen_chunk(const char* codes, char* dst, bool is_v, int r, int k) {
   using TL = TileLayout<D>;
-  const int chunk = tid % S::CPR, r0 = tid / S::CPR;
-#pragma unroll
-  for (int i = 0; i < S::PASSES; ++i) {
-    const int r = r0 + S::RPP * i;
-    if (r < kKeyTile) {
-      const bool live = (int64_t)t * kKeyTile + r < L;
-      const u32x2 c0 = fp8x4_to_bf16x4(st.x[i].x), c1 = fp8x4_to_bf16x4(st.x[i].y);
-      const u32x2 c2 = fp8x4_to_bf16x4(st.x[i].z), c3 = fp8x4_to_bf16x4(st.x[i].w);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      const int sw = IS_V ? TL::swz_v(r) : TL::swz_k(r);
-      *(u32x4*)(tile + r * D + 8 * ((2 * chunk) ^ sw)) = live ? u32x4{c0.x, c0.y, c1.x, c1.y} : z;
-      *(u32x4*)(tile + r * D + 8 * ((2 * chunk + 1) ^ sw)) = live ? u32x4{c2.x, c2.y, c3.x, c3.y} : z;
-    }
-  }
+  const u32x4 x = *(const u32x4*)(codes + r * D + 16 * k);
+  const u32x2 c0 = fp8x4_to_bf16x4(x.x), c1 = fp8x4_to_bf16x4(x.y);
+  const u32x2 c2 = fp8x4_to_bf16x4(x.z), c3 = fp8x4_to_bf16x4(x.w);
+  const int sw = is_v ? TL::swz_v(r) : TL::swz_k(r);
+  *(u32x4*)(dst + r * 2 * D + 16 * ((2 * k) ^ sw)) = u32x4{c0.x, c0.y, c1.x, c1.y};
+  *(u32x4*)(dst + r * 2 * D + 16 * ((2 * k + 1) ^ sw)) = u32x4{c2.x, c2.y, c3.x, c3.y};
 }
 
 __device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
@@ -417,12 +423,15 @@ void prefill_kernel(AttnParams p) {
   constexpr int NKS = D / 16;              // score MFMA k-steps
   constexpr int NDB = D / 32;              // output dim blocks
   // K/V ring depth: bf16 tiles arrive by DMA two at a time, one workgroup
-  // barrier per two tiles; fp8 tiles go through registers, one per barrier
-  constexpr int NS = ESZ == 2 ? 6 : 2;
+  // barrier per two tiles, 6 slots deep; fp8 codes arrive by DMA into code
+  // slots (two sets of four tiles) and are widened into 4-slot bf16 rings one
+  // hand-off later, with the same barrier cadence
+  constexpr int NS = ESZ == 2 ? 6 : 4;
   constexpr int TB = kKeyTile * D * 2;     // bytes per LDS tile
   using TL = TileLayout<D>;
   __shared__ __attribute__((aligned(16))) char sk[NS][TB];
   __shared__ __attribute__((aligned(16))) char sv[NS][TB];
+  __shared__ __attribute__((aligned(16))) char sc[ESZ == 1 ? 2 : 1][4][ESZ == 1 ? kKeyTile * D : 16];
 
   const int rank = (int)(blockIdx.x / (unsigned)p.Hkv), h = (int)(blockIdx.x % (unsigned)p.Hkv);
   const int tid = threadIdx.x, lane = tid & 63;
@@ -723,11 +732,6 @@ void prefill_kernel(AttnParams p) {
   using DM = Dma<D, WAVES>;
   // Page ids of this wave's rows; V(j) reuses the id fetched for K(j).
   int64_t page_k[2] = {0, 0}, page_v[2] = {0, 0};
-  Fp8Tile<D, THREADS> fk, fv;  // fp8 staging: iteration t fetches K(t+2) and V(t)
-  auto store8 = [&](int t, int slot) __attribute__((always_inline)) {
-    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[slot], t + 2, c.L, tid);
-    fp8_store<D, THREADS, true>(fv, (__bf16*)sv[slot], t, c.L, tid);
-  };
 
   bf16x8 pb_prev[2][NB];
 #pragma unroll
@@ -841,39 +845,97 @@ void prefill_kernel(AttnParams p) {
     }
     wait_vmem<0>();  // no tile write may land after the workgroup ends
   } else {
-    // fp8: iteration t converts K(t+2) and V(t) through registers into the
-    // slots that K(t) and V(t-2) held; a barrier per iteration
+    // fp8: a hand-off before every even iteration t.  After the barrier the
+    // bf16 slots hold K(t+1), K(t+2), V(t-1) and V(t) (read by iterations t
+    // and t+1), and the codes of K(t+5), K(t+6), V(t+3) and V(t+4) are
+    // fetched into code set (t/2) % 2, whose codes were widened before this
+    // barrier.  After iterations t and t+1, the codes the previous hand-off
+    // fetched, K(t+3), K(t+4), V(t+1) and V(t+2) (landed in set (t/2 + 1) % 2
+    // before the barrier), are widened into the four slots no wave reads any
+    // more; vmcnt(0) then lands this hand-off's codes before the next barrier.
+    // Widening there rather than right after the barrier measured 4 % faster
+    // (the widening's LDS round trip no longer delays the MFMAs' operands).
+    using M8 = Dma8<D, WAVES>;
+    constexpr int CPR = D / 16;
+    constexpr int TASKS = 4 * kKeyTile * CPR;  // 16-code chunks of a set
+    static_assert(TASKS % THREADS == 0 && (kKeyTile * CPR) % 64 == 0, "each wave widens chunks of one tile");
+    int64_t pg8[M8::LOADS];
+    // tile of code slot q fetched at the hand-off before iteration t
+    auto tile_of = [](int q, int t) { return q == 0 ? t + 5 : q == 1 ? t + 6 : q == 2 ? t + 3 : t + 4; };
+    auto next_pages = [&](int t) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < M8::LOADS; ++k) {
+        const int li = wave + WAVES * k, q = li / M8::PER_TILE, part = li % M8::PER_TILE;
+        pg8[k] = page8<D, WAVES>(c, tile_of(q, t), part);
+      }
+    };
+    auto fetch_codes = [&](int set, int t) __attribute__((always_inline)) {
+#pragma unroll
+      for (int k = 0; k < M8::LOADS; ++k) {
+        const int li = wave + WAVES * k, q = li / M8::PER_TILE, part = li % M8::PER_TILE;
+        dma8_rows<D, WAVES>(c, q < 2 ? c.kbase : c.vbase, sc[set][q], tile_of(q, t), part, pg8[k], lane);
+      }
+    };
+    // widen code set `set` (slots 0..3) into dst[q]; slots 2 and 3 hold V
+    // tiles unless v2 is false (the prologue's K(2))
+    auto widen = [&](int set, char* d0, char* d1, char* d2, char* d3, bool v2) __attribute__((always_inline)) {
+#pragma unroll
+      for (int j0 = 0; j0 < TASKS; j0 += THREADS) {
+        const int j = j0 + tid, q = j / (kKeyTile * CPR), task = j % (kKeyTile * CPR);
+        char* dst = q == 0 ? d0 : q == 1 ? d1 : q == 2 ? d2 : d3;
+        widen_chunk<D>(sc[set][q], dst, q == 3 || (q == 2 && v2), task / CPR, task % CPR);
+      }
+    };
+    auto pair8 = [&](auto mask_c, auto r_c, int t) __attribute__((always_inline)) {
+      constexpr int R = decltype(r_c)::value;
+      barrier_lds();
+      fetch_codes(R / 2, t);
+      compute(mask_c, r_c, t);
+      compute(mask_c, std::integral_constant<int, R + 1>{}, t + 1);
+      // (after the pair's MFMAs, whose operand reads it would otherwise delay;
+      // its writes reach the other waves through the next barrier)
+      widen((R / 2 + 1) % 2, sk[(R + 3) % NS], sk[R], sv[(R + 1) % NS], sv[(R + 2) % NS], true);
+      wait_vmem<0>();
+      __builtin_amdgcn_sched_barrier(0);
+      next_pages(t + 2);
+    };
+
+    // prologue: codes of K(0), K(1), K(2) and V(0) into set 0, of K(3), K(4),
+    // V(1) and V(2) into set 1; set 0 widened into K slots 0..2 and V slot 0,
+    // V slot 3 (V(-1), multiplied by P(-1) = 0) zeroed; the scores of tile 0
+#pragma unroll
+    for (int k = 0; k < M8::LOADS; ++k) {
+      const int li = wave + WAVES * k, q = li / M8::PER_TILE, part = li % M8::PER_TILE;
+      const int t0 = q == 3 ? 0 : q, t1 = q == 0 ? 3 : q == 1 ? 4 : q - 1;
+      dma8_rows<D, WAVES>(c, q == 3 ? c.vbase : c.kbase, sc[0][q], t0, part, page8<D, WAVES>(c, t0, part), lane);
+      dma8_rows<D, WAVES>(c, q >= 2 ? c.vbase : c.kbase, sc[1][q], t1, part, page8<D, WAVES>(c, t1, part), lane);
+    }
     load_q();
-    fp8_fetch<D, THREADS>(fk, c, c.kbase, 0, tid);
-    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[0], 0, c.L, tid);
-    fp8_fetch<D, THREADS>(fk, c, c.kbase, 1, tid);
-    fp8_store<D, THREADS, false>(fk, (__bf16*)sk[1], 1, c.L, tid);
-    for (int i = tid; i < TB / 16; i += THREADS) ((u32x4*)sv[1])[i] = u32x4{0u, 0u, 0u, 0u};
+    wait_vmem<0>();
+    barrier_lds();
+    widen(0, sk[0], sk[1], sk[2], sv[0], false);
+    for (int i = tid; i < TB / 16; i += THREADS) ((u32x4*)sv[3])[i] = u32x4{0u, 0u, 0u, 0u};
     barrier_lds();
     {
       bf16x8 ka[NKS];
       read_k(0, ka);
       scores(ka, s_cur);
     }
-    auto iteration = [&](auto mask_c, auto r_c, int t) __attribute__((always_inline)) {
-      constexpr int R = decltype(r_c)::value;
-      barrier_lds();
-      fp8_fetch<D, THREADS>(fk, c, c.kbase, t + 2, tid);
-      fp8_fetch<D, THREADS>(fv, c, c.vbase, t, tid);
-      compute(mask_c, r_c, t);
-      store8(t, R);
-    };
+    next_pages(0);
+
     using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
     const int t_split = t_diag / NS * NS;
     for (; t < t_split; t += NS) {
-      iteration(std::false_type{}, I0{}, t);
-      iteration(std::false_type{}, I1{}, t + 1);
+      pair8(std::false_type{}, I0{}, t);
+      pair8(std::false_type{}, I2{}, t + 2);
     }
     for (; t <= n_tiles; t += NS) {
-      iteration(std::true_type{}, I0{}, t);
-      iteration(std::true_type{}, I1{}, t + 1);
+      pair8(std::true_type{}, I0{}, t);
+      if (t + 2 > n_tiles) break;
+      pair8(std::true_type{}, I2{}, t + 2);
     }
+    wait_vmem<0>();  // no code fetch may land after the workgroup ends
   }
 
 
