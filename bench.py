@@ -499,6 +499,65 @@ def host_control_plane_timing() -> dict:
             "us_per_step_median": round(times[len(times) // 2] * 1e6, 1)}
 
 
+def _counter_means(run_dir: str, counter: str) -> dict:
+    """(mean, dispatches, largest) of `counter` per dispatch, by kernel name,
+    over the rocprofv3 counter-collection CSVs under run_dir."""
+    import csv
+    import glob
+    vals = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] == counter:
+                    vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: (sum(v) / len(v), len(v), max(v)) for k, v in vals.items()}
+
+
+def write_traffic(fetch_dir: str, write_dir: str) -> int:
+    """profiles/traffic.json from the FETCH_SIZE and WRITE_SIZE runs of
+    `--profile-workload decode` (the one-call step): each counter (KiB per
+    dispatch) is scaled by the factor that maps it, on the 256 MiB device copy
+    the profile run launches first, to the copy's true size."""
+    from paged_kv_cache_243_amd import workloads as W
+    fetch = _counter_means(fetch_dir, "FETCH_SIZE")
+    write = _counter_means(write_dir, "WRITE_SIZE")
+    kib = CALIB_BYTES / 1024
+
+    def calib(table):
+        # the largest device copy dispatch is the 256 MiB calibration copy
+        copies = [v[2] for k, v in table.items() if "copyBuffer" in k]
+        if not copies:
+            raise SystemExit("no calibration copy in the counter run")
+        return max(copies)
+    f_cal, w_cal = calib(fetch), calib(write)
+    ff, wf = kib / f_cal, kib / w_cal
+    key = next(k for k in fetch if "decode_kernel<2, 128>" in k)
+    w2 = W.generate(2, "cpu")
+    alg = decode_kernel_bytes(w2) + write_bytes(w2)
+    fb = fetch[key][0] * 1024 * ff
+    wb = write[key][0] * 1024 * wf
+    out = {
+        "kernel_source_hash": kernel_source_hash(),
+        "note": "HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each "
+                "scaled by the factor that maps the same counter on a 256 MiB device copy to its true size",
+        "calibration": {"copy_bytes": CALIB_BYTES, "FETCH_SIZE_KiB": round(f_cal, 1),
+                        "WRITE_SIZE_KiB": round(w_cal, 1), "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+        "kernels": {"decode_kernel<2,128>": {
+            "workload": "the one-call paged decode step, bf16, B=64, Hq=32, Hkv=8, D=128, L_b ~ U{512..4096} "
+                        "(the split-K pass also writes the 64 new rows)",
+            "FETCH_SIZE_KiB_mean": round(fetch[key][0], 1), "WRITE_SIZE_KiB_mean": round(write[key][0], 1),
+            "dispatches": fetch[key][1],
+            "fetch_bytes_per_launch": int(fb), "write_bytes_per_launch": int(wb),
+            "traffic_bytes_per_launch": int(fb + wb), "algorithmic_bytes_per_launch": alg,
+            "traffic_over_algorithmic": round((fb + wb) / alg, 4)}},
+    }
+    with open(PROFILE_TRAFFIC, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out["kernels"]), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -508,10 +567,17 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true", help="do not evict caches between steps")
     ap.add_argument("--profile-workload",
-                    choices=["decode", "prefill", "prefill_fp8", "shared", "sharedplain", "fp8", "fp8write", "csr",
-                             "decode_tp8", "fp8_tp8", "prefill_tp8"],
-                    help="time one workload only and print its median times (for profiler runs)")
+                    choices=["decode", "decode_2calls", "prefill", "prefill_fp8", "shared", "sharedplain", "fp8",
+                             "fp8write", "csr", "decode_tp8", "fp8_tp8", "prefill_tp8"],
+                    help="time one workload only and print its median times (for profiler runs); decode and fp8 "
+                         "run the one-call step the headline times")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="(no GPU) write profiles/traffic.json from the rocprofv3 FETCH_SIZE and WRITE_SIZE "
+                         "counter runs of --profile-workload decode")
     args = ap.parse_args(argv)
+
+    if args.write_traffic:
+        return write_traffic(*args.write_traffic)
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -541,8 +607,8 @@ def main(argv=None) -> int:
                           "write_ms_mean": statistics.fmean(t.write)}), flush=True)
         return 0
     if args.profile_workload:
-        cid = {"decode": 2, "prefill": 3, "prefill_fp8": 3, "shared": 4, "sharedplain": 4, "fp8": 5,
-               "decode_tp8": 2, "fp8_tp8": 5, "prefill_tp8": 3}[args.profile_workload]
+        cid = {"decode": 2, "decode_2calls": 2, "prefill": 3, "prefill_fp8": 3, "shared": 4, "sharedplain": 4,
+               "fp8": 5, "decode_tp8": 2, "fp8_tp8": 5, "prefill_tp8": 3}[args.profile_workload]
         if args.profile_workload == "prefill_fp8":
             w = W.generate(fp8_prefill_config(W), dev)
         else:
@@ -553,9 +619,11 @@ def main(argv=None) -> int:
         torch.empty_like(calib).copy_(calib)
         del calib
         pages = w.cfg.shared_prefix_tokens // w.cfg.page_size if args.profile_workload == "shared" else 0
-        t = time_steps(Runner(pkv, w, torch, shared_prefix_pages=pages), torch, args.steps, args.warmup, flush,
-                       args.profile_workload, mid_event=True)
-        print(json.dumps({"workload": w.cfg.name, "write_ms_median": statistics.median(t.write),
+        fused = args.profile_workload in ("decode", "fp8")
+        t = time_steps(Runner(pkv, w, torch, shared_prefix_pages=pages, fused=fused), torch, args.steps,
+                       args.warmup, flush, args.profile_workload, mid_event=not fused)
+        print(json.dumps({"workload": w.cfg.name, "form": "one call" if fused else "two calls",
+                          "write_ms_median": statistics.median(t.write) if t.write else None,
                           "attention_ms_median": statistics.median(t.attn),
                           "main_kernel_ms_median": statistics.median(t.kernel),
                           "main_kernel_ms_mean": statistics.fmean(t.kernel),
