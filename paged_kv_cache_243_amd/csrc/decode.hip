@@ -694,19 +694,30 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
 // Log-sum-exp merge of the partials of a sequence whose units span several
 // parts (and, with a shared prefix, of the prefix chunks' partials):
 //   M = max_w m_w,  out = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w.
-// One workgroup of nw waves (1 .. kMergeWaves, by the partials a sequence
-// has) per (query head, sequence).  Wave k takes the chunks k, k + nw, ... of
-// 8 consecutive partials (wave 0 also the prefix chunks'); every (m, l) and O
-// load of a chunk is issued before any of them is used, so a chunk costs one
-// memory round trip and the waves' round trips overlap.  With several waves
-// their (m, l, O) are then combined through LDS in wave order.
+// A workgroup serves nh query heads of one sequence (threadIdx.y), with nw
+// waves per head (1 .. kMergeWaves, by the partials a sequence has; nw * nh
+// <= kMergeWaves).  Wave k of a head takes the chunks k, k + nw, ... of 8
+// consecutive partials; wave 0 also the prefix chunks', whose loads go out
+// before the metadata's, as their slots do not depend on it.  Every (m, l)
+// and O load of a chunk is issued before any of them is used, so the merge
+// of a head costs two memory round trips (metadata, then partials) when its
+// partials fit one chunk.  With several waves per head their (m, l, O) are
+// then combined through LDS in wave order.  Several heads per workgroup keep
+// the CUs' wave slots full when there are many rows of few partials.
 constexpr int kMergeWaves = 4;
 
-// merge waves for a grid of `parts` parts over B sequences: one per 8 partials
-// a sequence holds on average, at most kMergeWaves
+// merge waves per head for a grid of `parts` parts over B sequences: one per
+// 8 partials a sequence holds on average, at most kMergeWaves
 static int merge_waves(int parts, int64_t B) {
   const int64_t per_seq = parts / std::max<int64_t>(B, 1) + 1;
   return (int)std::min<int64_t>(kMergeWaves, (per_seq + 7) / 8);
+}
+
+// heads per merge workgroup: the most that divides Hq within kMergeWaves waves
+static int merge_heads(int Hq, int nw) {
+  for (int nh = kMergeWaves / nw; nh > 1; nh /= 2)
+    if (Hq % nh == 0) return nh;
+  return 1;
 }
 
 template <int D>
@@ -715,15 +726,30 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
   constexpr int CHUNK = 8;
   __shared__ float s_ml[kMergeWaves][2];
   __shared__ float s_o[kMergeWaves][D];
-  const int hq = blockIdx.x, b = blockIdx.y;
+  const int nw = blockDim.x >> 6;
+  const int hq = blockIdx.x * blockDim.y + threadIdx.y, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = blockDim.x >> 6;
-  // every index this workgroup needs, loaded together (one memory round trip
-  // before the partials' own)
+  const int row_slot = threadIdx.y * nw;  // this head's LDS slots: row_slot .. row_slot + nw - 1
+  const bool prefix = p.prefix_len > 0;
+  // the prefix chunks' partials (at most kMaxPrefixChunks), loaded first
+  f32x2 mlc[kMaxPrefixChunks];
+  float oc[kMaxPrefixChunks][PER];
+  if (prefix && wave == 0) {
+    const f32x2* pml = (const f32x2*)p.ws_pre_ml;
+#pragma unroll
+    for (int c = 0; c < kMaxPrefixChunks; ++c) {
+      if (c < p.prefix_chunks) {
+        const int64_t slot = ((int64_t)c * p.B + b) * p.Hq + hq;
+        mlc[c] = pml[slot];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) oc[c][i] = p.ws_pre_o[slot * D + lane + 64 * i];
+      }
+    }
+  }
+  // every index this workgroup needs, loaded together
   const int64_t q_row = p.qsl[b], q_end = p.qsl[b + 1];
   const int32_t cb = p.ws_cum[b], ce = p.ws_cum[b + 1], units = p.ws_cum[p.B];
-  const bool prefix = p.prefix_len > 0;
   const bool has_units = ce > cb && units > 0;
   if (q_end == q_row || (!prefix && !has_units)) return;
   const Partition part(units, p.grid_parts);
@@ -739,28 +765,17 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
   if (prefix && wave == 0) {
-    // the prefix chunks' partials (at most kMaxPrefixChunks), all loads first
-    const f32x2* pml = (const f32x2*)p.ws_pre_ml;
-    f32x2 mlc[kMaxPrefixChunks];
-    float oc[kMaxPrefixChunks][PER];
+#pragma unroll
+    for (int c = 0; c < kMaxPrefixChunks; ++c)
+      if (c < p.prefix_chunks) M = fmaxf(M, mlc[c][0]);
 #pragma unroll
     for (int c = 0; c < kMaxPrefixChunks; ++c) {
-      const int64_t slot = ((int64_t)min(c, p.prefix_chunks - 1) * p.B + b) * p.Hq + hq;
-      mlc[c] = pml[slot];
+      if (c < p.prefix_chunks) {
+        const float f = __builtin_amdgcn_exp2f(mlc[c][0] - M);
+        l += f * mlc[c][1];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) oc[c][i] = p.ws_pre_o[slot * D + lane + 64 * i];
-    }
-#pragma unroll
-    for (int c = 0; c < kMaxPrefixChunks; ++c) {
-      mlc[c][0] = c < p.prefix_chunks ? mlc[c][0] : -INFINITY;
-      M = fmaxf(M, mlc[c][0]);
-    }
-#pragma unroll
-    for (int c = 0; c < kMaxPrefixChunks; ++c) {
-      const float f = __builtin_amdgcn_exp2f(mlc[c][0] - M);
-      l += f * mlc[c][1];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) o[i] += f * oc[c][i];
+        for (int i = 0; i < PER; ++i) o[i] += f * oc[c][i];
+      }
     }
   }
   for (int32_t w0 = wa + wave * CHUNK; w0 <= wz; w0 += nw * CHUNK) {
@@ -797,26 +812,28 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
     M = Mc;
   }
   if (nw > 1) {
-    // combine the waves' (M, l, O); a wave that took no partial has M = -inf,
-    // l = 0, O = 0 and weight 0 (wave 0 holds at least one live partial)
+    // combine the head's waves' (M, l, O); a wave that took no partial has
+    // M = -inf, l = 0, O = 0 and weight 0 (wave 0 holds at least one live
+    // partial)
     if (lane == 0) {
-      s_ml[wave][0] = M;
-      s_ml[wave][1] = l;
+      s_ml[row_slot + wave][0] = M;
+      s_ml[row_slot + wave][1] = l;
     }
 #pragma unroll
-    for (int i = 0; i < PER; ++i) s_o[wave][lane + 64 * i] = o[i];
+    for (int i = 0; i < PER; ++i) s_o[row_slot + wave][lane + 64 * i] = o[i];
     __syncthreads();
     if (wave != 0) return;
     float Mt = -INFINITY;
-    for (int k = 0; k < nw; ++k) Mt = fmaxf(Mt, s_ml[k][0]);
+    for (int k = 0; k < nw; ++k) Mt = fmaxf(Mt, s_ml[row_slot + k][0]);
     float lt = 0.f, ot[PER];
 #pragma unroll
     for (int i = 0; i < PER; ++i) ot[i] = 0.f;
     for (int k = 0; k < nw; ++k) {
-      const float f = s_ml[k][0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s_ml[k][0] - Mt);
-      lt += f * s_ml[k][1];
+      const float m_k = s_ml[row_slot + k][0];
+      const float f = m_k == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_k - Mt);
+      lt += f * s_ml[row_slot + k][1];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) ot[i] += f * s_o[k][lane + 64 * i];
+      for (int i = 0; i < PER; ++i) ot[i] += f * s_o[row_slot + k][lane + 64 * i];
     }
     l = lt;
 #pragma unroll
@@ -874,26 +891,52 @@ bool decode_can_fuse_write(const AttnParams& p, int64_t n_new, int64_t row_bytes
   return rows_per_wg * (row_bytes / 16) <= kCopyRegs * threads;
 }
 
+// With a shared prefix the prefix items and the split-K pass run at the same
+// time: the decode grid (sized for part of the CUs) on the call's stream, the
+// prefix rounds, prefix_wgs workgroups each, on the side stream.  The decode
+// is enqueued first, so that the host's time to enqueue the prefix rounds
+// overlaps it; the fork event is recorded before it, so the prefix waits only
+// for the work enqueued before the call.  At D = 128 a workgroup of either
+// kernel leaves too little LDS on its CU for one of the other, so the two
+// grids keep to disjoint CUs whichever is dispatched first.  The merge waits
+// for both.
 template <int ESZ, int D>
-static void launch_decode_t(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
+static hipError_t launch_decode_t(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev,
+                                  const SideStream* side) {
   const int R = decode_groups(p.Hkv);
   const int threads = 64 * decode_waves(p.Hkv) * R;
-  if (p.prefix_len > 0) (void)launch_prefix_partials(p, stream);
+  const bool fork = p.prefix_len > 0 && side;
+  if (fork) {
+    const hipError_t e = hipEventRecord(side->fork, stream);
+    if (e != hipSuccess) return e;
+  } else if (p.prefix_len > 0) {
+    (void)launch_prefix_partials(p, stream, false);
+  }
   if (ev.begin) (void)hipEventRecord(ev.begin, stream);
   hipLaunchKernelGGL((decode_kernel<ESZ, D>), dim3((unsigned)(p.grid_parts / R)), dim3(threads), 0, stream, p);
   if (ev.end) (void)hipEventRecord(ev.end, stream);
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)p.Hq, (unsigned)p.B), dim3(64 * merge_waves(p.grid_parts, p.B)), 0, stream, p);
+  if (fork) {
+    hipError_t e = hipStreamWaitEvent(side->stream, side->fork, 0);
+    if (e == hipSuccess) e = launch_prefix_partials(p, side->stream, true);
+    if (e == hipSuccess) e = hipEventRecord(side->join, side->stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
+    if (e != hipSuccess) return e;
+  }
+  const int nw = merge_waves(p.grid_parts, p.B), nh = merge_heads(p.Hq, nw);
+  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)(p.Hq / nh), (unsigned)p.B), dim3(64 * nw, nh), 0, stream, p);
+  return hipSuccess;
 }
 
-hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
+hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev, const SideStream* side) {
   if (p.B == 0) return hipSuccess;
   const bool fp8 = p.kv_type == KV_FP8;
+  hipError_t e;
   if (p.D == 128) {
-    if (fp8) launch_decode_t<1, 128>(p, stream, ev); else launch_decode_t<2, 128>(p, stream, ev);
+    e = fp8 ? launch_decode_t<1, 128>(p, stream, ev, side) : launch_decode_t<2, 128>(p, stream, ev, side);
   } else {
-    if (fp8) launch_decode_t<1, 64>(p, stream, ev); else launch_decode_t<2, 64>(p, stream, ev);
+    e = fp8 ? launch_decode_t<1, 64>(p, stream, ev, side) : launch_decode_t<2, 64>(p, stream, ev, side);
   }
-  return hipGetLastError();
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace pkv

@@ -71,6 +71,10 @@ struct AttnParams {
   // groups of sequences) x (prefix_chunks chunks of prefix_chunk_len keys)
   int64_t prefix_len;  // 0 = off; a multiple of 32
   int prefix_tiles, prefix_chunks, prefix_chunk_len;
+  // the prefix items run in rounds of prefix_wgs workgroups (a multiple of
+  // Hkv), beside the decode grid on the other CUs; a round's workgroup w runs
+  // item prefix_rank0 + w / Hkv of KV head w % Hkv
+  int prefix_wgs, prefix_rank0;
   float* ws_pre_ml;    // [prefix_chunks, B, Hq, 2] partial (max in log2 units, sum)
   float* ws_pre_o;     // [prefix_chunks, B, Hq, D] unnormalised partial outputs
   // decode fused with the write (n_new > 0, n_new = T: the new rows are the
@@ -91,12 +95,27 @@ struct LaunchEvents {
   hipEvent_t end = nullptr;
 };
 
+// A second stream on the device of a call's stream, and the two events that
+// fork work onto it and join it back (created once per device).
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr;
+  hipEvent_t join = nullptr;
+};
+
 hipError_t launch_write(const WriteParams& p, hipStream_t stream);
 hipError_t launch_write_fp8(const WriteFp8Params& p, hipStream_t stream);
-hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
+// A shared-prefix decode (prefix_len > 0) forks its prefix items onto
+// side->stream and joins them before the merge; with side NULL every kernel
+// runs on `stream`, one after the other.
+hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev,
+                         const SideStream* side = nullptr);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
-hipError_t launch_prefix_partials(const AttnParams& p, hipStream_t stream);
+// the prefix items in rounds of prefix_wgs workgroups (`rounds`), or all in
+// one launch
+hipError_t launch_prefix_partials(const AttnParams& p, hipStream_t stream, bool rounds);
+
 hipError_t launch_csr_to_block_table(const int64_t* indptr, const int64_t* indices, const int64_t* last_len,
                                      int64_t nnz, int64_t B, int64_t max_blocks, int64_t page_size,
                                      int64_t pad_page, int64_t* block_table, int64_t* seq_lens,
@@ -121,8 +140,12 @@ size_t prefill_workspace_bytes(const AttnParams& p);
 void prefill_workspace_carve(AttnParams& p, void* workspace);
 constexpr int kMaxPrefixChunks = 8;
 // groups of decode sequences, chunks and chunk length of a shared prefix of
-// prefix_len positions (fills p.prefix_*), and the partials' workspace bytes
-size_t prefix_plan(AttnParams& p, int64_t prefix_len);
+// prefix_len positions, and the workgroups its items run on beside the
+// decode, a share of the n_cu CUs (fills p.prefix_*; n_cu = 0 when the device
+// is not known).  Returns the partials' workspace bytes: for the planned
+// chunks when `tight`, else for the most chunks any plan can choose,
+// min(kMaxPrefixChunks, prefix_len / 32) (a size that fits any device).
+size_t prefix_plan(AttnParams& p, int64_t prefix_len, int n_cu, bool tight);
 void prefix_workspace_carve(AttnParams& p, void* region);
 int prefill_tokens_per_tile(int G);
 

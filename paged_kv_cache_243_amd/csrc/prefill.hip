@@ -433,7 +433,8 @@ void prefill_kernel(AttnParams p) {
   __shared__ __attribute__((aligned(16))) char sv[NS][TB];
   __shared__ __attribute__((aligned(16))) char sc[ESZ == 1 ? 2 : 1][4][ESZ == 1 ? kKeyTile * D : 16];
 
-  const int rank = (int)(blockIdx.x / (unsigned)p.Hkv), h = (int)(blockIdx.x % (unsigned)p.Hkv);
+  const int rank = (PREFIX ? p.prefix_rank0 : 0) + (int)(blockIdx.x / (unsigned)p.Hkv);
+  const int h = (int)(blockIdx.x % (unsigned)p.Hkv);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
@@ -1084,17 +1085,81 @@ __global__ __launch_bounds__(256) void prefill_split_merge_kernel(AttnParams p) 
 // sequences, chunk of the prefix).  The chunk count is chosen for about 256
 // workgroups whatever the device, so the workspace size depends on the shapes
 // only.
-size_t prefix_plan(AttnParams& p, int64_t prefix_len) {
+// Shared-prefix schedule.  The prefix items (group of sequences x chunk of
+// the prefix x KV head) run on prefix_wgs CUs while the decode of the
+// private positions streams on the rest.  The two are bound by different
+// units: the items by their MFMAs and exps, the decode by HBM, which a
+// streaming read keeps nearly as busy from 5/8 of the CUs as from all of them
+// (a plain read of the decode workloads' pages loses under 5 % there, and
+// 15 % from half of them).  The items run in rounds of prefix_wgs
+// workgroups, a whole number per KV head, so that workgroup w always serves
+// KV head w % Hkv (its K/V re-reads stay in one L2).
+//
+// The split comes from a model of the two times, with rates measured on
+// MI355X: an item costs (its 32-key tiles + kPrefixItemTiles) x kPrefixTileNs
+// (the fixed part is its start-up and the write-back of its partials), and
+// the decode streams at kCuStreamBytesPerNs per CU up to kHbmStreamBytesPerNs
+// in all, over an estimate of the private positions (half of what the block
+// table can hold past the prefix, as seq_lens stays on the device).  For each
+// number of items per head the chunk count with the fewest estimated tiles
+// is taken (ties: fewer chunks, fewer partials to merge), then the number
+// whose slower side is fastest; the decode keeps at least a quarter of the
+// CUs.
+constexpr int kPrefixItemTiles = 13;
+constexpr double kPrefixTileNs = 950.0;      // one 32-key tile of a 256-row item, D = 128
+constexpr double kCuStreamBytesPerNs = 37.5;
+constexpr double kHbmStreamBytesPerNs = 5600.0;
+
+// chunk count and estimated tiles of the prefix items at per_head workgroups per KV head
+static void prefix_chunking(int64_t n_tiles, int64_t groups, int64_t per_head, int64_t& chunks_out,
+                            int64_t& cost_out) {
+  const int64_t max_chunks = std::max<int64_t>(1, std::min<int64_t>(kMaxPrefixChunks, n_tiles));
+  chunks_out = 1;
+  cost_out = INT64_MAX;
+  for (int64_t c = 1; c <= max_chunks; ++c) {
+    const int64_t len = (n_tiles + c - 1) / c;  // tiles per chunk
+    if ((n_tiles + len - 1) / len != c) continue;  // the same cut as a smaller count
+    const int64_t rounds = (groups * c + per_head - 1) / per_head;
+    const int64_t cost = rounds * (len + kPrefixItemTiles);
+    if (cost < cost_out) {
+      chunks_out = c;
+      cost_out = cost;
+    }
+  }
+}
+
+size_t prefix_plan(AttnParams& p, int64_t prefix_len, int n_cu, bool tight) {
   const int tpt = prefill_tokens_per_tile(p.G);
   p.prefix_len = prefix_len;
   p.prefix_tiles = (int)((p.B + tpt - 1) / tpt);
-  const int64_t per_chunk = (int64_t)p.prefix_tiles * p.Hkv;
-  int64_t chunks = (256 + per_chunk - 1) / per_chunk;
-  chunks = std::max<int64_t>(1, std::min<int64_t>({chunks, (int64_t)kMaxPrefixChunks, prefix_len / kKeyTile}));
-  const int64_t len = (prefix_len / chunks + kKeyTile - 1) / kKeyTile * kKeyTile;
+  p.prefix_rank0 = 0;
+  const int64_t n_tiles = prefix_len / kKeyTile;
+  const double private_bytes = (double)p.B * std::max<int64_t>(0, p.max_blocks * 16 - prefix_len) / 2 * p.Hkv *
+                               p.D * std::max(p.kv_bytes, 1) * 2;
+  const double tile_ns = kPrefixTileNs * p.D / 128;
+  const int64_t max_per_head = std::max<int64_t>(1, ((int64_t)n_cu - n_cu / 4) / p.Hkv);
+  int64_t per_head = 1, chunks = 1, cost = 0;
+  double best = INFINITY;
+  for (int64_t k = 1; k <= max_per_head; ++k) {
+    int64_t c, tiles;
+    prefix_chunking(n_tiles, p.prefix_tiles, k, c, tiles);
+    const double cus = std::max<double>(1.0, (double)n_cu - (double)k * p.Hkv);
+    const double t_dec = private_bytes / std::min(cus * kCuStreamBytesPerNs, kHbmStreamBytesPerNs);
+    const double t = std::max(t_dec, tiles * tile_ns);
+    if (t < best) {
+      best = t;
+      per_head = k;
+      chunks = c;
+      cost = tiles;
+    }
+  }
+  (void)cost;
+  p.prefix_wgs = (int)(per_head * p.Hkv);
+  const int64_t len = (n_tiles + chunks - 1) / chunks * kKeyTile;
   p.prefix_chunk_len = (int)len;
   p.prefix_chunks = (int)((prefix_len + len - 1) / len);
-  const size_t slots = (size_t)p.prefix_chunks * p.B * p.Hq;
+  const int64_t max_chunks = std::max<int64_t>(1, std::min<int64_t>(kMaxPrefixChunks, n_tiles));
+  const size_t slots = (size_t)(tight ? p.prefix_chunks : max_chunks) * p.B * p.Hq;
   return (slots * 2 * sizeof(float) + 255) / 256 * 256 + slots * p.D * sizeof(float);
 }
 
@@ -1104,19 +1169,29 @@ void prefix_workspace_carve(AttnParams& p, void* region) {
   p.ws_pre_o = (float*)((char*)region + (slots * 2 * sizeof(float) + 255) / 256 * 256);
 }
 
-hipError_t launch_prefix_partials(const AttnParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((int64_t)p.prefix_tiles * p.prefix_chunks * p.Hkv));
+// The prefix items, prefix_wgs / Hkv of them per KV head and round, one
+// launch per round (or all of them in one launch).
+hipError_t launch_prefix_partials(const AttnParams& p, hipStream_t stream, bool rounds) {
+  const int items = p.prefix_tiles * p.prefix_chunks;
+  const int per_head = rounds ? p.prefix_wgs / p.Hkv : items;
   constexpr int NB = kPrefillRowBlocks;
   const dim3 block(512 / NB);
   const bool fp8 = p.kv_type == KV_FP8;
-  if (p.D == 128) {
-    if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 128, NB, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_kernel<2, 128, NB, true>), grid, block, 0, stream, p);
-  } else {
-    if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 64, NB, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((prefill_kernel<2, 64, NB, true>), grid, block, 0, stream, p);
+  for (int r0 = 0; r0 < items; r0 += per_head) {
+    AttnParams q = p;
+    q.prefix_rank0 = r0;
+    const dim3 grid((unsigned)((int64_t)std::min(per_head, items - r0) * p.Hkv));
+    if (p.D == 128) {
+      if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 128, NB, true>), grid, block, 0, stream, q);
+      else hipLaunchKernelGGL((prefill_kernel<2, 128, NB, true>), grid, block, 0, stream, q);
+    } else {
+      if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 64, NB, true>), grid, block, 0, stream, q);
+      else hipLaunchKernelGGL((prefill_kernel<2, 64, NB, true>), grid, block, 0, stream, q);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {

@@ -327,10 +327,9 @@ def test_shared_prefix_argument_errors(pages, max_q, status):
 
 def test_shared_prefix_workspace_size():
     """decode workspace plus the prefix partials: chunks x B x Hq slots of
-    (m, l) and D floats; 64 decode rows of G = 4 make one group of 64
-    sequences, 8 KV heads -> 8 workgroups per chunk, so 32 chunks are wanted
-    for 256 workgroups, capped by the 2 chunks of 32 positions a 4-page prefix
-    holds."""
+    (m, l) and D floats, sized (without a device) for the most chunks a plan
+    can choose: at most 8, and at most one per 32 prefix positions, so 2 for
+    a 4-page prefix and 8 for a 128-page one."""
     lib = pkv.load()
     q, kp = T([64, 32, 128], B.PKV_BF16), T([65536, 16, 8, 128], B.PKV_BF16)
     bt = T([64, 256], B.PKV_I64)
@@ -341,7 +340,7 @@ def test_shared_prefix_workspace_size():
     with_prefix = lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt), ctypes.byref(o))
     slots = 2 * 64 * 32
     assert with_prefix - base == (slots * 8 + 255) // 256 * 256 + slots * 128 * 4
-    # a 128-page prefix: min(32 wanted, 8 cap, 64 units) = 8 chunks of 256 positions
+    # a 128-page prefix: min(8 cap, 64 units) = 8 chunks
     o.shared_prefix_pages = 128
     big = lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt), ctypes.byref(o))
     slots = 8 * 64 * 32
