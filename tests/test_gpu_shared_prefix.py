@@ -51,6 +51,29 @@ def test_shared_prefix_single_kv_head(gpu, split):
     assert_close(out, ref, "bf16", f"shared prefix one KV head split={split}")
 
 
+def test_shared_prefix_in_rounds_head_dim_64(gpu):
+    """1024 sequences, 32 KV heads, head_dim 64: 8 groups of sequences per KV
+    head against at most 6 prefix workgroups per KV head beside the decode, so
+    the prefix items run in several rounds; at head_dim 64 a decode and a
+    prefix workgroup also fit on one CU together.  Every row against the
+    oracle, and the allocation-free form (the same plan on one stream, in one
+    launch) gives the same bits."""
+    cfg = dataclasses.replace(W.SMALL[4], name="shared-prefix-rounds-d64", batch=1024, hq=64, hkv=32, head_dim=64,
+                              num_pages=3300, old_max=40, shared_prefix_tokens=128)
+    note(f"shared prefix in rounds {cfg.name}")
+    w = W.generate(cfg, DEV)
+    kp, vp = gpu_write(gpu, w)
+    pages = cfg.shared_prefix_tokens // 16
+    out = attend_shared(gpu, w, kp, vp, pages)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, "bf16", cfg.name)
+    got = torch.full_like(w.q, float("nan"))
+    gpu.paged_attention_noalloc(w.q, kp, vp, w.block_table, w.seq_lens, w.query_start_loc, w.scale, got,
+                                max_query_len=1, shared_prefix_pages=pages)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().view(torch.int16).numpy(), out.cpu().view(torch.int16).numpy())
+
+
 def test_shared_prefix_full(gpu):
     """256 sequences on 128 shared pages, in the launch configuration the
     benchmark times; every row against the oracle."""
