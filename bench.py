@@ -799,8 +799,8 @@ def main(argv=None) -> int:
         a4p = statistics.median(t4p.attn)
         extra["shared_prefix_decode"] = {
             "workload": "256 sequences sharing 128 prefix pages + U{0..512} private tokens, Hq 64, Hkv 8",
-            "form": f"shared_prefix_pages={pages4}: the prefix once as MFMA tiles on a second stream, beside the "
-                    f"split-K decode of the private positions on the other CUs, then the merge",
+            "form": f"shared_prefix_pages={pages4}: one launch whose first workgroups run the split-K decode of the "
+                    f"private positions and the rest the prefix once as MFMA tiles, then the merge",
             "unit": "GB/s",
             "logical_GBps": round(decode_bytes(w4) / (a4 * 1e-3) / 1e9, 1),
             "unique_GBps": round(unique_decode_bytes(w4) / (a4 * 1e-3) / 1e9, 1),

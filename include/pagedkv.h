@@ -120,12 +120,8 @@ typedef struct {
                              tiles (all query rows of a group of sequences against the
                              prefix keys) and is merged with the split-K decode of each
                              sequence's own positions; the result is the same attention.
-                             paged_attention runs the prefix tiles on a second stream of
-                             the library's own (one per device, default priority, created
-                             by the first such call), beside the decode on part of the CUs,
-                             joined back to `stream` by events before the merge; nothing
-                             else runs on that stream.  paged_attention_noalloc runs the
-                             same kernels one after the other on `stream`.
+                             The prefix tiles and the split-K decode of the private
+                             positions run as one launch, on disjoint sets of CUs.
                              Must be even (32-position units) and <= max_blocks; 0 = off.
                              A statement that does not hold gives unspecified output. */
 } pkv_attn_opts;

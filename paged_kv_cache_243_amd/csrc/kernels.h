@@ -71,10 +71,10 @@ struct AttnParams {
   // groups of sequences) x (prefix_chunks chunks of prefix_chunk_len keys)
   int64_t prefix_len;  // 0 = off; a multiple of 32
   int prefix_tiles, prefix_chunks, prefix_chunk_len;
-  // the prefix items run in rounds of prefix_wgs workgroups (a multiple of
-  // Hkv), beside the decode grid on the other CUs; a round's workgroup w runs
-  // item prefix_rank0 + w / Hkv of KV head w % Hkv
-  int prefix_wgs, prefix_rank0;
+  // the prefix items run on prefix_wgs workgroups (a multiple of Hkv) beside
+  // the decode grid, workgroup w taking items w / Hkv, w / Hkv + prefix_wgs /
+  // Hkv, ... of KV head w % Hkv
+  int prefix_wgs;
   float* ws_pre_ml;    // [prefix_chunks, B, Hq, 2] partial (max in log2 units, sum)
   float* ws_pre_o;     // [prefix_chunks, B, Hq, D] unnormalised partial outputs
   // decode fused with the write (n_new > 0, n_new = T: the new rows are the
@@ -95,26 +95,14 @@ struct LaunchEvents {
   hipEvent_t end = nullptr;
 };
 
-// A second stream on the device of a call's stream, and the two events that
-// fork work onto it and join it back (created once per device).
-struct SideStream {
-  hipStream_t stream = nullptr;
-  hipEvent_t fork = nullptr;
-  hipEvent_t join = nullptr;
-};
-
 hipError_t launch_write(const WriteParams& p, hipStream_t stream);
 hipError_t launch_write_fp8(const WriteFp8Params& p, hipStream_t stream);
-// A shared-prefix decode (prefix_len > 0) forks its prefix items onto
-// side->stream and joins them before the merge; with side NULL every kernel
-// runs on `stream`, one after the other.
-hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev,
-                         const SideStream* side = nullptr);
+// (a shared-prefix decode, prefix_len > 0, runs its prefix items and the
+// split-K pass as one launch of shared_prefix_decode_kernel, then the merge)
+hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
-// the prefix items in rounds of prefix_wgs workgroups (`rounds`), or all in
-// one launch
-hipError_t launch_prefix_partials(const AttnParams& p, hipStream_t stream, bool rounds);
+hipError_t launch_shared_prefix_decode(const AttnParams& p, hipStream_t stream);
 
 hipError_t launch_csr_to_block_table(const int64_t* indptr, const int64_t* indices, const int64_t* last_len,
                                      int64_t nnz, int64_t B, int64_t max_blocks, int64_t page_size,

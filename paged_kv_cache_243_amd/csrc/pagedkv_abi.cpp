@@ -8,7 +8,6 @@
 #include <string.h>
 
 #include <algorithm>
-#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -94,53 +93,17 @@ int device_cu_count(int dev) {
   return cached[dev];
 }
 
-// The side stream of device `dev` for the shared-prefix decode, created on
-// first use (non-blocking, default priority, events without timing), and the
-// lock a call holds from the fork to the join, so that concurrent calls do
-// not interleave their records of the same two events.  NULL if it cannot be
-// created.
-struct SideSlot {
-  std::mutex lock;
-  pkv::SideStream side;
-  bool tried = false;
-  bool ok = false;
-};
-
-SideSlot* side_slot(int dev) {
-  static SideSlot slots[kMaxDevices];
-  static std::mutex create_lock;
-  if (dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideSlot& s = slots[dev];
-  std::lock_guard<std::mutex> g(create_lock);
-  if (!s.tried) {
-    s.tried = true;
-    int prev = -1;
-    if (hipGetDevice(&prev) != hipSuccess) return nullptr;
-    bool ok = hipSetDevice(dev) == hipSuccess;
-    ok = ok && hipStreamCreateWithFlags(&s.side.stream, hipStreamNonBlocking) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&s.side.fork, hipEventDisableTiming) == hipSuccess;
-    ok = ok && hipEventCreateWithFlags(&s.side.join, hipEventDisableTiming) == hipSuccess;
-    (void)hipSetDevice(prev);
-    s.ok = ok;
-  }
-  return s.ok ? &s : nullptr;
-}
-
 struct AttnPlan {
   AttnParams p;
   enum { kNone, kF32, kDecode, kPrefill } kernel;
   size_t workspace;
   int slot_parts;  // decode: partition ranges the partial slots are sized for
-  bool fork_prefix;  // shared-prefix decode: prefix items on the side stream, beside the decode
 };
 
 // Validates the attention arguments and fills the launch plan (no HIP calls).
 // n_cu > 0 fixes the decode grid for a device of that many CUs (0: a size
 // query, no grid); `tight` sizes the decode partials for that grid instead of
-// for any device.  A shared-prefix decode is planned for its prefix items on a
-// second stream beside the decode grid; `tight` (the allocation-free form,
-// which creates no stream) launches the same plan on the call's stream alone,
-// one kernel after the other, so both forms give the same bits.
+// for any device.
 int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_tensor* value_pool,
                    const pkv_tensor* block_table, const pkv_tensor* seq_lens,
                    const pkv_tensor* query_start_loc, float scale, const pkv_tensor* out,
@@ -235,7 +198,6 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
   p.max_query_len = (int)std::min<int64_t>(max_q, INT32_MAX);
 
   plan.workspace = 0;
-  plan.fork_prefix = false;
   if (T == 0 || B == 0) {
     plan.kernel = AttnPlan::kNone;
   } else if (kv == PKV_F32) {
@@ -251,7 +213,6 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
     size_t prefix_bytes = 0;
     int decode_cu = n_cu;
     if (shared_pages > 0) {
-      plan.fork_prefix = !tight;
       prefix_bytes = pkv::prefix_plan(p, shared_pages * kPageSize, n_cu, tight);
       if (n_cu > 0) decode_cu = std::max(n_cu - p.prefix_wgs, n_cu / 4);
     }
@@ -289,17 +250,9 @@ int launch_attention(AttnPlan& plan, void* ws, const pkv_attn_opts* opts, hipStr
       break;
     case AttnPlan::kDecode:
       pkv::decode_workspace_carve(p, ws, plan.slot_parts);
-      if (p.prefix_len > 0 && plan.fork_prefix) {
+      if (p.prefix_len > 0)
         pkv::prefix_workspace_carve(p, (char*)ws + pkv::decode_workspace_bytes(p.B, p.Hq, p.D, plan.slot_parts));
-        SideSlot* slot = side_slot(stream_device(s));
-        if (slot == nullptr) return PKV_ERR_HIP;
-        std::lock_guard<std::mutex> g(slot->lock);
-        err = pkv::launch_decode(p, s, ev, &slot->side);
-      } else {
-        if (p.prefix_len > 0)
-          pkv::prefix_workspace_carve(p, (char*)ws + pkv::decode_workspace_bytes(p.B, p.Hq, p.D, plan.slot_parts));
-        err = pkv::launch_decode(p, s, ev);
-      }
+      err = pkv::launch_decode(p, s, ev);
       break;
     case AttnPlan::kPrefill:
       pkv::prefill_workspace_carve(p, ws);

@@ -49,10 +49,12 @@
 #include <math.h>
 
 #include <algorithm>
+#include <numeric>
 
 #include <type_traits>
 
 #include "common.h"
+#include "decode_device.h"
 #include "kernels.h"
 
 namespace pkv {
@@ -410,14 +412,28 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | N);
 }
 
-// PREFIX: the shared-prefix form of decode (see launch_prefix_partials).  An
+// PREFIX: the shared-prefix form of decode (see shared_prefix_decode_kernel).  An
 // item is then (group of decode sequences, chunk of the shared prefix): its
 // rows are the query rows of tpt consecutive sequences, its keys the chunk's
 // positions of the prefix pages every block_table row starts with, and it
 // writes an unnormalised partial (m, l, O) per row instead of the output.
-template <int ESZ, int D, int NB, bool PREFIX = false>
-__global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
-void prefill_kernel(AttnParams p) {
+// LDS of one prefill workgroup: the bf16 K and V rings and (fp8 pools) the
+// code slots
+template <int ESZ, int D>
+struct PrefillLds {
+  static constexpr int NS = ESZ == 2 ? 6 : 4;
+  static constexpr int TB = kKeyTile * D * 2;
+  alignas(16) char sk[NS][TB];
+  alignas(16) char sv[NS][TB];
+  alignas(16) char sc[ESZ == 1 ? 2 : 1][4][ESZ == 1 ? kKeyTile * D : 16];
+};
+
+// One work item, run by workgroup `block`: item rank0 + block / Hkv of KV
+// head block % Hkv (prefill_kernel: rank0 = 0, or the round's first item in
+// the PREFIX form; the shared-prefix kernel loops its workgroups over rounds).
+template <int ESZ, int D, int NB, bool PREFIX>
+__device__ __forceinline__ void prefill_item(const AttnParams& p, PrefillLds<ESZ, D>& lds, const unsigned block,
+                                             const int rank0) {
   constexpr int WAVES = 8 / NB;            // 32 NB query rows per wave, 256 per workgroup
   constexpr int THREADS = 64 * WAVES;
   constexpr int NKS = D / 16;              // score MFMA k-steps
@@ -429,12 +445,12 @@ void prefill_kernel(AttnParams p) {
   constexpr int NS = ESZ == 2 ? 6 : 4;
   constexpr int TB = kKeyTile * D * 2;     // bytes per LDS tile
   using TL = TileLayout<D>;
-  __shared__ __attribute__((aligned(16))) char sk[NS][TB];
-  __shared__ __attribute__((aligned(16))) char sv[NS][TB];
-  __shared__ __attribute__((aligned(16))) char sc[ESZ == 1 ? 2 : 1][4][ESZ == 1 ? kKeyTile * D : 16];
+  auto& sk = lds.sk;
+  auto& sv = lds.sv;
+  auto& sc = lds.sc;
 
-  const int rank = (PREFIX ? p.prefix_rank0 : 0) + (int)(blockIdx.x / (unsigned)p.Hkv);
-  const int h = (int)(blockIdx.x % (unsigned)p.Hkv);
+  const int rank = rank0 + (int)(block / (unsigned)p.Hkv);
+  const int h = (int)(block % (unsigned)p.Hkv);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G;
@@ -1016,6 +1032,49 @@ void prefill_kernel(AttnParams p) {
   }
 }
 
+template <int ESZ, int D, int NB>
+__global__ __launch_bounds__(512 / NB) __attribute__((amdgpu_waves_per_eu(3 - NB, 3 - NB)))
+void prefill_kernel(AttnParams p) {
+  __shared__ PrefillLds<ESZ, D> lds;
+  prefill_item<ESZ, D, NB, false>(p, lds, blockIdx.x, 0);
+}
+
+// Shared-prefix decode in one launch.  Workgroups 0 .. n_dec - 1 run the
+// split-K pass over the positions past the prefix (n_dec = grid_parts /
+// parts per workgroup), the next prefix_wgs workgroups the prefix items:
+// workgroup j takes items j / Hkv, j / Hkv + per_head, ... of KV head
+// j % Hkv, per_head = prefix_wgs / Hkv.  The two kinds are bound by different
+// units (HBM; MFMA and exp) and start together, so the prefix's tiles run
+// while the private positions stream.  n_dec and prefix_wgs are multiples of
+// 8 and workgroups are dealt to the 8 XCDs in turn, so a prefix workgroup and
+// its KV head keep to one XCD (the items of a head re-read its K/V from that
+// XCD's L2).  Every workgroup has 8 waves: a decode workgroup whose groups
+// use fewer leaves the others idle after the length scan.
+template <int ESZ, int D>
+union SharedPrefixLds {
+  dk::DecodeLds<D> dec;
+  PrefillLds<ESZ, D> pre;
+};
+
+template <int ESZ, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void shared_prefix_decode_kernel(AttnParams p) {
+  __shared__ SharedPrefixLds<ESZ, D> lds;
+  const unsigned n_dec = (unsigned)(p.grid_parts / dk::decode_groups(p.Hkv));
+  if (blockIdx.x < n_dec) {
+    dk::decode_body<ESZ, D>(p, lds.dec, blockIdx.x, n_dec);
+    return;
+  }
+  const unsigned j = blockIdx.x - n_dec;
+  const int per_head = p.prefix_wgs / p.Hkv;
+  const int items = p.prefix_tiles * p.prefix_chunks;
+  static_assert(kPrefillRowBlocks == 1, "prefix items run as 8 waves of 32 rows, like the decode workgroups");
+  for (int r0 = 0; r0 < items; r0 += per_head) {
+    if (r0 > 0) __syncthreads();  // every wave is done with the last item's tiles
+    prefill_item<ESZ, D, 1, true>(p, lds.pre, j, r0);
+  }
+}
+
 // Key-split prefill: combine the chunks' partials of every row of a split
 // (sequence, query tile, KV head) with a log-sum-exp merge,
 //   M = max_c m_c,  out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,
@@ -1085,30 +1144,30 @@ __global__ __launch_bounds__(256) void prefill_split_merge_kernel(AttnParams p) 
 // sequences, chunk of the prefix).  The chunk count is chosen for about 256
 // workgroups whatever the device, so the workspace size depends on the shapes
 // only.
-// Shared-prefix schedule.  The prefix items (group of sequences x chunk of
-// the prefix x KV head) run on prefix_wgs CUs while the decode of the
-// private positions streams on the rest.  The two are bound by different
-// units: the items by their MFMAs and exps, the decode by HBM, which a
-// streaming read keeps nearly as busy from 5/8 of the CUs as from all of them
-// (a plain read of the decode workloads' pages loses under 5 % there, and
-// 15 % from half of them).  The items run in rounds of prefix_wgs
-// workgroups, a whole number per KV head, so that workgroup w always serves
-// KV head w % Hkv (its K/V re-reads stay in one L2).
+// Shared-prefix schedule (shared_prefix_decode_kernel).  The prefix items
+// (group of sequences x chunk of the prefix x KV head) run on prefix_wgs
+// workgroups while the decode of the private positions streams on the rest
+// of the CUs.  The two are bound by different units: the items by their
+// MFMAs and exps, the decode by the loads each CU keeps in flight.
 //
-// The split comes from a model of the two times, with rates measured on
-// MI355X: an item costs (its 32-key tiles + kPrefixItemTiles) x kPrefixTileNs
-// (the fixed part is its start-up and the write-back of its partials), and
-// the decode streams at kCuStreamBytesPerNs per CU up to kHbmStreamBytesPerNs
-// in all, over an estimate of the private positions (half of what the block
-// table can hold past the prefix, as seq_lens stays on the device).  For each
-// number of items per head the chunk count with the fewest estimated tiles
-// is taken (ties: fewer chunks, fewer partials to merge), then the number
-// whose slower side is fastest; the decode keeps at least a quarter of the
-// CUs.
+// The split comes from a model fitted to measurements on MI355X:
+//  * an item costs (its 32-key tiles + kPrefixItemTiles) x kPrefixTileNs (the
+//    fixed part is its start-up and the write-back of its partials);
+//  * the decode streams an estimate of the private bytes (half of what the
+//    block table holds past the prefix, as seq_lens stays on the device) at
+//    kDecodeBytesPerNs x n / (n + kDecodeHalfCus) on n CUs: each CU's rate
+//    rises as fewer CUs share HBM;
+//  * the merge then reads each prefix chunk's partials at kMergeBytesPerNs.
+// For each number of items per head (a multiple of 8 / gcd(Hkv, 8), so that
+// the decode part keeps a multiple of 8 workgroups) the chunk count with the
+// fewest estimated tiles is taken (ties: fewer chunks), then the number with
+// the least estimated time, max(decode, items) + merge (ties: fewer prefix
+// workgroups); the decode keeps at least a quarter of the CUs.
 constexpr int kPrefixItemTiles = 13;
 constexpr double kPrefixTileNs = 950.0;      // one 32-key tile of a 256-row item, D = 128
-constexpr double kCuStreamBytesPerNs = 37.5;
-constexpr double kHbmStreamBytesPerNs = 5600.0;
+constexpr double kDecodeBytesPerNs = 5600.0;
+constexpr double kDecodeHalfCus = 75.0;
+constexpr double kMergeBytesPerNs = 3000.0;
 
 // chunk count and estimated tiles of the prefix items at per_head workgroups per KV head
 static void prefix_chunking(int64_t n_tiles, int64_t groups, int64_t per_head, int64_t& chunks_out,
@@ -1132,28 +1191,27 @@ size_t prefix_plan(AttnParams& p, int64_t prefix_len, int n_cu, bool tight) {
   const int tpt = prefill_tokens_per_tile(p.G);
   p.prefix_len = prefix_len;
   p.prefix_tiles = (int)((p.B + tpt - 1) / tpt);
-  p.prefix_rank0 = 0;
   const int64_t n_tiles = prefix_len / kKeyTile;
   const double private_bytes = (double)p.B * std::max<int64_t>(0, p.max_blocks * 16 - prefix_len) / 2 * p.Hkv *
                                p.D * std::max(p.kv_bytes, 1) * 2;
   const double tile_ns = kPrefixTileNs * p.D / 128;
-  const int64_t max_per_head = std::max<int64_t>(1, ((int64_t)n_cu - n_cu / 4) / p.Hkv);
-  int64_t per_head = 1, chunks = 1, cost = 0;
+  const int64_t step = 8 / std::gcd<int64_t>(p.Hkv, 8);
+  const int64_t max_per_head = std::max<int64_t>(step, ((int64_t)n_cu - n_cu / 4) / p.Hkv / step * step);
+  int64_t per_head = step, chunks = 1;
   double best = INFINITY;
-  for (int64_t k = 1; k <= max_per_head; ++k) {
+  for (int64_t k = step; k <= max_per_head; k += step) {
     int64_t c, tiles;
     prefix_chunking(n_tiles, p.prefix_tiles, k, c, tiles);
     const double cus = std::max<double>(1.0, (double)n_cu - (double)k * p.Hkv);
-    const double t_dec = private_bytes / std::min(cus * kCuStreamBytesPerNs, kHbmStreamBytesPerNs);
-    const double t = std::max(t_dec, tiles * tile_ns);
+    const double t_dec = private_bytes * (cus + kDecodeHalfCus) / (kDecodeBytesPerNs * cus);
+    const double t_merge = (double)c * p.B * p.Hq * (p.D + 2) * sizeof(float) / kMergeBytesPerNs;
+    const double t = std::max(t_dec, tiles * tile_ns) + t_merge;
     if (t < best) {
       best = t;
       per_head = k;
       chunks = c;
-      cost = tiles;
     }
   }
-  (void)cost;
   p.prefix_wgs = (int)(per_head * p.Hkv);
   const int64_t len = (n_tiles + chunks - 1) / chunks * kKeyTile;
   p.prefix_chunk_len = (int)len;
@@ -1169,29 +1227,18 @@ void prefix_workspace_carve(AttnParams& p, void* region) {
   p.ws_pre_o = (float*)((char*)region + (slots * 2 * sizeof(float) + 255) / 256 * 256);
 }
 
-// The prefix items, prefix_wgs / Hkv of them per KV head and round, one
-// launch per round (or all of them in one launch).
-hipError_t launch_prefix_partials(const AttnParams& p, hipStream_t stream, bool rounds) {
-  const int items = p.prefix_tiles * p.prefix_chunks;
-  const int per_head = rounds ? p.prefix_wgs / p.Hkv : items;
-  constexpr int NB = kPrefillRowBlocks;
-  const dim3 block(512 / NB);
+hipError_t launch_shared_prefix_decode(const AttnParams& p, hipStream_t stream) {
+  const int n_dec = p.grid_parts / dk::decode_groups(p.Hkv);
+  const dim3 grid((unsigned)(n_dec + p.prefix_wgs)), block(512);
   const bool fp8 = p.kv_type == KV_FP8;
-  for (int r0 = 0; r0 < items; r0 += per_head) {
-    AttnParams q = p;
-    q.prefix_rank0 = r0;
-    const dim3 grid((unsigned)((int64_t)std::min(per_head, items - r0) * p.Hkv));
-    if (p.D == 128) {
-      if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 128, NB, true>), grid, block, 0, stream, q);
-      else hipLaunchKernelGGL((prefill_kernel<2, 128, NB, true>), grid, block, 0, stream, q);
-    } else {
-      if (fp8) hipLaunchKernelGGL((prefill_kernel<1, 64, NB, true>), grid, block, 0, stream, q);
-      else hipLaunchKernelGGL((prefill_kernel<2, 64, NB, true>), grid, block, 0, stream, q);
-    }
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  if (p.D == 128) {
+    if (fp8) hipLaunchKernelGGL((shared_prefix_decode_kernel<1, 128>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((shared_prefix_decode_kernel<2, 128>), grid, block, 0, stream, p);
+  } else {
+    if (fp8) hipLaunchKernelGGL((shared_prefix_decode_kernel<1, 64>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((shared_prefix_decode_kernel<2, 64>), grid, block, 0, stream, p);
   }
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {

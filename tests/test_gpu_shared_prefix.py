@@ -54,10 +54,8 @@ def test_shared_prefix_single_kv_head(gpu, split):
 def test_shared_prefix_in_rounds_head_dim_64(gpu):
     """1024 sequences, 32 KV heads, head_dim 64: 8 groups of sequences per KV
     head against at most 6 prefix workgroups per KV head beside the decode, so
-    the prefix items run in several rounds; at head_dim 64 a decode and a
-    prefix workgroup also fit on one CU together.  Every row against the
-    oracle, and the allocation-free form (the same plan on one stream, in one
-    launch) gives the same bits."""
+    each prefix workgroup runs several items in turn.  Every row against the
+    oracle, and the allocation-free form gives the same bits."""
     cfg = dataclasses.replace(W.SMALL[4], name="shared-prefix-rounds-d64", batch=1024, hq=64, hkv=32, head_dim=64,
                               num_pages=3300, old_max=40, shared_prefix_tokens=128)
     note(f"shared prefix in rounds {cfg.name}")
