@@ -429,8 +429,8 @@ struct PrefillLds {
 };
 
 // One work item, run by workgroup `block`: item rank0 + block / Hkv of KV
-// head block % Hkv (prefill_kernel: rank0 = 0, or the round's first item in
-// the PREFIX form; the shared-prefix kernel loops its workgroups over rounds).
+// head block % Hkv (prefill_kernel: rank0 = 0; the shared-prefix kernel's
+// prefix workgroups run the PREFIX form for rank0 = 0, prefix_wgs / Hkv, ...).
 template <int ESZ, int D, int NB, bool PREFIX>
 __device__ __forceinline__ void prefill_item(const AttnParams& p, PrefillLds<ESZ, D>& lds, const unsigned block,
                                              const int rank0) {
