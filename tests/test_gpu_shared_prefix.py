@@ -72,6 +72,30 @@ def test_shared_prefix_in_rounds_head_dim_64(gpu):
     assert np.array_equal(got.cpu().view(torch.int16).numpy(), out.cpu().view(torch.int16).numpy())
 
 
+@pytest.mark.parametrize("hq,hkv", [(6, 3), (24, 12)])
+def test_shared_prefix_decode_groups_below_eight_waves(gpu, hq, hkv):
+    """3 and 12 KV heads: a decode workgroup's groups use 6 of its 8 waves
+    (the shared-prefix kernel launches 8 for its prefix items), so 2 waves
+    only take part in the length scan.  Against the oracle, and the one-call
+    write + attention (whose new rows the decode workgroups store, surplus
+    waves included) bit for bit against the two calls."""
+    cfg = dataclasses.replace(W.SMALL[4], name=f"shared-prefix-{hkv}kv", hq=hq, hkv=hkv, batch=40, num_pages=1024)
+    note(f"shared prefix {cfg.name}")
+    w = W.generate(cfg, DEV)
+    kp, vp = gpu_write(gpu, w)
+    pages = cfg.shared_prefix_tokens // 16
+    out = attend_shared(gpu, w, kp, vp, pages)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, "bf16", cfg.name)
+    fkp, fvp = w.key_pool.clone(), w.value_pool.clone()
+    fused = torch.full_like(w.q, float("nan"))
+    gpu.paged_kv_write_attention(w.k_new, w.v_new, w.slot_mapping, fkp, fvp, w.q, w.block_table, w.seq_lens,
+                                 w.query_start_loc, w.scale, fused, max_query_len=1, shared_prefix_pages=pages)
+    torch.cuda.synchronize()
+    assert torch.equal(fkp.view(torch.uint8), kp.view(torch.uint8)) and torch.equal(fvp.view(torch.uint8), vp.view(torch.uint8))
+    assert torch.equal(fused.view(torch.int16), out.view(torch.int16))
+
+
 def test_shared_prefix_full(gpu):
     """256 sequences on 128 shared pages, in the launch configuration the
     benchmark times; every row against the oracle."""
