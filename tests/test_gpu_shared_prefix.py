@@ -96,6 +96,21 @@ def test_shared_prefix_decode_groups_below_eight_waves(gpu, hq, hkv):
     assert torch.equal(fused.view(torch.int16), out.view(torch.int16))
 
 
+@pytest.mark.parametrize("g,d,kv", [(16, 128, "bf16"), (2, 64, "fp8_e4m3fn"), (4, 64, "bf16")])
+def test_shared_prefix_geometries(gpu, g, d, kv):
+    """The shared-prefix kernel's other instances and group sizes: the largest
+    GQA group (16 query heads per KV head, 16 sequences per prefix item), fp8
+    pools at head_dim 64, and bf16 at head_dim 64; against the oracle."""
+    cfg = dataclasses.replace(W.SMALL[4], name=f"shared-prefix-g{g}-d{d}-{kv}", hq=2 * g, hkv=2, head_dim=d,
+                              kv_dtype=kv, batch=48, num_pages=1024, shared_prefix_tokens=96)
+    note(f"shared prefix {cfg.name}")
+    w = W.generate(cfg, DEV, seed=23)
+    kp, vp = gpu_write(gpu, w)
+    out = attend_shared(gpu, w, kp, vp, cfg.shared_prefix_tokens // 16)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, kv, cfg.name)
+
+
 def test_shared_prefix_full(gpu):
     """256 sequences on 128 shared pages, in the launch configuration the
     benchmark times; every row against the oracle."""
