@@ -43,6 +43,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # dense: 256 CU x 4096 flop/clk x 2.4 GHz
+# Core clock the chip sustains under the prefill kernel's MFMA + exp load:
+# rocprofv3 --pmc GRBM_GUI_ACTIVE per XCD over the kernel's traced duration
+# (about 528K cycles in 265 us, profiles/prefill_bf16_b8_n512.md).  The
+# MFMA peak at that clock is the one the kernel can reach on this load.
+PREFILL_SUSTAINED_CLOCK_GHZ = 2.0
+NOMINAL_CLOCK_GHZ = 2.4
 METRIC = "decode KV-read GB/s (% of HBM peak) + prefill TFLOP/s (% MFMA peak), 1 GPU"
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "traffic.json")
 CALIB_BYTES = 256 << 20
@@ -749,6 +755,10 @@ def main(argv=None) -> int:
             "achieved": round(fl / (k3 * 1e-3) / 1e12, 2),
             "peak": BF16_MFMA_PEAK_TFLOPS,
             "frac": round(fl / (k3 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4),
+            "sustained_clock_GHz": PREFILL_SUSTAINED_CLOCK_GHZ,
+            "frac_of_peak_at_sustained_clock": round(fl / (k3 * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS
+                                                     * NOMINAL_CLOCK_GHZ / PREFILL_SUSTAINED_CLOCK_GHZ, 4),
+            "sustained_clock_source": "rocprofv3 GRBM_GUI_ACTIVE per XCD over the traced kernel duration",
             "flop_per_launch": fl,
             "launch_ms_mean": round(k3, 5),
             "call_ms_median": round(a3, 5),
