@@ -142,13 +142,81 @@ __device__ __forceinline__ int item_chunks(const AttnParams& p, int64_t kv) {
 //   [2 + 2 rank] = b << 16 | tile, [3 + 2 rank] = tile index * split_max_chunks + chunk,
 //   [2 + 2 items_cap + tile index] = b << 16 | tile.
 // Above kPlanSortMax items the natural order is kept.
+//
+// The natural order is by sequence, then query tile, then chunk.  Each thread
+// first counts the tiles and items of its run of `per` sequences; block-wide
+// prefix sums of both give every run's first tile and item.  Then one thread
+// per tile finds its run by binary search over the tile sums, and the tile's
+// first item by adding the chunk counts of the run's tiles before it, and
+// lists the tile's items.  The ranking counts, for each item, the items with
+// a larger 64-bit key (key range << 32 | ~index: longer first, then listed
+// earlier).
+
+// tiles and chunks of sequence b: the query tiles' key ranges P + min((t + 1)
+// tpt, n), t < ceil(n / tpt)
+struct PlanSeq {
+  int64_t n, P;
+  int nt;
+};
+
+__device__ __forceinline__ PlanSeq plan_seq(const AttnParams& p, int b, int tpt) {
+  PlanSeq q;
+  q.n = p.qsl[b + 1] - p.qsl[b];
+  q.P = p.seq_lens[b] - q.n;
+  q.nt = (int)((q.n + tpt - 1) / tpt);
+  return q;
+}
+
+__device__ __forceinline__ int64_t plan_tile_kv(const PlanSeq& q, int t, int tpt) {
+  return q.P + min((int64_t)(t + 1) * tpt, q.n);
+}
+
+// items of tiles 0 .. t - 1 of a sequence
+__device__ __forceinline__ int32_t plan_items_before(const AttnParams& p, const PlanSeq& q, int t, int tpt) {
+  if (p.split_keys == 0) return t;
+  int32_t a = 0;
+  for (int u = 0; u < t; ++u) a += item_chunks(p, plan_tile_kv(q, u, tpt));
+  return a;
+}
+
+// Inclusive sums of a and c over the 1024 threads (lane shuffles within each
+// wave, then the 16 wave totals through LDS: one barrier); returns them in
+// a and c, and the totals.
+__device__ __forceinline__ void plan_scan2(int32_t& a, int32_t& c, int32_t (&s_wave)[2][16], int32_t& total_a,
+                                           int32_t& total_c) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t ya = __shfl_up(a, off, 64), yc = __shfl_up(c, off, 64);
+    if (lane >= off) {
+      a += ya;
+      c += yc;
+    }
+  }
+  if (lane == 63) {
+    s_wave[0][wave] = a;
+    s_wave[1][wave] = c;
+  }
+  __syncthreads();
+  total_a = 0;
+  total_c = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    const int32_t ta = s_wave[0][w], tc = s_wave[1][w];
+    a += w < wave ? ta : 0;
+    c += w < wave ? tc : 0;
+    total_a += ta;
+    total_c += tc;
+  }
+}
 
 __global__ __launch_bounds__(1024) void prefill_plan_kernel(AttnParams p) {
   __shared__ uint32_t s_item[kPlanSortMax];
   __shared__ int32_t s_tc[kPlanSortMax];
-  __shared__ int32_t s_work[kPlanSortMax];
-  __shared__ int32_t s_scan[1024];   // items (inclusive scan over threads)
+  __shared__ uint64_t s_key[kPlanSortMax];
+  __shared__ int32_t s_scan[1024];   // items (inclusive sums over threads' runs)
   __shared__ int32_t s_tscan[1024];  // tiles
+  __shared__ int32_t s_wave[2][16];
   const int tid = threadIdx.x;
   const int B = (int)p.B;
   const int tpt = kPrefillRows / p.G;
@@ -161,66 +229,71 @@ __global__ __launch_bounds__(1024) void prefill_plan_kernel(AttnParams p) {
   for (int i = 0; i < per; ++i) {
     const int b = tid * per + i;
     if (b >= B) continue;
-    const int64_t n = p.qsl[b + 1] - p.qsl[b];
-    const int64_t P = p.seq_lens[b] - n;
-    const int nt = (int)((n + tpt - 1) / tpt);
-    mine_t += nt;
-    for (int t = 0; t < nt; ++t) mine += item_chunks(p, P + min((int64_t)(t + 1) * tpt, n));
+    const PlanSeq q = plan_seq(p, b, tpt);
+    mine_t += q.nt;
+    mine += plan_items_before(p, q, q.nt, tpt);
   }
+  int32_t all_items, all_tiles;
+  plan_scan2(mine, mine_t, s_wave, all_items, all_tiles);
   s_scan[tid] = mine;
   s_tscan[tid] = mine_t;
   __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scans
-    const int32_t v = tid >= off ? s_scan[tid - off] : 0;
-    const int32_t vt = tid >= off ? s_tscan[tid - off] : 0;
-    __syncthreads();
-    s_scan[tid] += v;
-    s_tscan[tid] += vt;
-    __syncthreads();
-  }
-  const int32_t total = (int32_t)min((int64_t)s_scan[1023], items_cap);
+  const int32_t total = (int32_t)min((int64_t)all_items, items_cap);
   const bool sort = total <= kPlanSortMax;
-  int32_t at = tid ? s_scan[tid - 1] : 0;
-  int32_t gt = tid ? s_tscan[tid - 1] : 0;
-  for (int i = 0; i < per; ++i) {
-    const int b = tid * per + i;
-    if (b >= B) continue;
-    const int64_t n = p.qsl[b + 1] - p.qsl[b];
-    const int64_t P = p.seq_lens[b] - n;
-    const int nt = (int)((n + tpt - 1) / tpt);
-    for (int t = 0; t < nt; ++t, ++gt) {
-      const uint32_t item = ((uint32_t)b << 16) | (uint32_t)t;
-      if (gt < tiles_cap) tiles[gt] = (int32_t)item;
-      const int64_t kv = P + min((int64_t)(t + 1) * tpt, n);
-      const int nch = item_chunks(p, kv);
-      for (int ch = 0; ch < nch; ++ch, ++at) {
-        if (at >= total) continue;
-        const int32_t tc = gt * MC + ch;
-        if (sort) {
-          const int64_t w = nch == 1 ? kv : (ch + 1 < nch ? (int64_t)p.split_keys : kv - (int64_t)ch * p.split_keys);
-          s_item[at] = item;
-          s_tc[at] = tc;
-          s_work[at] = (int32_t)min(w, (int64_t)INT32_MAX);
-        } else {
-          list[2 * at] = (int32_t)item;
-          list[2 * at + 1] = tc;
-        }
+  for (int g = tid; g < all_tiles; g += 1024) {
+    // the run holding tile g: the first thread whose inclusive tile sum exceeds g
+    int lo = 0, hi = 1023;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (s_tscan[mid] > g) hi = mid;
+      else lo = mid + 1;
+    }
+    int32_t local = g - (lo ? s_tscan[lo - 1] : 0);
+    int32_t at = lo ? s_scan[lo - 1] : 0;
+    int b = lo * per;
+    PlanSeq q = plan_seq(p, b, tpt);
+    while (local >= q.nt) {  // earlier sequences of the run
+      local -= q.nt;
+      at += plan_items_before(p, q, q.nt, tpt);
+      q = plan_seq(p, ++b, tpt);
+    }
+    const int t = local;
+    at += plan_items_before(p, q, t, tpt);
+    const uint32_t item = ((uint32_t)b << 16) | (uint32_t)t;
+    if (g < tiles_cap) tiles[g] = (int32_t)item;
+    const int64_t kv = plan_tile_kv(q, t, tpt);
+    const int nch = item_chunks(p, kv);
+    for (int ch = 0; ch < nch; ++ch, ++at) {
+      if (at >= total) break;
+      const int32_t tc = g * MC + ch;
+      if (sort) {
+        const int64_t w = nch == 1 ? kv : (ch + 1 < nch ? (int64_t)p.split_keys : kv - (int64_t)ch * p.split_keys);
+        s_item[at] = item;
+        s_tc[at] = tc;
+        s_key[at] = ((uint64_t)min(w, (int64_t)INT32_MAX) << 32) | (uint32_t)~at;
+      } else {
+        list[2 * at] = (int32_t)item;
+        list[2 * at + 1] = tc;
       }
     }
   }
   if (tid == 0) {
     p.ws_plan[0] = total;
-    p.ws_plan[1] = (int32_t)min((int64_t)s_tscan[1023], tiles_cap);
+    p.ws_plan[1] = (int32_t)min((int64_t)all_tiles, tiles_cap);
   }
   if (!sort) return;
   __syncthreads();
-  // rank = items that go first: longer, or as long and listed earlier
+  // rank = items with a larger key: longer, or as long and listed earlier
   for (int i = tid; i < total; i += 1024) {
-    const int32_t w = s_work[i];
-    int32_t rank = 0;
-    // (unrolled so that several LDS reads are in flight at once)
-#pragma unroll 8
-    for (int j = 0; j < total; ++j) rank += (s_work[j] > w) | ((s_work[j] == w) & (j < i));
+    const uint64_t k = s_key[i];
+    int32_t r0 = 0, r1 = 0;
+    int j = 0;
+    for (; j + 2 <= total; j += 2) {
+      r0 += s_key[j] > k;
+      r1 += s_key[j + 1] > k;
+    }
+    if (j < total) r0 += s_key[j] > k;
+    const int rank = r0 + r1;
     list[2 * rank] = (int32_t)s_item[i];
     list[2 * rank + 1] = s_tc[i];
   }
