@@ -102,6 +102,8 @@ hipError_t launch_write_fp8(const WriteFp8Params& p, hipStream_t stream);
 hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_prefill(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
 hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev);
+// the shared-prefix decode's split-K pass and prefix items as one launch
+// (prefix_len > 0; the merge follows in launch_decode)
 hipError_t launch_shared_prefix_decode(const AttnParams& p, hipStream_t stream);
 
 hipError_t launch_csr_to_block_table(const int64_t* indptr, const int64_t* indices, const int64_t* last_len,

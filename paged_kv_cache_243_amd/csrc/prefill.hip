@@ -1265,7 +1265,7 @@ size_t prefix_plan(AttnParams& p, int64_t prefix_len, int n_cu, bool tight) {
   p.prefix_len = prefix_len;
   p.prefix_tiles = (int)((p.B + tpt - 1) / tpt);
   const int64_t n_tiles = prefix_len / kKeyTile;
-  const double private_bytes = (double)p.B * std::max<int64_t>(0, p.max_blocks * 16 - prefix_len) / 2 * p.Hkv *
+  const double private_bytes = (double)p.B * std::max<int64_t>(0, p.max_blocks * kPageSize - prefix_len) / 2 * p.Hkv *
                                p.D * std::max(p.kv_bytes, 1) * 2;
   const double tile_ns = kPrefixTileNs * p.D / 128;
   const int64_t step = 8 / std::gcd<int64_t>(p.Hkv, 8);
