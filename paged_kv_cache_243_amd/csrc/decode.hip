@@ -70,8 +70,8 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
 //   M = max_w m_w,  out = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w.
 // A workgroup serves nh query heads of one sequence (threadIdx.y), with nw
 // waves per head (1 .. kMergeWaves, by the partials a sequence has; nw * nh
-// <= kMergeWaves).  Wave k of a head takes the chunks k, k + nw, ... of 8
-// consecutive partials; wave 0 also the prefix chunks', whose loads go out
+// <= kMergeWaves).  Wave k of a head takes the chunks k, k + nw, ... of
+// CHUNK consecutive partials; wave 0 also the prefix chunks', whose loads go out
 // before the metadata's, as their slots do not depend on it.  Every (m, l)
 // and O load of a chunk is issued before any of them is used, so the merge
 // of a head costs two memory round trips (metadata, then partials) when its
@@ -87,6 +87,14 @@ static int merge_waves(int parts, int64_t B) {
   return (int)std::min<int64_t>(kMergeWaves, (per_seq + 7) / 8);
 }
 
+// partials a merge wave loads together: as many as a sequence holds on
+// average, rounded up to 2, 4 or 8 (fewer registers and loads when most rows
+// have one or two decode partials, as with a shared prefix)
+static int merge_chunk(int parts, int64_t B) {
+  const int64_t per_seq = parts / std::max<int64_t>(B, 1) + 1;
+  return per_seq <= 2 ? 2 : per_seq <= 4 ? 4 : 8;
+}
+
 // heads per merge workgroup: the most that divides Hq within kMergeWaves waves
 static int merge_heads(int Hq, int nw) {
   for (int nh = kMergeWaves / nw; nh > 1; nh /= 2)
@@ -94,10 +102,9 @@ static int merge_heads(int Hq, int nw) {
   return 1;
 }
 
-template <int D>
+template <int D, int CHUNK>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
   constexpr int PER = D / 64;
-  constexpr int CHUNK = 8;
   __shared__ float s_ml[kMergeWaves][2];
   __shared__ float s_o[kMergeWaves][D];
   const int nw = blockDim.x >> 6;
@@ -276,7 +283,12 @@ static void launch_decode_t(const AttnParams& p, hipStream_t stream, const Launc
     hipLaunchKernelGGL((decode_kernel<ESZ, D>), dim3((unsigned)(p.grid_parts / R)), dim3(threads), 0, stream, p);
   if (ev.end) (void)hipEventRecord(ev.end, stream);
   const int nw = merge_waves(p.grid_parts, p.B), nh = merge_heads(p.Hq, nw);
-  hipLaunchKernelGGL((merge_kernel<D>), dim3((unsigned)(p.Hq / nh), (unsigned)p.B), dim3(64 * nw, nh), 0, stream, p);
+  const dim3 mgrid((unsigned)(p.Hq / nh), (unsigned)p.B), mblock(64 * nw, nh);
+  switch (merge_chunk(p.grid_parts, p.B)) {
+    case 2: hipLaunchKernelGGL((merge_kernel<D, 2>), mgrid, mblock, 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((merge_kernel<D, 4>), mgrid, mblock, 0, stream, p); break;
+    default: hipLaunchKernelGGL((merge_kernel<D, 8>), mgrid, mblock, 0, stream, p); break;
+  }
 }
 
 hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
