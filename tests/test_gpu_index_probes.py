@@ -21,7 +21,7 @@ import torch
 
 from paged_kv_cache_243_amd import workloads as W
 from tests import helpers as H
-from tests.gpu_helpers import assert_close, gpu_write, note
+from tests.gpu_helpers import as_f64, assert_close, gpu_write, note, sample_rows
 from tests.helpers import S
 from tests.probes import (assert_probes, decode_runs, decode_targets, prefill_runs, prefill_targets,
                            probe_run, rows_of)
@@ -144,6 +144,35 @@ def test_prefill_index_probes_every_row_full_size(gpu, kv, tp):
     lens = S(w.seq_lens)
     assert all((b, j) in seen for b in range(len(lens)) for j in range(-(-int(lens[b]) // 16))), \
         "a page no probe reached"
+
+
+def test_prefill_long_context_page_ids_past_65535(gpu):
+    """A chunked prefill of 256 new tokens onto 60,000-position fp8 contexts in a
+    131,072-page pool (page ids past 65,535, so page byte offsets past 2^32;
+    few items, so the keys are split): sampled rows against the oracle, and
+    index probes on every page of both sequences."""
+    cfg = dataclasses.replace(W.CONFIGS[3], name="prefill-fp8-60k", batch=2, kv_dtype="fp8_e4m3fn", n_new=256,
+                              old_min=60000, old_max=60000, num_pages=131072)
+    note(f"long-context prefill {cfg.name}")
+    w = W.generate(cfg, DEV)
+    kp, vp = gpu_write(gpu, w)
+    attend = _attend_fn(gpu, w, kp, vp)
+    rows = sample_rows(w, 8, seed=21)
+    out = attend(w.q)
+    ref = H.oracle_attend(w, S(kp).copy(), S(vp).copy(), sel_tokens=rows)
+    assert_close(as_f64(out)[rows], ref, w.kv_dtype, f"{cfg.name} ({rows.shape[0]} rows)")
+    rng = np.random.default_rng(22)
+    seq, _ = rows_of(w)
+    seen, high = set(), 0
+    for run in range(prefill_runs(w)):
+        t = prefill_targets(w, rng, run)
+        got, want, pages = probe_run(w, kp, vp, t, attend)
+        assert_probes(got, want, f"{cfg.name} run {run}", quiet=run > 0)
+        seen.update(zip(np.repeat(seq, t.shape[1]).tolist(), (t // 16).reshape(-1).tolist()))
+        high += int((pages >= 65536).sum())
+    lens = S(w.seq_lens)
+    assert all((b, j) in seen for b in range(len(lens)) for j in range(-(-int(lens[b]) // 16))), "a page no probe reached"
+    assert high > 0, "no probe landed on a page id past 65535"
 
 
 @pytest.mark.parametrize("tp", [8, 4])
