@@ -71,6 +71,31 @@ def test_decode_index_probes_full_size(gpu, case):
         assert high > 0, "no probe landed on a page id past 65535"
 
 
+def test_decode_in_pools_past_4_gib(gpu):
+    """bf16 pools of 262,144 pages (8 GiB each, page byte offsets past 2^32):
+    the write stores every new row bit for bit at its slot, and index probes
+    on every page of every sequence find the rows the block table names."""
+    cfg = dataclasses.replace(W.CONFIGS[2], name="decode-bf16-8gib-pool", batch=16, old_min=2000, old_max=4000,
+                              num_pages=262144)
+    note(f"decode in 8 GiB pools {cfg.name}")
+    w = W.generate(cfg, DEV)
+    kp, vp = gpu_write(gpu, w)
+    slots = w.slot_mapping
+    assert int(slots.max()) * cfg.hkv * cfg.head_dim * 2 >= 2 ** 32, "no new row past 4 GiB"
+    rows_k = kp.view(-1, cfg.hkv, cfg.head_dim)[slots]
+    rows_v = vp.view(-1, cfg.hkv, cfg.head_dim)[slots]
+    assert torch.equal(rows_k.view(torch.int16), w.k_new.view(torch.int16))
+    assert torch.equal(rows_v.view(torch.int16), w.v_new.view(torch.int16))
+    attend = _attend_fn(gpu, w, kp, vp)
+    rng = np.random.default_rng(23)
+    high = 0
+    for run in range(decode_runs(w)):
+        got, want, pages = probe_run(w, kp, vp, decode_targets(w, run, rng), attend)
+        assert_probes(got, want, f"{cfg.name} run {run}", quiet=run > 0)
+        high += int((pages >= 131072).sum())
+    assert high > 0, "no probe landed past 4 GiB"
+
+
 def test_shared_prefix_decode_index_probes_full_size(gpu):
     """The shared-prefix decode (256 sequences on one 128-page prefix, the
     prefix run once as MFMA tiles and merged with each sequence's split-K
