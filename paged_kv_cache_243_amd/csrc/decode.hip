@@ -102,31 +102,45 @@ static int merge_heads(int Hq, int nw) {
   return 1;
 }
 
-template <int D, int CHUNK>
+// rows (query heads of one sequence) a merge wave takes: 2 when the rows
+// outnumber one round of the chip's wave slots and every head has one wave,
+// so the waves fit one round; else 1
+constexpr int64_t kMergeOneRoundRows = 8192;
+static int merge_rows_per_wave(int64_t B, int Hq, int nw) {
+  return nw == 1 && B * Hq > kMergeOneRoundRows && Hq % 2 == 0 ? 2 : 1;
+}
+
+// RPW rows per wave (consecutive query heads; only with one wave per head),
+// CHUNK decode partials per load round, and the prefix chunks' partials held
+// for at most PMAX chunks (1 when there is at most one).  Each row's
+// arithmetic is the same whatever RPW and PMAX are.
+template <int D, int CHUNK, int RPW, int PMAX>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
   constexpr int PER = D / 64;
   __shared__ float s_ml[kMergeWaves][2];
   __shared__ float s_o[kMergeWaves][D];
   const int nw = blockDim.x >> 6;
-  const int hq = blockIdx.x * blockDim.y + threadIdx.y, b = blockIdx.y;
+  const int hq0 = (blockIdx.x * blockDim.y + threadIdx.y) * RPW, b = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row_slot = threadIdx.y * nw;  // this head's LDS slots: row_slot .. row_slot + nw - 1
   const bool prefix = p.prefix_len > 0;
-  // the prefix chunks' partials (at most kMaxPrefixChunks), loaded first
-  f32x2 mlc[kMaxPrefixChunks];
-  float oc[kMaxPrefixChunks][PER];
+  // the prefix chunks' partials, loaded first
+  f32x2 mlc[RPW][PMAX];
+  float oc[RPW][PMAX][PER];
   if (prefix && wave == 0) {
     const f32x2* pml = (const f32x2*)p.ws_pre_ml;
 #pragma unroll
-    for (int c = 0; c < kMaxPrefixChunks; ++c) {
-      if (c < p.prefix_chunks) {
-        const int64_t slot = ((int64_t)c * p.B + b) * p.Hq + hq;
-        mlc[c] = pml[slot];
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
-        for (int i = 0; i < PER; ++i) oc[c][i] = p.ws_pre_o[slot * D + lane + 64 * i];
+      for (int c = 0; c < PMAX; ++c) {
+        if (c < p.prefix_chunks) {
+          const int64_t slot = ((int64_t)c * p.B + b) * p.Hq + hq0 + r;
+          mlc[r][c] = pml[slot];
+#pragma unroll
+          for (int i = 0; i < PER; ++i) oc[r][c][i] = p.ws_pre_o[slot * D + lane + 64 * i];
+        }
       }
-    }
   }
   // every index this workgroup needs, loaded together
   const int64_t q_row = p.qsl[b], q_end = p.qsl[b + 1];
@@ -141,89 +155,131 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
   }
   if (!prefix && wa == wz) return;  // written directly by decode_kernel
   const f32x2* ml = (const f32x2*)p.ws_ml;
-  float M = -INFINITY, l = 0.f;
-  float o[PER];
+  float M[RPW], l[RPW], o[RPW][PER];
 #pragma unroll
-  for (int i = 0; i < PER; ++i) o[i] = 0.f;
+  for (int r = 0; r < RPW; ++r) {
+    M[r] = -INFINITY;
+    l[r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[r][i] = 0.f;
+  }
   if (prefix && wave == 0) {
 #pragma unroll
-    for (int c = 0; c < kMaxPrefixChunks; ++c)
-      if (c < p.prefix_chunks) M = fmaxf(M, mlc[c][0]);
+    for (int r = 0; r < RPW; ++r) {
 #pragma unroll
-    for (int c = 0; c < kMaxPrefixChunks; ++c) {
-      if (c < p.prefix_chunks) {
-        const float f = __builtin_amdgcn_exp2f(mlc[c][0] - M);
-        l += f * mlc[c][1];
+      for (int c = 0; c < PMAX; ++c)
+        if (c < p.prefix_chunks) M[r] = fmaxf(M[r], mlc[r][c][0]);
 #pragma unroll
-        for (int i = 0; i < PER; ++i) o[i] += f * oc[c][i];
+      for (int c = 0; c < PMAX; ++c) {
+        if (c < p.prefix_chunks) {
+          const float f = __builtin_amdgcn_exp2f(mlc[r][c][0] - M[r]);
+          l[r] += f * mlc[r][c][1];
+#pragma unroll
+          for (int i = 0; i < PER; ++i) o[r][i] += f * oc[r][c][i];
+        }
       }
     }
   }
   for (int32_t w0 = wa + wave * CHUNK; w0 <= wz; w0 += nw * CHUNK) {
-    f32x2 mlw[CHUNK];
-    float ow[CHUNK][PER];
+    f32x2 mlw[RPW][CHUNK];
+    float ow[RPW][CHUNK][PER];
 #pragma unroll
-    for (int c = 0; c < CHUNK; ++c) {
-      const int32_t w = min(w0 + c, wz);
-      const int64_t slot = ((int64_t)b + w) * p.Hq + hq;
-      mlw[c] = ml[slot];
+    for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int i = 0; i < PER; ++i) ow[c][i] = p.ws_o[slot * D + lane + 64 * i];
+      for (int c = 0; c < CHUNK; ++c) {
+        const int32_t w = min(w0 + c, wz);
+        const int64_t slot = ((int64_t)b + w) * p.Hq + hq0 + r;
+        mlw[r][c] = ml[slot];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) ow[r][c][i] = p.ws_o[slot * D + lane + 64 * i];
+      }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      float Mc = M[r];
+#pragma unroll
+      for (int c = 0; c < CHUNK; ++c) {
+        // slots past wz repeat wz, and empty ranges wrote nothing: weight 0
+        const bool live = w0 + c <= wz && !part.empty(w0 + c);
+        mlw[r][c][0] = live ? mlw[r][c][0] : -INFINITY;
+        Mc = fmaxf(Mc, mlw[r][c][0]);
+      }
+      // rescale what earlier chunks summed (nothing yet: M = Mc = -inf would give NaN)
+      const float alpha = M[r] == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M[r] - Mc);
+      l[r] *= alpha;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[r][i] *= alpha;
+#pragma unroll
+      for (int c = 0; c < CHUNK; ++c) {
+        const float f = __builtin_amdgcn_exp2f(mlw[r][c][0] - Mc);
+        l[r] += f * mlw[r][c][1];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) o[r][i] += f * ow[r][c][i];
+      }
+      M[r] = Mc;
     }
-    float Mc = M;
-#pragma unroll
-    for (int c = 0; c < CHUNK; ++c) {
-      // slots past wz repeat wz, and empty ranges wrote nothing: weight 0
-      const bool live = w0 + c <= wz && !part.empty(w0 + c);
-      mlw[c][0] = live ? mlw[c][0] : -INFINITY;
-      Mc = fmaxf(Mc, mlw[c][0]);
-    }
-    // rescale what earlier chunks summed (nothing yet: M = Mc = -inf would give NaN)
-    const float alpha = M == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(M - Mc);
-    l *= alpha;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] *= alpha;
-#pragma unroll
-    for (int c = 0; c < CHUNK; ++c) {
-      const float f = __builtin_amdgcn_exp2f(mlw[c][0] - Mc);
-      l += f * mlw[c][1];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) o[i] += f * ow[c][i];
-    }
-    M = Mc;
   }
-  if (nw > 1) {
-    // combine the head's waves' (M, l, O); a wave that took no partial has
-    // M = -inf, l = 0, O = 0 and weight 0 (wave 0 holds at least one live
-    // partial)
-    if (lane == 0) {
-      s_ml[row_slot + wave][0] = M;
-      s_ml[row_slot + wave][1] = l;
+  if constexpr (RPW == 1) {
+    if (nw > 1) {
+      // combine the head's waves' (M, l, O); a wave that took no partial has
+      // M = -inf, l = 0, O = 0 and weight 0 (wave 0 holds at least one live
+      // partial)
+      if (lane == 0) {
+        s_ml[row_slot + wave][0] = M[0];
+        s_ml[row_slot + wave][1] = l[0];
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i) s_o[row_slot + wave][lane + 64 * i] = o[0][i];
+      __syncthreads();
+      if (wave != 0) return;
+      float Mt = -INFINITY;
+      for (int k = 0; k < nw; ++k) Mt = fmaxf(Mt, s_ml[row_slot + k][0]);
+      float lt = 0.f, ot[PER];
+#pragma unroll
+      for (int i = 0; i < PER; ++i) ot[i] = 0.f;
+      for (int k = 0; k < nw; ++k) {
+        const float m_k = s_ml[row_slot + k][0];
+        const float f = m_k == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_k - Mt);
+        lt += f * s_ml[row_slot + k][1];
+#pragma unroll
+        for (int i = 0; i < PER; ++i) ot[i] += f * s_o[row_slot + k][lane + 64 * i];
+      }
+      l[0] = lt;
+#pragma unroll
+      for (int i = 0; i < PER; ++i) o[0][i] = ot[i];
     }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) s_o[row_slot + wave][lane + 64 * i] = o[i];
-    __syncthreads();
-    if (wave != 0) return;
-    float Mt = -INFINITY;
-    for (int k = 0; k < nw; ++k) Mt = fmaxf(Mt, s_ml[row_slot + k][0]);
-    float lt = 0.f, ot[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) ot[i] = 0.f;
-    for (int k = 0; k < nw; ++k) {
-      const float m_k = s_ml[row_slot + k][0];
-      const float f = m_k == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_k - Mt);
-      lt += f * s_ml[row_slot + k][1];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) ot[i] += f * s_o[row_slot + k][lane + 64 * i];
-    }
-    l = lt;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) o[i] = ot[i];
   }
-  const float inv = 1.0f / l;
 #pragma unroll
-  for (int i = 0; i < PER; ++i)
-    ((__bf16*)p.out)[(q_row * p.Hq + hq) * D + lane + 64 * i] = (__bf16)(o[i] * inv);
+  for (int r = 0; r < RPW; ++r) {
+    const float inv = 1.0f / l[r];
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      ((__bf16*)p.out)[(q_row * p.Hq + hq0 + r) * D + lane + 64 * i] = (__bf16)(o[r][i] * inv);
+  }
+}
+
+template <int D, int CHUNK>
+static void launch_merge_c(const AttnParams& p, int rpw, int pmax, dim3 grid, dim3 block, hipStream_t stream) {
+  if (rpw == 2) {
+    if (pmax == 1) hipLaunchKernelGGL((merge_kernel<D, CHUNK, 2, 1>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((merge_kernel<D, CHUNK, 2, kMaxPrefixChunks>), grid, block, 0, stream, p);
+  } else {
+    if (pmax == 1) hipLaunchKernelGGL((merge_kernel<D, CHUNK, 1, 1>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((merge_kernel<D, CHUNK, 1, kMaxPrefixChunks>), grid, block, 0, stream, p);
+  }
+}
+
+template <int D>
+static void launch_merge(const AttnParams& p, hipStream_t stream) {
+  const int nw = merge_waves(p.grid_parts, p.B);
+  const int rpw = merge_rows_per_wave(p.B, p.Hq, nw);
+  const int nh = merge_heads(p.Hq / rpw, nw);
+  const int pmax = p.prefix_len > 0 && p.prefix_chunks > 1 ? kMaxPrefixChunks : 1;
+  const dim3 grid((unsigned)(p.Hq / (rpw * nh)), (unsigned)p.B), block(64 * nw, nh);
+  switch (merge_chunk(p.grid_parts, p.B)) {
+    case 2: launch_merge_c<D, 2>(p, rpw, pmax, grid, block, stream); break;
+    case 4: launch_merge_c<D, 4>(p, rpw, pmax, grid, block, stream); break;
+    default: launch_merge_c<D, 8>(p, rpw, pmax, grid, block, stream); break;
+  }
 }
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
@@ -282,13 +338,7 @@ static void launch_decode_t(const AttnParams& p, hipStream_t stream, const Launc
   else
     hipLaunchKernelGGL((decode_kernel<ESZ, D>), dim3((unsigned)(p.grid_parts / R)), dim3(threads), 0, stream, p);
   if (ev.end) (void)hipEventRecord(ev.end, stream);
-  const int nw = merge_waves(p.grid_parts, p.B), nh = merge_heads(p.Hq, nw);
-  const dim3 mgrid((unsigned)(p.Hq / nh), (unsigned)p.B), mblock(64 * nw, nh);
-  switch (merge_chunk(p.grid_parts, p.B)) {
-    case 2: hipLaunchKernelGGL((merge_kernel<D, 2>), mgrid, mblock, 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((merge_kernel<D, 4>), mgrid, mblock, 0, stream, p); break;
-    default: hipLaunchKernelGGL((merge_kernel<D, 8>), mgrid, mblock, 0, stream, p); break;
-  }
+  launch_merge<D>(p, stream);
 }
 
 hipError_t launch_decode(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
