@@ -8,42 +8,48 @@
 // (page, offset) in the pool.  The copy moves 16-byte integer vectors, so any
 // bit pattern (NaN payloads included) is stored unchanged; a negative slot
 // writes nothing.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace pkv {
 
-// One thread moves one 16-byte chunk of one K or V row.  Consecutive threads
-// take consecutive chunks of the same row, so reads of k/v and stores into the
-// pool row are both fully coalesced.
+// One workgroup per new token: its slot is read once (a negative slot ends
+// the workgroup), and its threads move the row's 16-byte chunks, the K row's
+// then the V row's, consecutive threads taking consecutive chunks, so the
+// reads of k/v and the stores into the pool rows are both fully coalesced.
 __global__ __launch_bounds__(256) void slot_scatter_kernel(const uint4* __restrict__ k,
                                                            const uint4* __restrict__ v,
                                                            const int64_t* __restrict__ slots,
                                                            uint4* __restrict__ key_pool,
                                                            uint4* __restrict__ value_pool,
-                                                           int64_t n_tokens, int64_t row_vecs) {
-  const int64_t per_tensor = n_tokens * row_vecs;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= 2 * per_tensor) return;
-  const bool is_v = gid >= per_tensor;
-  const int64_t idx = is_v ? gid - per_tensor : gid;
-  const int64_t t = idx / row_vecs;
-  const int64_t c = idx - t * row_vecs;
+                                                           int64_t row_vecs) {
+  const int64_t t = blockIdx.x;
   const int64_t slot = slots[t];
   if (slot < 0) return;
-  const uint4* src = is_v ? v : k;
-  uint4* dst = is_v ? value_pool : key_pool;
-  dst[slot * row_vecs + c] = src[t * row_vecs + c];
+  const uint4* ks = k + t * row_vecs;
+  const uint4* vs = v + t * row_vecs;
+  uint4* kd = key_pool + slot * row_vecs;
+  uint4* vd = value_pool + slot * row_vecs;
+  for (int64_t c = threadIdx.x; c < row_vecs; c += blockDim.x) {
+    const uint4 a = ks[c], b = vs[c];
+    kd[c] = a;
+    vd[c] = b;
+  }
+}
+
+// threads per write workgroup: the row's chunks rounded up to whole waves, at most 256
+static unsigned write_threads(int64_t row_chunks) {
+  return (unsigned)std::min<int64_t>(256, (row_chunks + 63) / 64 * 64);
 }
 
 hipError_t launch_write(const WriteParams& p, hipStream_t stream) {
   if (p.n_tokens == 0) return hipSuccess;
   const int64_t row_vecs = p.row_bytes / 16;
-  const int64_t work = 2 * p.n_tokens * row_vecs;
-  const int64_t blocks = (work + 255) / 256;
-  hipLaunchKernelGGL(slot_scatter_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const uint4*)p.k, (const uint4*)p.v, p.slots, (uint4*)p.key_pool,
-                     (uint4*)p.value_pool, p.n_tokens, row_vecs);
+  hipLaunchKernelGGL(slot_scatter_kernel, dim3((unsigned)p.n_tokens), dim3(write_threads(row_vecs)), 0, stream,
+                     (const uint4*)p.k, (const uint4*)p.v, p.slots, (uint4*)p.key_pool, (uint4*)p.value_pool,
+                     row_vecs);
   return hipGetLastError();
 }
 
@@ -69,9 +75,11 @@ __device__ __forceinline__ uint32_t e4m3fn_pair(float ya, float yb, uint32_t xa_
   return r;
 }
 
-// One thread converts 8 consecutive elements of one K or V row (16 bytes in,
-// 8 bytes out); consecutive threads take consecutive groups, so loads and
-// stores are coalesced.  D is a multiple of 8, so a group lies in one head.
+// One workgroup per new token (its slot read once; a negative slot ends the
+// workgroup); a thread converts 8 consecutive elements of the K row and the
+// same 8 of the V row (16 bytes in, 8 bytes out each), consecutive threads
+// taking consecutive groups, so loads and stores are coalesced.  D is a
+// multiple of 8, so a group lies in one head.
 __global__ __launch_bounds__(256) void slot_scatter_fp8_kernel(const uint4* __restrict__ k,
                                                                const uint4* __restrict__ v,
                                                                const int64_t* __restrict__ slots,
@@ -79,40 +87,38 @@ __global__ __launch_bounds__(256) void slot_scatter_fp8_kernel(const uint4* __re
                                                                uint2* __restrict__ value_pool,
                                                                const float* __restrict__ k_scale,
                                                                const float* __restrict__ v_scale,
-                                                               int64_t n_tokens, int64_t row_groups,
-                                                               int64_t head_groups) {
-  const int64_t per_tensor = n_tokens * row_groups;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= 2 * per_tensor) return;
-  const bool is_v = gid >= per_tensor;
-  const int64_t idx = is_v ? gid - per_tensor : gid;
-  const int64_t t = idx / row_groups;
-  const int64_t c = idx - t * row_groups;
+                                                               int64_t row_groups, int32_t head_groups) {
+  const int64_t t = blockIdx.x;
   const int64_t slot = slots[t];
   if (slot < 0) return;
-  const float s = (is_v ? v_scale : k_scale)[c / head_groups];
-  const uint4 x = (is_v ? v : k)[t * row_groups + c];
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-  uint32_t code[4];
+  auto convert = [](const uint4 x, float s) {
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t code[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t xl = w[i] << 16, xh = w[i] & 0xFFFF0000u;
-    code[i] = e4m3fn_pair(__builtin_bit_cast(float, xl) / s, __builtin_bit_cast(float, xh) / s, xl, xh);
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t xl = w[i] << 16, xh = w[i] & 0xFFFF0000u;
+      code[i] = e4m3fn_pair(__builtin_bit_cast(float, xl) / s, __builtin_bit_cast(float, xh) / s, xl, xh);
+    }
+    uint2 out;
+    out.x = code[0] | (code[1] << 16);
+    out.y = code[2] | (code[3] << 16);
+    return out;
+  };
+  for (int64_t c = threadIdx.x; c < row_groups; c += blockDim.x) {
+    const uint32_t h = (uint32_t)c / (uint32_t)head_groups;
+    const uint4 xk = k[t * row_groups + c], xv = v[t * row_groups + c];
+    const float sk = k_scale[h], sv = v_scale[h];
+    key_pool[slot * row_groups + c] = convert(xk, sk);
+    value_pool[slot * row_groups + c] = convert(xv, sv);
   }
-  uint2 out;
-  out.x = code[0] | (code[1] << 16);
-  out.y = code[2] | (code[3] << 16);
-  (is_v ? value_pool : key_pool)[slot * row_groups + c] = out;
 }
 
 hipError_t launch_write_fp8(const WriteFp8Params& p, hipStream_t stream) {
   if (p.n_tokens == 0) return hipSuccess;
   const int64_t row_groups = p.Hkv * p.D / 8;
-  const int64_t work = 2 * p.n_tokens * row_groups;
-  const int64_t blocks = (work + 255) / 256;
-  hipLaunchKernelGGL(slot_scatter_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     (const uint4*)p.k, (const uint4*)p.v, p.slots, (uint2*)p.key_pool,
-                     (uint2*)p.value_pool, p.k_scale, p.v_scale, p.n_tokens, row_groups, p.D / 8);
+  hipLaunchKernelGGL(slot_scatter_fp8_kernel, dim3((unsigned)p.n_tokens), dim3(write_threads(row_groups)), 0,
+                     stream, (const uint4*)p.k, (const uint4*)p.v, p.slots, (uint2*)p.key_pool,
+                     (uint2*)p.value_pool, p.k_scale, p.v_scale, row_groups, (int32_t)(p.D / 8));
   return hipGetLastError();
 }
 
