@@ -346,8 +346,6 @@ int plan_write(const pkv_tensor* k, const pkv_tensor* v, const pkv_tensor* slot_
   p.value_pool = value_pool->data;
   p.n_tokens = k->shape[0];
   p.row_bytes = row_bytes;
-  // one workgroup per new token
-  if (p.n_tokens > INT32_MAX) return PKV_ERR_UNSUPPORTED;
   return PKV_OK;
 }
 
@@ -390,7 +388,6 @@ int paged_kv_write_fp8(const pkv_tensor* k, const pkv_tensor* v, const pkv_tenso
   p.n_tokens = k->shape[0];
   p.Hkv = key_pool->shape[2];
   p.D = key_pool->shape[3];
-  if (p.n_tokens > INT32_MAX) return PKV_ERR_UNSUPPORTED;  // one workgroup per new token
   if (p.n_tokens == 0) return PKV_OK;
   return pkv::launch_write_fp8(p, (hipStream_t)stream) == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }

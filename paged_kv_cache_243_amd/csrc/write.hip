@@ -15,27 +15,29 @@
 
 namespace pkv {
 
-// One workgroup per new token: its slot is read once (a negative slot ends
-// the workgroup), and its threads move the row's 16-byte chunks, the K row's
-// then the V row's, consecutive threads taking consecutive chunks, so the
-// reads of k/v and the stores into the pool rows are both fully coalesced.
+// A workgroup per new token (tokens t = blockIdx.x, + gridDim.x, ... when
+// there are more tokens than workgroups): the token's slot is read once (a
+// negative slot skips it), and the threads move the row's 16-byte chunks, the
+// K row's and the V row's, consecutive threads taking consecutive chunks, so
+// the reads of k/v and the stores into the pool rows are both fully coalesced.
 __global__ __launch_bounds__(256) void slot_scatter_kernel(const uint4* __restrict__ k,
                                                            const uint4* __restrict__ v,
                                                            const int64_t* __restrict__ slots,
                                                            uint4* __restrict__ key_pool,
                                                            uint4* __restrict__ value_pool,
-                                                           int64_t row_vecs) {
-  const int64_t t = blockIdx.x;
-  const int64_t slot = slots[t];
-  if (slot < 0) return;
-  const uint4* ks = k + t * row_vecs;
-  const uint4* vs = v + t * row_vecs;
-  uint4* kd = key_pool + slot * row_vecs;
-  uint4* vd = value_pool + slot * row_vecs;
-  for (int64_t c = threadIdx.x; c < row_vecs; c += blockDim.x) {
-    const uint4 a = ks[c], b = vs[c];
-    kd[c] = a;
-    vd[c] = b;
+                                                           int64_t row_vecs, int64_t n_tokens) {
+  for (int64_t t = blockIdx.x; t < n_tokens; t += gridDim.x) {
+    const int64_t slot = slots[t];
+    if (slot < 0) continue;
+    const uint4* ks = k + t * row_vecs;
+    const uint4* vs = v + t * row_vecs;
+    uint4* kd = key_pool + slot * row_vecs;
+    uint4* vd = value_pool + slot * row_vecs;
+    for (int64_t c = threadIdx.x; c < row_vecs; c += blockDim.x) {
+      const uint4 a = ks[c], b = vs[c];
+      kd[c] = a;
+      vd[c] = b;
+    }
   }
 }
 
@@ -44,12 +46,18 @@ static unsigned write_threads(int64_t row_chunks) {
   return (unsigned)std::min<int64_t>(256, (row_chunks + 63) / 64 * 64);
 }
 
+// workgroups of a write launch: one per token, at most kWriteMaxGroups (the
+// workgroups then loop over the tokens), which keeps the launch's work-items
+// (workgroups x threads) below 2^32
+constexpr int64_t kWriteMaxGroups = 1 << 20;
+static unsigned write_groups(int64_t n_tokens) { return (unsigned)std::min(n_tokens, kWriteMaxGroups); }
+
 hipError_t launch_write(const WriteParams& p, hipStream_t stream) {
   if (p.n_tokens == 0) return hipSuccess;
   const int64_t row_vecs = p.row_bytes / 16;
-  hipLaunchKernelGGL(slot_scatter_kernel, dim3((unsigned)p.n_tokens), dim3(write_threads(row_vecs)), 0, stream,
+  hipLaunchKernelGGL(slot_scatter_kernel, dim3(write_groups(p.n_tokens)), dim3(write_threads(row_vecs)), 0, stream,
                      (const uint4*)p.k, (const uint4*)p.v, p.slots, (uint4*)p.key_pool, (uint4*)p.value_pool,
-                     row_vecs);
+                     row_vecs, p.n_tokens);
   return hipGetLastError();
 }
 
@@ -75,11 +83,11 @@ __device__ __forceinline__ uint32_t e4m3fn_pair(float ya, float yb, uint32_t xa_
   return r;
 }
 
-// One workgroup per new token (its slot read once; a negative slot ends the
-// workgroup); a thread converts 8 consecutive elements of the K row and the
-// same 8 of the V row (16 bytes in, 8 bytes out each), consecutive threads
-// taking consecutive groups, so loads and stores are coalesced.  D is a
-// multiple of 8, so a group lies in one head.
+// A workgroup per new token, as in the plain write (its slot read once; a
+// negative slot skips it); a thread converts 8 consecutive elements of the K
+// row and the same 8 of the V row (16 bytes in, 8 bytes out each),
+// consecutive threads taking consecutive groups, so loads and stores are
+// coalesced.  D is a multiple of 8, so a group lies in one head.
 __global__ __launch_bounds__(256) void slot_scatter_fp8_kernel(const uint4* __restrict__ k,
                                                                const uint4* __restrict__ v,
                                                                const int64_t* __restrict__ slots,
@@ -87,10 +95,8 @@ __global__ __launch_bounds__(256) void slot_scatter_fp8_kernel(const uint4* __re
                                                                uint2* __restrict__ value_pool,
                                                                const float* __restrict__ k_scale,
                                                                const float* __restrict__ v_scale,
-                                                               int64_t row_groups, int32_t head_groups) {
-  const int64_t t = blockIdx.x;
-  const int64_t slot = slots[t];
-  if (slot < 0) return;
+                                                               int64_t row_groups, int32_t head_groups,
+                                                               int64_t n_tokens) {
   auto convert = [](const uint4 x, float s) {
     const uint32_t w[4] = {x.x, x.y, x.z, x.w};
     uint32_t code[4];
@@ -104,21 +110,25 @@ __global__ __launch_bounds__(256) void slot_scatter_fp8_kernel(const uint4* __re
     out.y = code[2] | (code[3] << 16);
     return out;
   };
-  for (int64_t c = threadIdx.x; c < row_groups; c += blockDim.x) {
-    const uint32_t h = (uint32_t)c / (uint32_t)head_groups;
-    const uint4 xk = k[t * row_groups + c], xv = v[t * row_groups + c];
-    const float sk = k_scale[h], sv = v_scale[h];
-    key_pool[slot * row_groups + c] = convert(xk, sk);
-    value_pool[slot * row_groups + c] = convert(xv, sv);
+  for (int64_t t = blockIdx.x; t < n_tokens; t += gridDim.x) {
+    const int64_t slot = slots[t];
+    if (slot < 0) continue;
+    for (int64_t c = threadIdx.x; c < row_groups; c += blockDim.x) {
+      const uint32_t h = (uint32_t)c / (uint32_t)head_groups;
+      const uint4 xk = k[t * row_groups + c], xv = v[t * row_groups + c];
+      const float sk = k_scale[h], sv = v_scale[h];
+      key_pool[slot * row_groups + c] = convert(xk, sk);
+      value_pool[slot * row_groups + c] = convert(xv, sv);
+    }
   }
 }
 
 hipError_t launch_write_fp8(const WriteFp8Params& p, hipStream_t stream) {
   if (p.n_tokens == 0) return hipSuccess;
   const int64_t row_groups = p.Hkv * p.D / 8;
-  hipLaunchKernelGGL(slot_scatter_fp8_kernel, dim3((unsigned)p.n_tokens), dim3(write_threads(row_groups)), 0,
+  hipLaunchKernelGGL(slot_scatter_fp8_kernel, dim3(write_groups(p.n_tokens)), dim3(write_threads(row_groups)), 0,
                      stream, (const uint4*)p.k, (const uint4*)p.v, p.slots, (uint2*)p.key_pool,
-                     (uint2*)p.value_pool, p.k_scale, p.v_scale, row_groups, (int32_t)(p.D / 8));
+                     (uint2*)p.value_pool, p.k_scale, p.v_scale, row_groups, (int32_t)(p.D / 8), p.n_tokens);
   return hipGetLastError();
 }
 

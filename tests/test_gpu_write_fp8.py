@@ -93,3 +93,46 @@ def test_write_fp8_then_attend(gpu, full):
     rows = np.arange(S(w.q).shape[0], dtype=np.int64)
     ref = H.oracle_attend(w, okp, ovp, sel_tokens=rows)
     assert_close(out, ref, w.kv_dtype, f"fp8 write then attend full={full}")
+
+
+@pytest.mark.parametrize("quantise", [False, True])
+def test_write_of_more_rows_than_one_launch_has_workgroups(gpu, quantise):
+    """2^20 + 4099 new rows: more than the 2^20 workgroups a write launch
+    runs, so workgroups take several tokens each.  Slots are a seeded
+    permutation of the pool rows with every seventh one negative; rows of one
+    KV head of 8 elements (the narrowest both writes take: one 16-byte chunk
+    of bf16, one 8-element group to quantise).  Pools compared byte for byte (plain bf16 copy, and the
+    quantising write into fp8 pools).  The expected pools apply the oracle's
+    write to consecutive 4096-row pieces of the rows: the slots are distinct,
+    so the pieces' order does not matter, and the oracle's all-pairs
+    duplicate-slot check stays quick."""
+    n = (1 << 20) + 4099
+    note(f"write of {n} rows, quantising={quantise}")
+    Hkv, D, ps = 1, 8, 16
+    num_pages = -(-n // ps) + 64
+    rng = np.random.default_rng(41)
+    slots = torch.as_tensor(rng.permutation(num_pages * ps)[:n].astype(np.int64))
+    slots[::7] = -1
+    k, v = bf16_rows((n, Hkv, D), 42, 1.0), bf16_rows((n, Hkv, D), 43, 3.0)
+    kb, vb, sl = bits(k), bits(v), S(slots)
+    pieces = [slice(a, min(a + 4096, n)) for a in range(0, n, 4096)]
+    if quantise:
+        pool = torch.full((num_pages, ps, Hkv, D), 0x7F, dtype=torch.uint8, device=DEV)
+        ks, vs = torch.tensor([0.02], dtype=torch.float32), torch.tensor([0.05], dtype=torch.float32)
+        kpg, vpg = pool.clone(), pool.clone()
+        gpu.paged_kv_write_fp8(k.to(DEV), v.to(DEV), slots.to(DEV), kpg, vpg, ks.to(DEV), vs.to(DEV))
+        torch.cuda.synchronize()
+        okp, ovp = S(pool).copy(), S(pool).copy()
+        for r in pieces:
+            oracle.paged_kv_write_fp8(kb[r], vb[r], sl[r], S(ks), S(vs), okp, ovp)
+    else:
+        pool = torch.full((num_pages, ps, Hkv, D), -1, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+        kpg, vpg = pool.clone(), pool.clone()
+        gpu.paged_kv_write(k.to(DEV), v.to(DEV), slots.to(DEV), kpg, vpg)
+        torch.cuda.synchronize()
+        okp, ovp = S(pool).copy(), S(pool).copy()
+        for r in pieces:
+            oracle.paged_kv_write(kb[r], vb[r], sl[r], okp, ovp)
+    kp, vp = S(kpg), S(vpg)
+    assert np.array_equal(kp.view(np.uint8), okp.view(np.uint8)), f"{np.count_nonzero(kp != okp)} key elements differ"
+    assert np.array_equal(vp.view(np.uint8), ovp.view(np.uint8)), f"{np.count_nonzero(vp != ovp)} value elements differ"
