@@ -7,11 +7,14 @@
 // throughput target here and must match an fp64 reference to 1e-5, so this is
 // a plain VALU kernel in fp32 arithmetic rather than a bf16 MFMA tiling.
 //
-// One wave per (packed query row t, KV head h).  Lanes take 64 key positions at
+// One wave per (packed query row t, KV head h) (with more rows than the grid's
+// kF32MaxRowGroups, a wave takes rows t, t + gridDim.x, ...).  Lanes take 64 key positions at
 // a time and compute the G dot products of their key; an online softmax
 // (natural exponent, fp32) keeps a running max and sum per head; the lanes then
 // switch to value dimensions and accumulate the weighted value rows.
 #include <math.h>
+
+#include <algorithm>
 
 #include "common.h"
 #include "kernels.h"
@@ -29,11 +32,13 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// rows of the grid: the launch's work-items (rows x 64) stay below 2^32
+constexpr int64_t kF32MaxRowGroups = 1 << 20;
+
 template <int D>
-__global__ __launch_bounds__(64) void attention_f32_kernel(AttnParams p) {
+__device__ __forceinline__ void attention_f32_row(const AttnParams& p, const int64_t t) {
   constexpr int PER = D / 64;
   constexpr int GMAX = 16;
-  const int64_t t = blockIdx.x;
   const int h = blockIdx.y;
   const int lane = threadIdx.x;
   const int G = p.G;
@@ -128,9 +133,17 @@ __global__ __launch_bounds__(64) void attention_f32_kernel(AttnParams p) {
   }
 }
 
+template <int D>
+__global__ __launch_bounds__(64) void attention_f32_kernel(AttnParams p) {
+  for (int64_t t = blockIdx.x; t < p.T; t += gridDim.x) {
+    attention_f32_row<D>(p, t);
+    __syncthreads();  // the next row rewrites the query and weight tiles
+  }
+}
+
 hipError_t launch_attention_f32(const AttnParams& p, hipStream_t stream, const LaunchEvents& ev) {
   if (p.T == 0) return hipSuccess;
-  dim3 grid((unsigned)p.T, (unsigned)p.Hkv);
+  dim3 grid((unsigned)std::min<int64_t>(p.T, kF32MaxRowGroups), (unsigned)p.Hkv);
   if (ev.begin) (void)hipEventRecord(ev.begin, stream);
   if (p.D == 128)
     hipLaunchKernelGGL(attention_f32_kernel<128>, grid, dim3(64), 0, stream, p);

@@ -61,3 +61,20 @@ def test_csr_unpacking_keeps_reads_inside_the_table_for_bad_values(gpu):
     assert bt[1].tolist() == [105, 7, 7] and sl[1] == 16
     assert bt[2].tolist() == [7, 7, 7] and sl[2] == 0
     assert bt[3].tolist() == [106, 107, 108] and sl[3] <= 3 * 16
+
+
+def test_csr_unpacking_of_a_table_larger_than_one_launch(gpu):
+    """4096 rows of 65537 entries (2^28 + 4096 of them): more than the 2^28
+    threads one unpacking launch runs, so threads take several entries.  Rows
+    hold 0 to 40 seeded pages; table and lengths equal the oracle's."""
+    B, max_blocks, pad = 4096, 65537, 3
+    note(f"csr unpacking of a {B} x {max_blocks} table")
+    rng = np.random.default_rng(23)
+    n = rng.integers(0, 41, size=B)
+    indptr = np.concatenate([[0], np.cumsum(n)]).astype(np.int64)
+    indices = rng.integers(0, 1 << 20, size=int(indptr[-1])).astype(np.int64)
+    last = rng.integers(1, 17, size=B).astype(np.int64)
+    bt, sl = unpack_gpu(gpu, indptr, indices, last, B, max_blocks, pad)
+    obt, osl = oracle.block_table_from_csr(indptr, indices, last, 16, pad, max_blocks)
+    assert np.array_equal(sl, osl)
+    assert np.array_equal(bt, obt)
