@@ -38,8 +38,10 @@
  *    B * ceil(max_blocks * 16 / 32) < 2^31; for
  *    calls with several query rows per sequence, block_table rows of at most
  *    2^31 - 1 positions and at most 65535 query tiles of 256 / (Hq / Hkv)
- *    rows (ceil(T / tile) <= 65535).  Anything else is PKV_ERR_UNSUPPORTED;
- *    there is no fallback path.
+ *    rows (ceil(T / tile) <= 65535), and at most 2^22 (query tile, KV head)
+ *    work items counting the key chunks of a split (in practice a bound on
+ *    Hkv x query tiles).  Anything else is PKV_ERR_UNSUPPORTED; there is no
+ *    fallback path.
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H

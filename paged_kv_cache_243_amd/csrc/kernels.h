@@ -129,6 +129,9 @@ void prefill_split_plan(AttnParams& p);
 size_t prefill_workspace_bytes(const AttnParams& p);
 void prefill_workspace_carve(AttnParams& p, void* workspace);
 constexpr int kMaxPrefixChunks = 8;
+// prefill workgroups one launch may hold (512 threads each: 2^31 work-items,
+// below the launch limit of 2^32)
+constexpr int64_t kPrefillMaxGroups = (int64_t)1 << 22;
 // groups of decode sequences, chunks and chunk length of a shared prefix of
 // prefix_len positions, and the workgroups its items run on beside the
 // decode, a share of the n_cu CUs (fills p.prefix_*; n_cu = 0 when the device

@@ -228,6 +228,9 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
     if (max_blocks * kPageSize > INT32_MAX) return PKV_ERR_UNSUPPORTED;
     if ((T + tpt - 1) / tpt > 65535) return PKV_ERR_UNSUPPORTED;
     pkv::prefill_split_plan(p);
+    // a workgroup of 512 threads per (query tile, key chunk, KV head): the
+    // launch's work-items must stay below 2^32
+    if (p.plan_tiles_cap * p.split_max_chunks * Hkv > pkv::kPrefillMaxGroups) return PKV_ERR_UNSUPPORTED;
     plan.workspace = pkv::prefill_workspace_bytes(p);
   }
   return PKV_OK;

@@ -304,6 +304,21 @@ def test_prefill_key_split_workspace():
     assert n8 == align((2 + 2 * tiles * 8 + tiles) * 4) + align(rows8 * 2 * 4) + rows8 * 128 * 4
 
 
+def test_prefill_grid_limit():
+    """A prefill launch holds at most 2^22 workgroups (one per query tile and
+    KV head, 512 threads each, so the launch stays below 2^32 work-items):
+    2^20 rows with G = 1 make 4096 + 1 tiles, which 1024 KV heads take just
+    past the limit (4097 x 1024 > 2^22) and 1023 do not."""
+    lib = pkv.load()
+    bt = T([1, 65600], B.PKV_I64)
+    o = opts(max_query_len=1 << 20)
+    size = lambda hkv: lib.paged_attention_workspace_size(
+        ctypes.byref(T([1 << 20, hkv, 64], B.PKV_BF16)), ctypes.byref(T([65600, 16, hkv, 64], B.PKV_BF16)),
+        ctypes.byref(bt), ctypes.byref(o))
+    assert size(1024) == ctypes.c_size_t(-1).value
+    assert size(1023) != ctypes.c_size_t(-1).value
+
+
 @pytest.mark.parametrize("pages,max_q,status", [
     (3, 1, -4),       # odd: units are 32 positions
     (258, 1, -4),     # more than max_blocks
