@@ -28,10 +28,12 @@
  *    index adopts stay alive while it holds them.
  *
  * Object model.  A pool manages page ids [0, num_pages).  A page handle is
- * (generation << 32 | page id) and a sequence handle (epoch << 32 | slot);
- * the generation of a page grows each time it returns to the free list and
- * the epoch of a sequence slot each time the sequence is released, so a handle
- * kept past that point no longer matches.  Each in-use page has a reference
+ * (generation << 32 | page id) and a sequence handle (epoch << 32 | slot),
+ * both counted modulo 2^31 so that handles are non-negative; the generation
+ * of a page grows each time it returns to the free list and the epoch of a
+ * sequence slot each time the sequence is released, so a handle kept past
+ * that point no longer matches (until 2^31 more recyclings of the same page
+ * or slot).  Each in-use page has a reference
  * count: one per sequence holding it and one while the prefix index holds it.
  * A page is in exactly one of: free, or in use with a positive count.
  *

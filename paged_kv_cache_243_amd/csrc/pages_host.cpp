@@ -24,7 +24,11 @@ namespace {
 
 constexpr int64_t kIdMask = 0xFFFFFFFFll;
 
-int64_t make_handle(uint32_t gen, int64_t id) { return ((int64_t)gen << 32) | id; }
+// A handle is (generation << 32 | id) with the generation's low 31 bits, so
+// handles stay non-negative; a generation is compared the same way.
+constexpr uint32_t kGenMask = 0x7FFFFFFFu;
+int64_t make_handle(uint32_t gen, int64_t id) { return (int64_t)((uint64_t)(gen & kGenMask) << 32) | id; }
+uint32_t handle_gen(int64_t handle) { return (uint32_t)(handle >> 32) & kGenMask; }
 
 // 64-bit mixing step (splitmix64 finaliser constants, a published integer
 // hash) for the trie's chained keys
@@ -76,7 +80,7 @@ struct pkv_page_pool {
     const int64_t slot = handle & kIdMask;
     if (handle < 0 || slot >= (int64_t)seqs.size()) return -1;
     const Seq& s = seqs[(size_t)slot];
-    if (!s.live || s.epoch != (uint32_t)(handle >> 32)) return -1;
+    if (!s.live || (s.epoch & kGenMask) != handle_gen(handle)) return -1;
     return slot;
   }
 
@@ -180,7 +184,7 @@ int pkv_page_release(pkv_page_pool* pool, const int64_t* handles, int64_t n) {
   for (int64_t i = 0; i < n; ++i) {
     const int64_t h = handles[i], pg = h & kIdMask;
     if (h < 0 || pg >= pool->num_pages) return PKV_ERR_BAD_HANDLE;
-    if (pool->ref[(size_t)pg] == 0 || pool->gen[(size_t)pg] != (uint32_t)(h >> 32)) return PKV_ERR_BAD_HANDLE;
+    if (pool->ref[(size_t)pg] == 0 || (pool->gen[(size_t)pg] & kGenMask) != handle_gen(h)) return PKV_ERR_BAD_HANDLE;
     if (++count[pg] > pool->ref[(size_t)pg]) return PKV_ERR_BAD_HANDLE;
   }
   for (int64_t i = 0; i < n; ++i) pool->unref(handles[i] & kIdMask);
