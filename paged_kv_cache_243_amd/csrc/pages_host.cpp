@@ -13,8 +13,10 @@
 
 #include <algorithm>
 #include <cstring>
+#include <functional>
 #include <new>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "pagedkv.h"
@@ -434,16 +436,24 @@ int pkv_prefix_match(pkv_page_pool* pool, uint64_t namespace_digest, const int32
 int pkv_prefix_evict(pkv_page_pool* pool, int64_t pages, int64_t* freed_out) {
   if (!pool || !freed_out) return PKV_ERR_NULL;
   if (pages < 0) return PKV_ERR_SHAPE;
+  // Evict, one at a time, the least recently used leaf whose page only the
+  // index holds.  The candidates sit in a min-heap by recency (the clock
+  // values are distinct); evicting a node can only add its parent to them.
+  auto evictable = [&](int64_t i) {
+    const Node& n = pool->nodes[(size_t)i];
+    return n.live && n.children == 0 && pool->ref[(size_t)n.page] == 1;
+  };
+  using Cand = std::pair<uint64_t, int64_t>;  // (last_use, node)
+  std::vector<Cand> heap;
+  if (pages > 0)
+    for (int64_t i = 0; i < (int64_t)pool->nodes.size(); ++i)
+      if (evictable(i)) heap.emplace_back(pool->nodes[(size_t)i].last_use, i);
+  std::make_heap(heap.begin(), heap.end(), std::greater<Cand>());
   int64_t freed = 0;
-  while (freed < pages) {
-    // the least recently used leaf whose page only the index holds
-    int64_t best = -1;
-    for (int64_t i = 0; i < (int64_t)pool->nodes.size(); ++i) {
-      const Node& n = pool->nodes[(size_t)i];
-      if (!n.live || n.children > 0 || pool->ref[(size_t)n.page] != 1) continue;
-      if (best < 0 || n.last_use < pool->nodes[(size_t)best].last_use) best = i;
-    }
-    if (best < 0) break;
+  while (freed < pages && !heap.empty()) {
+    std::pop_heap(heap.begin(), heap.end(), std::greater<Cand>());
+    const int64_t best = heap.back().second;
+    heap.pop_back();
     Node& n = pool->nodes[(size_t)best];
     auto range = pool->by_key.equal_range(n.key);
     for (auto it = range.first; it != range.second; ++it)
@@ -451,13 +461,18 @@ int pkv_prefix_evict(pkv_page_pool* pool, int64_t pages, int64_t* freed_out) {
         pool->by_key.erase(it);
         break;
       }
-    if (n.parent >= 0) --pool->nodes[(size_t)n.parent].children;
+    const int64_t parent = n.parent;
+    if (parent >= 0) --pool->nodes[(size_t)parent].children;
     pool->unref(n.page);
     --pool->index_pages;
     n.live = false;
     n.tokens.clear();
     pool->free_nodes.push_back(best);
     ++freed;
+    if (parent >= 0 && evictable(parent)) {
+      heap.emplace_back(pool->nodes[(size_t)parent].last_use, parent);
+      std::push_heap(heap.begin(), heap.end(), std::greater<Cand>());
+    }
   }
   *freed_out = freed;
   return PKV_OK;

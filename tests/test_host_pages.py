@@ -251,6 +251,103 @@ def test_prefix_eviction_is_lru_leaves_first_and_spares_pages_in_use():
     assert p.prefix_evict(10) == 2 and p.prefix_pages == 0 and p.free_pages == 32
 
 
+def test_prefix_index_follows_the_model_under_random_operations():
+    """Random inserts, matches, sequence releases and evictions over prompts
+    that share and diverge at random blocks, checked after every operation
+    against a Python model of the header's rules: one node per (parent,
+    block of tokens); recency from one counter, ticked for each node an
+    insert passes and each node a match returns, in path order; eviction
+    takes, one page at a time, the least recently used leaf whose page only
+    the index holds.  The model predicts every page's reference count."""
+    rng = np.random.default_rng(77)
+    num_pages, ps = 256, 16
+    p = Hs.PagePool(num_pages, ps)
+    bases = [rng.integers(0, 1000, size=160).astype(np.int32) for _ in range(3)]
+    nodes = {}            # (parent, block tokens) -> node id
+    node = {}             # id -> dict(page, parent, last_use, children, live)
+    seqs = {}             # handle -> page list
+    clock = [0]
+
+    def prompt():
+        t = bases[int(rng.integers(0, 3))].copy()
+        n = int(rng.integers(1, 160))
+        if rng.random() < 0.5:
+            t[int(rng.integers(0, n))] += 1  # diverge inside some block
+        return t[:n]
+
+    def model_refs():
+        ref = np.zeros(num_pages, dtype=np.int64)
+        for pages in seqs.values():
+            for pg in pages:
+                ref[pg] += 1
+        for nd in node.values():
+            if nd["live"]:
+                ref[nd["page"]] += 1
+        return ref
+
+    for step in range(600):
+        op = rng.random()
+        if op < 0.35 and p.free_pages >= 10:             # new sequence, appended, inserted
+            toks = prompt()
+            s = p.create()
+            p.append(s, len(toks))
+            seqs[s] = p.pages(s).tolist()
+            p.prefix_insert(NS, s, toks)
+            parent = -1
+            for i in range(len(toks) // ps):
+                key = (parent, tuple(toks[i * ps:(i + 1) * ps].tolist()))
+                if key not in nodes or not node[nodes[key]]["live"]:
+                    nid = len(node)
+                    nodes[key] = nid
+                    node[nid] = dict(page=seqs[s][i], parent=parent, last_use=0, children=0, live=True)
+                    if parent >= 0:
+                        node[parent]["children"] += 1
+                clock[0] += 1
+                node[nodes[key]]["last_use"] = clock[0]
+                parent = nodes[key]
+        elif op < 0.6:                                    # match
+            toks = prompt()
+            path, parent = [], -1
+            for i in range((len(toks) - 1) // ps):
+                key = (parent, tuple(toks[i * ps:(i + 1) * ps].tolist()))
+                if key not in nodes or not node[nodes[key]]["live"]:
+                    break
+                path.append(nodes[key])
+                parent = nodes[key]
+            s, matched = p.prefix_match(NS, toks)
+            assert matched == ps * len(path), step
+            for nid in path:
+                clock[0] += 1
+                node[nid]["last_use"] = clock[0]
+            seqs[s] = [node[nid]["page"] for nid in path]
+            assert p.pages(s).tolist() == seqs[s], step
+        elif op < 0.85 and seqs:                          # release a sequence
+            s = list(seqs)[int(rng.integers(0, len(seqs)))]
+            p.release_seq(s)
+            del seqs[s]
+        else:                                             # evict
+            k = int(rng.integers(1, 8))
+            ref = model_refs()
+            want = 0
+            while want < k:
+                cand = [(nd["last_use"], nid) for nid, nd in node.items()
+                        if nd["live"] and nd["children"] == 0 and ref[nd["page"]] == 1]
+                if not cand:
+                    break
+                _, nid = min(cand)
+                nd = node[nid]
+                nd["live"] = False
+                ref[nd["page"]] -= 1
+                if nd["parent"] >= 0:
+                    node[nd["parent"]]["children"] -= 1
+                want += 1
+            assert p.prefix_evict(k) == want, step
+        ref = model_refs()
+        got = np.array([p.refcount(pg) for pg in range(num_pages)])
+        assert np.array_equal(got, ref), (step, np.nonzero(got != ref))
+        assert p.prefix_pages == sum(nd["live"] for nd in node.values()), step
+
+
 # ---- end to end through the oracle
 
 def test_metadata_from_the_control_plane_gives_dense_attention():
