@@ -5,7 +5,8 @@ Each case draws, from its own seed, a geometry inside the supported range (1 to
 or fp8 E4M3FN KV), a batch shape (decode rows only, a mixed batch whose
 sequences have 0 to 90 query rows, or decode rows on a shared prefix of 2 to
 32 pages), lengths, a split size and the call form (the write and the
-attention as two calls, or ``paged_kv_write_attention``).  The pools after the
+attention as two calls, ``paged_kv_write_attention``, or the write and then
+``paged_attention_noalloc``, whose workspace is the library's fixed scratch).  The pools after the
 write must match the oracle's bit for bit and every output row must meet the
 bound of its KV type.  The cases combine the kernels' options (groups of
 parts, key split, prefix items, fused write, merge shapes) in ways the
@@ -45,7 +46,7 @@ def draw_case(i: int) -> dict:
     n_max = int(rng.integers(2, 91)) if mode == "mixed" else 1
     prefix_pages = 2 * int(rng.integers(1, 17)) if mode == "prefix" else 0
     split = int(rng.choice([0, 0, 16, 64, 256, 2048])) if mode != "mixed" else 0
-    one_call = bool(rng.integers(0, 2))
+    form = ("two calls", "one call", "no-alloc")[int(rng.integers(0, 3))]
     n_rows = rng.integers(0, n_max + 1, size=batch) if mode == "mixed" else np.ones(batch, dtype=np.int64)
     # keep the oracle's work within budget: fewer sequences, then shorter ones
     def work(b, om):
@@ -56,7 +57,7 @@ def draw_case(i: int) -> dict:
         old_max //= 2
     old_min = min(old_min, old_max)
     return dict(kv=kv, hkv=hkv, g=g, d=d, mode=mode, batch=batch, old_min=old_min, old_max=old_max,
-                n_max=n_max, n_rows=n_rows[:batch], prefix_pages=prefix_pages, split=split, one_call=one_call,
+                n_max=n_max, n_rows=n_rows[:batch], prefix_pages=prefix_pages, split=split, form=form,
                 seed=9100 + i)
 
 
@@ -91,19 +92,20 @@ def test_random_geometry(gpu, i):
     c = draw_case(i)
     desc = (f"case {i}: {c['mode']} {c['kv']} Hkv={c['hkv']} G={c['g']} D={c['d']} B={c['batch']} "
             f"old {c['old_min']}..{c['old_max']} rows<={c['n_max']} prefix {c['prefix_pages']} pages "
-            f"split {c['split']} {'one call' if c['one_call'] else 'two calls'}")
+            f"split {c['split']} {c['form']}")
     note(desc)
     w = build(c)
     kp, vp = w.key_pool.clone(), w.value_pool.clone()
     out = torch.empty_like(w.q)
     kw = dict(k_scale=w.k_scale, v_scale=w.v_scale, max_query_len=w.max_query_len, split_tokens=c["split"],
               shared_prefix_pages=c["prefix_pages"])
-    if c["one_call"]:
+    if c["form"] == "one call":
         gpu.paged_kv_write_attention(w.k_new, w.v_new, w.slot_mapping, kp, vp, w.q, w.block_table, w.seq_lens,
                                      w.query_start_loc, w.scale, out, **kw)
     else:
         gpu.paged_kv_write(w.k_new, w.v_new, w.slot_mapping, kp, vp)
-        gpu.paged_attention(w.q, kp, vp, w.block_table, w.seq_lens, w.query_start_loc, w.scale, out, **kw)
+        attend = gpu.paged_attention if c["form"] == "two calls" else gpu.paged_attention_noalloc
+        attend(w.q, kp, vp, w.block_table, w.seq_lens, w.query_start_loc, w.scale, out, **kw)
     torch.cuda.synchronize()
     okp, ovp = H.oracle_write(w)
     assert np.array_equal(S(kp).view(np.uint8), okp.view(np.uint8)), f"{desc}: key pool differs"
