@@ -837,8 +837,15 @@ __device__ __forceinline__ void prefill_item(const AttnParams& p, PrefillLds<ESZ
   // tile t), and the two are interleaved instruction by instruction so that
   // they co-execute.  Tiles past the sequence are zero filled and fully
   // masked, so iterations past the last tile add nothing.
+  // The iteration is fenced off from the code around it (the two iterations
+  // of a hand-off share a basic block, and the scheduler would otherwise mix
+  // them and undo the interleave), and runs at wave priority 1, so that a
+  // wave in its MFMA stream wins the issue over one fetching or widening
+  // tiles between iterations.
   auto compute = [&](auto mask_c, auto r_c, int t) __attribute__((always_inline)) {
     constexpr int R = decltype(r_c)::value;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
     bf16x8 ka[NKS], va[NDB][2];
     read_k((R + 1) % NS, ka);
     read_v((R + NS - 1) % NS, va);
@@ -855,6 +862,8 @@ __device__ __forceinline__ void prefill_item(const AttnParams& p, PrefillLds<ESZ
       pb_prev[0][nb] = pb[0][nb];
       pb_prev[1][nb] = pb[1][nb];
     }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // iterations 0 .. n_tiles (the last one only adds P(n_tiles - 1) V):
