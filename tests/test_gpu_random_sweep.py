@@ -12,6 +12,7 @@ bound of its KV type.  The cases combine the kernels' options (groups of
 parts, key split, prefix items, fused write, merge shapes) in ways the
 hand-picked cases do not."""
 import dataclasses
+import os
 
 import numpy as np
 import pytest
@@ -24,7 +25,8 @@ from tests.helpers import S
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-N_CASES = 96
+# cases run (PKV_SWEEP_CASES overrides; the first 96 are the suite's)
+N_CASES = int(os.environ.get("PKV_SWEEP_CASES", "96"))
 # oracle work bound per case: query rows x visible keys x query heads x head_dim
 ORACLE_BUDGET = 2e9
 
