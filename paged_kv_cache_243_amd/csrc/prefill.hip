@@ -870,16 +870,18 @@ __device__ __forceinline__ void prefill_item(const AttnParams& p, PrefillLds<ESZ
   // unmasked up to the group holding the diagonal, masked after
   int t = 0;
   if constexpr (ESZ == 2) {
-    // bf16: a hand-off before every even iteration t.  After the barrier
-    // K(t+1), K(t+2), V(t-1) and V(t) are resident (read by iterations t and
-    // t+1), K(t+3), K(t+4), V(t+1) and V(t+2) may still be in flight, and no
-    // wave reads any other slot any more: the hand-off fetches K(t+5),
-    // K(t+6), V(t+3) and V(t+4) into those.  Every hand-off issues the same
-    // number of transfers, so vmcnt(4 LOADS) before the next barrier leaves
-    // exactly the latest hand-off's transfers in flight.
+    // bf16: a hand-off at every even iteration t.  After the barrier before
+    // iteration t, K(t+1), K(t+2), V(t-1) and V(t) are resident (read by
+    // iterations t and t+1), K(t+3), K(t+4), V(t+1) and V(t+2) may still be
+    // in flight, and no wave reads any other slot any more: the hand-off
+    // fetches K(t+5), K(t+6), V(t+3) and V(t+4) into those.  The fetches are
+    // issued after iteration t, so that the iteration's MFMA stream starts
+    // right after the barrier (2 % faster than issuing them first).  Every
+    // hand-off issues the same number of transfers, so vmcnt(4 LOADS) before
+    // the next barrier leaves exactly the latest hand-off's transfers in
+    // flight.
     auto handoff = [&](auto r_c, int t) __attribute__((always_inline)) {
       constexpr int R = decltype(r_c)::value;
-      barrier_lds();
       dma_tile<D, WAVES, false>(c, (__bf16*)sk[(R + 5) % NS], t + 5, page_k[0], wave, lane);
       dma_tile<D, WAVES, false>(c, (__bf16*)sk[R], t + 6, page_k[1], wave, lane);
       dma_tile<D, WAVES, true>(c, (__bf16*)sv[(R + 3) % NS], t + 3, page_v[0], wave, lane);
@@ -889,8 +891,9 @@ __device__ __forceinline__ void prefill_item(const AttnParams& p, PrefillLds<ESZ
     };
     auto pair = [&](auto mask_c, auto r_c, int t) __attribute__((always_inline)) {
       constexpr int R = decltype(r_c)::value;
-      handoff(r_c, t);
+      barrier_lds();
       compute(mask_c, r_c, t);
+      handoff(r_c, t);
       compute(mask_c, std::integral_constant<int, R + 1>{}, t + 1);
       wait_vmem<4 * DM::LOADS>();
       // the next page ids, loaded just before the barrier that waits for them
