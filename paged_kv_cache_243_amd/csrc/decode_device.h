@@ -38,6 +38,11 @@ __host__ __device__ inline int decode_groups(int Hkv) {
   const int g = kMaxWaves / decode_waves(Hkv);
   return g < PKV_DECODE_MAX_GROUPS ? g : PKV_DECODE_MAX_GROUPS;
 }
+// workgroups of the decode launch of p: grid_parts / groups per workgroup,
+// each group running decode_rounds consecutive parts
+__host__ __device__ inline int decode_workgroups(const AttnParams& p) {
+  return p.grid_parts / (decode_groups(p.Hkv) * (p.decode_rounds > 1 ? p.decode_rounds : 1));
+}
 
 // Units of sequence b: its 32-position blocks past the shared prefix (if
 // any), or none when it has no query row.  len_out = seq_lens[b].
@@ -303,14 +308,16 @@ struct Partition {
 };
 
 // Stream-K decode.  The flattened list of (sequence, unit) pairs is cut into
-// grid_parts = nblocks * R equal contiguous ranges (parts), group gi of
-// workgroup w running part w * R + gi; a group walks the sequences its range
-// overlaps (segments).  Wave k of a group handles KV heads k, k + (waves per
-// group), ... of every segment.  A segment that covers a whole sequence writes
-// the normalised output; otherwise it writes an unnormalised partial to slot
-// (b + part), which merge_kernel combines.  Slots are unique because the
-// ranges are ordered: a later sequence only meets later parts.  After the
-// scan the groups share no barrier, so a group whose range is empty leaves.
+// grid_parts equal contiguous ranges (parts).  Group gi of workgroup w runs
+// the `rounds` = grid_parts / (nblocks * R) consecutive parts from
+// (w * R + gi) * rounds on, as one stream; it walks the segments of its range:
+// the pieces of a sequence that lie in one part.  Wave k of a group handles
+// KV heads k, k + (waves per group), ... of every segment.  A segment that
+// covers a whole sequence writes the normalised output; otherwise it writes an
+// unnormalised partial to slot (b + part), which merge_kernel combines.  Slots
+// are unique because the ranges are ordered: a later sequence only meets later
+// parts.  After the scan the groups share no barrier, so a group whose range
+// is empty leaves.
 //
 // Each wave processes its work as one stream of units: a run is one KV head of
 // one segment, runs follow segment by segment (heads inside a segment), and
@@ -319,11 +326,13 @@ struct Partition {
 // ahead.  Lengths come from the
 // scan's LDS tables, so opening a run needs no dependent global load.
 
-// A position in a wave's stream: unit j of run (sequence b, head slot hk),
-// the run covering units [.., j1) of b.  b < 0 past the end of the stream.
+// A position in a wave's stream: unit j of run (sequence b, head slot hk) of
+// the segment of b that lies in part w, units [j0, j1) of b.  b < 0 past the
+// end of the stream.
 struct StreamPos {
   int b, hk;
-  int32_t j, j1;
+  int32_t j, j0, j1;
+  int w;
 };
 
 // LDS of one decode workgroup
@@ -335,7 +344,6 @@ struct DecodeLds {
   // positions of each sequence's last unit (1..32), to rebuild its length
   uint8_t tail[kDecodeMaxSeqs];
   alignas(16) int32_t wave_units[kMaxWaves];
-  alignas(16) int32_t first[kMaxWaves];  // the sequence holding each group's first unit
 };
 
 // The split-K pass as run by workgroup `block` of `nblocks` (decode_kernel:
@@ -349,7 +357,6 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
   auto& s_cum = lds.cum;
   auto& s_tail = lds.tail;
   auto& s_wave_units = lds.wave_units;
-  auto& s_first = lds.first;
   auto& s_ktile = lds.ktile;
   auto& s_vtile = lds.vtile;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -401,7 +408,7 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
   const int wpg = decode_waves(p.Hkv);
   const int R = (nthreads >> 6) / wpg;
   const int gi = wave / wpg, wig = wave - gi * wpg;
-  const int W = nblocks * R, wg = block * R + gi;
+  const int W = p.grid_parts;
   int32_t U;
   {
     const int per = (B + nthreads - 1) / nthreads;
@@ -427,16 +434,11 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
       acc_units += w < wave ? t : 0;
       U += t;
     }
-    const Partition part0(U, W);
     if (tid == 0) s_cum[0] = 0;
     for (int i = 0; i < per; ++i) {
       const int b = b_lo + i;
       if (b < B) {
         const int32_t n = seq_units(p, b, len);
-        for (int r = 0; r < R; ++r) {
-          const int32_t first_unit = part0.start(block * R + r);
-          if (n > 0 && acc_units <= first_unit && first_unit < acc_units + n) s_first[r] = b;
-        }
         // len = prefix_len + 32 (n - 1) + tail with tail in [1, 32]
         s_tail[b] = (uint8_t)(n > 0 ? len - p.prefix_len - (int64_t)kUnit * (n - 1) : 0);
         acc_units += n;
@@ -460,12 +462,15 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
     return;
   }
   const Partition part(U, W);
-  const int32_t u0 = (int32_t)__builtin_amdgcn_readfirstlane(part.start(wg));
-  const int32_t u1 = (int32_t)__builtin_amdgcn_readfirstlane(part.start(wg + 1));
+  const int rounds = W / ((int)nblocks * R);
+  const int g0 = ((int)block * R + gi) * rounds;  // the group's first part
+  const int32_t u0 = (int32_t)__builtin_amdgcn_readfirstlane(part.start(g0));
+  const int32_t u1 = (int32_t)__builtin_amdgcn_readfirstlane(part.start(g0 + rounds));
   if (u0 >= u1) {
     finish_copy();
     return;
   }
+  auto part_end = [&](int w) { return (int32_t)__builtin_amdgcn_readfirstlane(part.start(w + 1)); };
 
   const int hpw = decode_heads_per_wave(p.Hkv);
   const uint32_t row_stride = (uint32_t)p.Hkv * D * ESZ;
@@ -488,31 +493,32 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
     const int32_t n = uniform(s_cum[b + 1] - s_cum[b]), t = uniform(s_tail[b]);
     return base + (int64_t)kUnit * (n - 1) + t;
   };
+  // the segment that starts at unit u of the group's range (u in part w or a
+  // later one): the sequence holding u is the last b with cum[b] <= u, as
+  // empty sequences share their cum with the next one
+  auto segment_at = [&](int32_t u, int b, int w) {
+    while (part_end(w) <= u) ++w;
+    while (uniform(s_cum[b + 1]) <= u) ++b;
+    const int32_t cb = uniform(s_cum[b]), ce = uniform(s_cum[b + 1]);
+    const int32_t j = uniform(u - cb);
+    return StreamPos{b, 0, j, j, uniform(min(part_end(w), ce) - cb), w};
+  };
   auto advance = [&](StreamPos c) {
     if (c.b < 0) return c;
     if (++c.j < c.j1) return c;
     if (c.hk + 1 < hpw && wig + (c.hk + 1) * wpg < p.Hkv) {  // next head of the segment
       ++c.hk;
-      const int32_t cb = uniform(s_cum[c.b]);
-      c.j = uniform(max(u0, cb) - cb);
+      c.j = c.j0;
       return c;
     }
-    for (int b = c.b + 1; b < B; ++b) {  // next segment (starts at its sequence's unit 0)
-      const int32_t cb = uniform(s_cum[b]);
-      if (cb >= u1) break;
-      const int32_t ce = uniform(s_cum[b + 1]);
-      if (ce > cb) {
-        c.b = b;
-        c.hk = 0;
-        c.j = 0;
-        c.j1 = uniform(min(u1, ce) - cb);
-        return c;
-      }
+    const int32_t u = uniform(s_cum[c.b]) + c.j1;  // the next segment's first unit
+    if (u >= u1) {
+      c.b = -1;
+      return c;
     }
-    c.b = -1;
-    return c;
+    return segment_at(u, c.b, c.w);
   };
-  auto same_run = [](const StreamPos& a, const StreamPos& c) { return a.b == c.b && a.hk == c.hk; };
+  auto same_run = [](const StreamPos& a, const StreamPos& c) { return a.b == c.b && a.hk == c.hk && a.w == c.w; };
   // wave-uniform reads of metadata the kernel never writes, as scalar loads
   using c64p = const __attribute__((address_space(4))) int64_t*;
   using cf32p = const __attribute__((address_space(4))) float*;
@@ -569,9 +575,13 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
 
   StreamPos c0;
   {
-    const int lo = uniform(s_first[gi]);  // the sequence holding unit u0
-    const int32_t cb = uniform(s_cum[lo]), ce = uniform(s_cum[lo + 1]);
-    c0 = StreamPos{lo, 0, uniform(u0 - cb), uniform(min(u1, ce) - cb)};
+    // the sequence holding unit u0, by binary search over the unit counts
+    int lo = 0, hi = B;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (uniform(s_cum[mid]) <= u0) lo = mid; else hi = mid;
+    }
+    c0 = segment_at(u0, lo, g0);
   }
   int64_t L0 = seq_len(c0.b), q_row0 = q_row_of(c0.b);
   bf16x8 qb[NKK];
@@ -595,6 +605,15 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
   float m_run = -INFINITY, l_run = 0.f;
   float logit_scale, out_scale;
   run_scales(head_of(c0), logit_scale, out_scale);
+  // fp8 pools: the first partial that ends before the stream does is held in
+  // registers and stored with the last one.  Partial stores made while the
+  // loads stream slow the stream far more than their bytes would; that shows
+  // on long fp8 sequences split into several parts per group (bf16 has
+  // neither the registers nor a measured gain).
+  constexpr bool kHold = ESZ == 1;
+  f32x4 hacc[kHold ? NJ : 1];
+  float hm = 0.f, hl = 0.f;
+  int64_t hslot = -1;  // the held partial's slot for the group's first query head, or -1
 
   while (true) {
     // the unit after c1 (page ids fetched below, loads issued while c1 is computed)
@@ -626,7 +645,8 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
       l_run += xor_shuffle(l_run, 32);
       // (with a shared prefix, its partial joins in the merge: never whole)
       const int32_t cb = s_cum[c0.b], ce = s_cum[c0.b + 1];
-      const bool whole = u0 <= cb && ce <= u1 && p.prefix_len == 0;
+      const bool whole = c0.j0 == 0 && cb + c0.j1 == ce && p.prefix_len == 0;
+      const bool hold = kHold && !whole && hslot < 0 && c1.b >= 0;
       if (col < p.G) {
         const int hq = h0 * p.G + col;
         // acc[t][i] = O^T[dim 16t + 4*grp + i][head col]
@@ -637,8 +657,8 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
           for (int t = 0; t < NJ; ++t)
             *(u32x2*)(orow + 16 * t + 4 * grp) =
                 u32x2{pack_bf16x2(acc[t][0] * inv, acc[t][1] * inv), pack_bf16x2(acc[t][2] * inv, acc[t][3] * inv)};
-        } else {
-          const int64_t slot = ((int64_t)c0.b + wg) * p.Hq + hq;
+        } else if (!hold) {
+          const int64_t slot = ((int64_t)c0.b + c0.w) * p.Hq + hq;
           float* orow = p.ws_o + slot * D;
 #pragma unroll
           for (int t = 0; t < NJ; ++t) *(f32x4*)(orow + 16 * t + 4 * grp) = acc[t] * out_scale;
@@ -648,7 +668,26 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
           }
         }
       }
+      if constexpr (kHold) {
+        if (hold) {
+          hslot = ((int64_t)c0.b + c0.w) * p.Hq + h0 * p.G;
+#pragma unroll
+          for (int t = 0; t < NJ; ++t) hacc[t] = acc[t] * out_scale;
+          hm = m_run;
+          hl = l_run;
+        }
+      }
       if (c1.b < 0) {
+        if (kHold && hslot >= 0 && col < p.G) {
+          const int64_t slot = hslot + col;
+          float* orow = p.ws_o + slot * D;
+#pragma unroll
+          for (int t = 0; t < NJ; ++t) *(f32x4*)(orow + 16 * t + 4 * grp) = hacc[t];
+          if (grp == 0) {
+            p.ws_ml[2 * slot] = hm;
+            p.ws_ml[2 * slot + 1] = hl;
+          }
+        }
         finish_copy();
         break;
       }

@@ -51,6 +51,7 @@ struct AttnParams {
   // decode: stream-K over (sequence, 32-position block) units
   int split_tokens;    // requested positions per partition (0 = library choice)
   int grid_parts;      // partition ranges (parts) of the decode work, a multiple of the parts per workgroup
+  int decode_rounds;   // consecutive parts each decode group runs as one stream (>= 1)
   int32_t* ws_cum;     // [B + 1] units before each sequence (written by workgroup 0)
   float* ws_ml;        // [B + grid_parts, Hq, 2] partial (max in log2 units, sum)
   float* ws_o;         // [B + grid_parts, Hq, D] unnormalised partial outputs
@@ -117,6 +118,10 @@ hipError_t launch_csr_to_block_table(const int64_t* indptr, const int64_t* indic
 size_t decode_workspace_bytes(int64_t B, int Hq, int D, int parts);
 // partition ranges of the decode work: a multiple of the parts one workgroup runs
 int decode_grid_parts(int64_t B, int64_t max_len, int split_tokens, int n_cu, int Hkv);
+// parts each group of a decode grid of one workgroup per CU (n_cu of them) runs:
+// grid_parts / (groups * n_cu) when that divides evenly, else 1 (a workgroup per
+// part)
+int decode_rounds(int grid_parts, int n_cu, int Hkv);
 // whether the decode launch planned in p (grid_parts set) can also write
 // n_new rows of row_bytes each (the fused write)
 bool decode_can_fuse_write(const AttnParams& p, int64_t n_new, int64_t row_bytes);

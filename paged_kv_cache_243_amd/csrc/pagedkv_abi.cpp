@@ -217,6 +217,7 @@ int plan_attention(const pkv_tensor* q, const pkv_tensor* key_pool, const pkv_te
       if (n_cu > 0) decode_cu = std::max(n_cu - p.prefix_wgs, n_cu / 4);
     }
     if (n_cu > 0) p.grid_parts = pkv::decode_grid_parts(B, max_blocks * kPageSize, split, decode_cu, (int)Hkv);
+    p.decode_rounds = pkv::decode_rounds(p.grid_parts, decode_cu, (int)Hkv);
     plan.slot_parts = tight ? p.grid_parts : pkv::kDecodeMaxParts;
     plan.workspace = pkv::decode_workspace_bytes(B, (int)Hq, (int)D, plan.slot_parts) + prefix_bytes;
   } else {

@@ -1125,8 +1125,8 @@ void prefill_kernel(AttnParams p) {
 }
 
 // Shared-prefix decode in one launch.  Workgroups 0 .. n_dec - 1 run the
-// split-K pass over the positions past the prefix (n_dec = grid_parts /
-// parts per workgroup), the next prefix_wgs workgroups the prefix items:
+// split-K pass over the positions past the prefix (n_dec =
+// dk::decode_workgroups(p)), the next prefix_wgs workgroups the prefix items:
 // workgroup j takes items j / Hkv, j / Hkv + per_head, ... of KV head
 // j % Hkv, per_head = prefix_wgs / Hkv.  The two kinds are bound by different
 // units (HBM; MFMA and exp) and start together, so the prefix's tiles run
@@ -1145,7 +1145,7 @@ template <int ESZ, int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void shared_prefix_decode_kernel(AttnParams p) {
   __shared__ SharedPrefixLds<ESZ, D> lds;
-  const unsigned n_dec = (unsigned)(p.grid_parts / dk::decode_groups(p.Hkv));
+  const unsigned n_dec = (unsigned)dk::decode_workgroups(p);
   if (blockIdx.x < n_dec) {
     dk::decode_body<ESZ, D>(p, lds.dec, blockIdx.x, n_dec);
     return;
@@ -1313,7 +1313,7 @@ void prefix_workspace_carve(AttnParams& p, void* region) {
 }
 
 hipError_t launch_shared_prefix_decode(const AttnParams& p, hipStream_t stream) {
-  const int n_dec = p.grid_parts / dk::decode_groups(p.Hkv);
+  const int n_dec = dk::decode_workgroups(p);
   const dim3 grid((unsigned)(n_dec + p.prefix_wgs)), block(512);
   const bool fp8 = p.kv_type == KV_FP8;
   if (p.D == 128) {
