@@ -110,10 +110,26 @@ static int merge_rows_per_wave(int64_t B, int Hq, int nw) {
   return nw == 1 && B * Hq > kMergeOneRoundRows && Hq % 2 == 0 ? 2 : 1;
 }
 
+// elements lane * PER .. + PER - 1 of an fp16 row, widened
+template <int PER>
+__device__ __forceinline__ void load_f16_elems(const _Float16* row, const int lane, float (&o)[PER]) {
+  if constexpr (PER == 2) {
+    const f16x2 v = ((const f16x2*)row)[lane];
+    o[0] = (float)v[0];
+    o[1] = (float)v[1];
+  } else {
+    static_assert(PER == 1, "head_dim 64 or 128");
+    o[0] = (float)row[lane];
+  }
+}
+
 // RPW rows per wave (consecutive query heads; only with one wave per head),
 // CHUNK decode partials per load round, and the prefix chunks' partials held
 // for at most PMAX chunks (1 when there is at most one).  Each row's
-// arithmetic is the same whatever RPW and PMAX are.
+// arithmetic is the same whatever RPW and PMAX are.  A lane owns elements
+// lane * PER .. + PER - 1 of each row.  A decode partial is its unnormalised
+// row in fp16 times a power of two, with (max, sum, the power's inverse); a
+// prefix partial is its unnormalised row in fp32 with (max, sum).
 template <int D, int CHUNK, int RPW, int PMAX>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
   constexpr int PER = D / 64;
@@ -138,7 +154,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
           const int64_t slot = ((int64_t)c * p.B + b) * p.Hq + hq0 + r;
           mlc[r][c] = pml[slot];
 #pragma unroll
-          for (int i = 0; i < PER; ++i) oc[r][c][i] = p.ws_pre_o[slot * D + lane + 64 * i];
+          for (int i = 0; i < PER; ++i) oc[r][c][i] = p.ws_pre_o[slot * D + lane * PER + i];
         }
       }
   }
@@ -154,7 +170,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
     wz = part.owner(ce - 1);
   }
   if (!prefix && wa == wz) return;  // written directly by decode_kernel
-  const f32x2* ml = (const f32x2*)p.ws_ml;
+  const f32x4* ml = (const f32x4*)p.ws_ml;
   float M[RPW], l[RPW], o[RPW][PER];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
@@ -181,7 +197,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
     }
   }
   for (int32_t w0 = wa + wave * CHUNK; w0 <= wz; w0 += nw * CHUNK) {
-    f32x2 mlw[RPW][CHUNK];
+    f32x4 mlw[RPW][CHUNK];
     float ow[RPW][CHUNK][PER];
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
@@ -190,8 +206,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
         const int32_t w = min(w0 + c, wz);
         const int64_t slot = ((int64_t)b + w) * p.Hq + hq0 + r;
         mlw[r][c] = ml[slot];
-#pragma unroll
-        for (int i = 0; i < PER; ++i) ow[r][c][i] = p.ws_o[slot * D + lane + 64 * i];
+        load_f16_elems<PER>(p.ws_o + slot * D, lane, ow[r][c]);
       }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
@@ -212,8 +227,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
       for (int c = 0; c < CHUNK; ++c) {
         const float f = __builtin_amdgcn_exp2f(mlw[r][c][0] - Mc);
         l[r] += f * mlw[r][c][1];
+        const float g = f * mlw[r][c][2];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) o[r][i] += f * ow[r][c][i];
+        for (int i = 0; i < PER; ++i) o[r][i] += g * ow[r][c][i];
       }
       M[r] = Mc;
     }
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
         s_ml[row_slot + wave][1] = l[0];
       }
 #pragma unroll
-      for (int i = 0; i < PER; ++i) s_o[row_slot + wave][lane + 64 * i] = o[0][i];
+      for (int i = 0; i < PER; ++i) s_o[row_slot + wave][lane * PER + i] = o[0][i];
       __syncthreads();
       if (wave != 0) return;
       float Mt = -INFINITY;
@@ -241,7 +257,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
         const float f = m_k == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_k - Mt);
         lt += f * s_ml[row_slot + k][1];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) ot[i] += f * s_o[row_slot + k][lane + 64 * i];
+        for (int i = 0; i < PER; ++i) ot[i] += f * s_o[row_slot + k][lane * PER + i];
       }
       l[0] = lt;
 #pragma unroll
@@ -251,9 +267,11 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
     const float inv = 1.0f / l[r];
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      ((__bf16*)p.out)[(q_row * p.Hq + hq0 + r) * D + lane + 64 * i] = (__bf16)(o[r][i] * inv);
+    __bf16* orow = (__bf16*)p.out + (q_row * p.Hq + hq0 + r) * D;
+    if constexpr (PER == 2)
+      ((uint32_t*)orow)[lane] = pack_bf16x2(o[r][0] * inv, o[r][1] * inv);
+    else
+      orow[lane] = (__bf16)(o[r][0] * inv);
   }
 }
 
@@ -288,8 +306,8 @@ static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // b in part w writes slot b + w < B + parts
 size_t decode_workspace_bytes(int64_t B, int Hq, int D, int parts) {
   const size_t slots = (size_t)(B + parts) * Hq;
-  return align256((size_t)(B + 1) * sizeof(int32_t)) + align256(slots * 2 * sizeof(float)) +
-         align256(slots * D * sizeof(float));
+  return align256((size_t)(B + 1) * sizeof(int32_t)) + align256(slots * 4 * sizeof(float)) +
+         align256(slots * D * sizeof(_Float16));
 }
 
 void decode_workspace_carve(AttnParams& p, void* workspace, int parts) {
@@ -298,8 +316,8 @@ void decode_workspace_carve(AttnParams& p, void* workspace, int parts) {
   p.ws_cum = (int32_t*)w;
   w += align256((size_t)(p.B + 1) * sizeof(int32_t));
   p.ws_ml = (float*)w;
-  w += align256(slots * 2 * sizeof(float));
-  p.ws_o = (float*)w;
+  w += align256(slots * 4 * sizeof(float));
+  p.ws_o = (_Float16*)w;
 }
 
 // Workgroups of the decode grid: one per CU (one 8-wave workgroup fits a CU),

@@ -44,6 +44,15 @@ __host__ __device__ inline int decode_workgroups(const AttnParams& p) {
   return p.grid_parts / (decode_groups(p.Hkv) * (p.decode_rounds > 1 ? p.decode_rounds : 1));
 }
 
+// four accumulator values times inv, as two packed bf16 pairs
+__device__ __forceinline__ u32x2 normalised(const f32x4 a, const float inv) {
+  return u32x2{pack_bf16x2(a[0] * inv, a[1] * inv), pack_bf16x2(a[2] * inv, a[3] * inv)};
+}
+// four accumulator values times s, as two packed fp16 pairs (round to nearest even)
+__device__ __forceinline__ u32x2 scaled_f16(const f32x4 a, const float s) {
+  return u32x2{pack_f16x2(a[0] * s, a[1] * s), pack_f16x2(a[2] * s, a[3] * s)};
+}
+
 // Units of sequence b: its 32-position blocks past the shared prefix (if
 // any), or none when it has no query row.  len_out = seq_lens[b].
 __device__ __forceinline__ int32_t seq_units(const AttnParams& p, int b, int64_t& len_out) {
@@ -313,8 +322,14 @@ struct Partition {
 // (w * R + gi) * rounds on, as one stream; it walks the segments of its range:
 // the pieces of a sequence that lie in one part.  Wave k of a group handles
 // KV heads k, k + (waves per group), ... of every segment.  A segment that
-// covers a whole sequence writes the normalised output; otherwise it writes an
-// unnormalised partial to slot (b + part), which merge_kernel combines.  Slots
+// covers a whole sequence writes the normalised output; otherwise it writes a
+// partial to slot (b + part): its (max, sum) in fp32 and its unnormalised
+// output row in fp16, scaled by a power of two that puts the row's largest
+// magnitude in [2^14, 2^15) (the third fp32 beside max and sum undoes it).
+// fp16 halves the bytes of an fp32 row, which cost the stream about twice
+// as much HBM time, and keeps 11 significant bits (bf16 would keep 8 and
+// double the error of the merged output).  merge_kernel combines the
+// partials.  Slots
 // are unique because the ranges are ordered: a later sequence only meets later
 // parts.  After the scan the groups share no barrier, so a group whose range
 // is empty leaves.
@@ -611,8 +626,8 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
   // on long fp8 sequences split into several parts per group (bf16 has
   // neither the registers nor a measured gain).
   constexpr bool kHold = ESZ == 1;
-  f32x4 hacc[kHold ? NJ : 1];
-  float hm = 0.f, hl = 0.f;
+  u32x2 hacc[kHold ? NJ : 1];
+  float hm = 0.f, hl = 0.f, hu = 0.f;
   int64_t hslot = -1;  // the held partial's slot for the group's first query head, or -1
 
   while (true) {
@@ -647,46 +662,53 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
       const int32_t cb = s_cum[c0.b], ce = s_cum[c0.b + 1];
       const bool whole = c0.j0 == 0 && cb + c0.j1 == ce && p.prefix_len == 0;
       const bool hold = kHold && !whole && hslot < 0 && c1.b >= 0;
+      // a partial's power-of-two scale: the head's largest |value| (its 4
+      // lane groups hold 32 dims each) lands in [2^14, 2^15) in fp16
+      float sc = 1.f, unsc = 1.f;
+      if (!whole) {
+        float mx = 0.f;
+#pragma unroll
+        for (int t = 0; t < NJ; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[t][i]));
+        mx = fmaxf(mx, xor_shuffle(mx, 16));
+        mx = fmaxf(mx, xor_shuffle(mx, 32));
+        const int k = min(max(__builtin_amdgcn_frexp_expf(mx * fabsf(out_scale)), -100), 128);
+        sc = out_scale * __builtin_amdgcn_ldexpf(1.f, 15 - k);
+        unsc = __builtin_amdgcn_ldexpf(1.f, k - 15);
+      }
       if (col < p.G) {
         const int hq = h0 * p.G + col;
         // acc[t][i] = O^T[dim 16t + 4*grp + i][head col]
         if (whole) {
-          const float inv = out_scale / l_run;
           __bf16* orow = (__bf16*)p.out + (q_row0 * p.Hq + hq) * D;
 #pragma unroll
-          for (int t = 0; t < NJ; ++t)
-            *(u32x2*)(orow + 16 * t + 4 * grp) =
-                u32x2{pack_bf16x2(acc[t][0] * inv, acc[t][1] * inv), pack_bf16x2(acc[t][2] * inv, acc[t][3] * inv)};
+          for (int t = 0; t < NJ; ++t) *(u32x2*)(orow + 16 * t + 4 * grp) = normalised(acc[t], out_scale / l_run);
         } else if (!hold) {
           const int64_t slot = ((int64_t)c0.b + c0.w) * p.Hq + hq;
-          float* orow = p.ws_o + slot * D;
+          _Float16* orow = p.ws_o + slot * D;
 #pragma unroll
-          for (int t = 0; t < NJ; ++t) *(f32x4*)(orow + 16 * t + 4 * grp) = acc[t] * out_scale;
-          if (grp == 0) {
-            p.ws_ml[2 * slot] = m_run;
-            p.ws_ml[2 * slot + 1] = l_run;
-          }
+          for (int t = 0; t < NJ; ++t) *(u32x2*)(orow + 16 * t + 4 * grp) = scaled_f16(acc[t], sc);
+          if (grp == 0) *(f32x4*)(p.ws_ml + 4 * slot) = f32x4{m_run, l_run, unsc, 0.f};
         }
       }
       if constexpr (kHold) {
         if (hold) {
           hslot = ((int64_t)c0.b + c0.w) * p.Hq + h0 * p.G;
 #pragma unroll
-          for (int t = 0; t < NJ; ++t) hacc[t] = acc[t] * out_scale;
+          for (int t = 0; t < NJ; ++t) hacc[t] = scaled_f16(acc[t], sc);
           hm = m_run;
           hl = l_run;
+          hu = unsc;
         }
       }
       if (c1.b < 0) {
         if (kHold && hslot >= 0 && col < p.G) {
           const int64_t slot = hslot + col;
-          float* orow = p.ws_o + slot * D;
+          _Float16* orow = p.ws_o + slot * D;
 #pragma unroll
-          for (int t = 0; t < NJ; ++t) *(f32x4*)(orow + 16 * t + 4 * grp) = hacc[t];
-          if (grp == 0) {
-            p.ws_ml[2 * slot] = hm;
-            p.ws_ml[2 * slot + 1] = hl;
-          }
+          for (int t = 0; t < NJ; ++t) *(u32x2*)(orow + 16 * t + 4 * grp) = hacc[t];
+          if (grp == 0) *(f32x4*)(p.ws_ml + 4 * slot) = f32x4{hm, hl, hu, 0.f};
         }
         finish_copy();
         break;

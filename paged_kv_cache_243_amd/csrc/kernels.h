@@ -53,8 +53,8 @@ struct AttnParams {
   int grid_parts;      // partition ranges (parts) of the decode work, a multiple of the parts per workgroup
   int decode_rounds;   // consecutive parts each decode group runs as one stream (>= 1)
   int32_t* ws_cum;     // [B + 1] units before each sequence (written by workgroup 0)
-  float* ws_ml;        // [B + grid_parts, Hq, 2] partial (max in log2 units, sum)
-  float* ws_o;         // [B + grid_parts, Hq, D] unnormalised partial outputs
+  float* ws_ml;        // [B + grid_parts, Hq, 4] partial (max in log2 units, sum, unscale, unused)
+  _Float16* ws_o;      // [B + grid_parts, Hq, D] unnormalised partial outputs times 1 / unscale
   // prefill work list: [0] item count, [1] tile count, then 2 words per item
   // (b << 16 | query tile, tile index * split_max_chunks + chunk), then the
   // (b << 16 | query tile) of every tile

@@ -266,10 +266,10 @@ def test_workspace_size():
     ws = lambda o: lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt),
                                                       ctypes.byref(o))
     # decode: per-sequence unit offsets, then (B + 2048) partial slots of
-    # Hq x (2 + D) floats, whatever the partition size
+    # Hq x (4 floats + D fp16), whatever the partition size
     align = lambda n: (n + 255) // 256 * 256
     slots = (64 + 2048) * 32
-    want = align(65 * 4) + align(slots * 2 * 4) + slots * 128 * 4
+    want = align(65 * 4) + align(slots * 4 * 4) + slots * 128 * 2
     assert ws(opts(max_query_len=1, split_tokens=512)) == want
     assert ws(opts(max_query_len=1, split_tokens=0)) == want
     # prefill: the work list, two counts, two words per item and one per
