@@ -127,9 +127,9 @@ __device__ __forceinline__ void load_f16_elems(const _Float16* row, const int la
 // CHUNK decode partials per load round, and the prefix chunks' partials held
 // for at most PMAX chunks (1 when there is at most one).  Each row's
 // arithmetic is the same whatever RPW and PMAX are.  A lane owns elements
-// lane * PER .. + PER - 1 of each row.  A decode partial is its unnormalised
-// row in fp16 times a power of two, with (max, sum, the power's inverse); a
-// prefix partial is its unnormalised row in fp32 with (max, sum).
+// lane * PER .. + PER - 1 of each row.  A partial (decode or prefix) is its
+// unnormalised row in fp16 times a power of two, with (max, sum, the power's
+// inverse) in fp32.
 template <int D, int CHUNK, int RPW, int PMAX>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
   constexpr int PER = D / 64;
@@ -142,10 +142,10 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
   const int row_slot = threadIdx.y * nw;  // this head's LDS slots: row_slot .. row_slot + nw - 1
   const bool prefix = p.prefix_len > 0;
   // the prefix chunks' partials, loaded first
-  f32x2 mlc[RPW][PMAX];
+  f32x4 mlc[RPW][PMAX];
   float oc[RPW][PMAX][PER];
   if (prefix && wave == 0) {
-    const f32x2* pml = (const f32x2*)p.ws_pre_ml;
+    const f32x4* pml = (const f32x4*)p.ws_pre_ml;
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
@@ -153,8 +153,7 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
         if (c < p.prefix_chunks) {
           const int64_t slot = ((int64_t)c * p.B + b) * p.Hq + hq0 + r;
           mlc[r][c] = pml[slot];
-#pragma unroll
-          for (int i = 0; i < PER; ++i) oc[r][c][i] = p.ws_pre_o[slot * D + lane * PER + i];
+          load_f16_elems<PER>(p.ws_pre_o + slot * D, lane, oc[r][c]);
         }
       }
   }
@@ -190,8 +189,9 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(AttnParams p) {
         if (c < p.prefix_chunks) {
           const float f = __builtin_amdgcn_exp2f(mlc[r][c][0] - M[r]);
           l[r] += f * mlc[r][c][1];
+          const float g = f * mlc[r][c][2];
 #pragma unroll
-          for (int i = 0; i < PER; ++i) o[r][i] += f * oc[r][c][i];
+          for (int i = 0; i < PER; ++i) o[r][i] += g * oc[r][c][i];
         }
       }
     }

@@ -76,8 +76,8 @@ struct AttnParams {
   // the decode grid, workgroup w taking items w / Hkv, w / Hkv + prefix_wgs /
   // Hkv, ... of KV head w % Hkv
   int prefix_wgs;
-  float* ws_pre_ml;    // [prefix_chunks, B, Hq, 2] partial (max in log2 units, sum)
-  float* ws_pre_o;     // [prefix_chunks, B, Hq, D] unnormalised partial outputs
+  float* ws_pre_ml;    // [prefix_chunks, B, Hq, 4] partial (max in log2 units, sum, unscale, unused)
+  _Float16* ws_pre_o;  // [prefix_chunks, B, Hq, D] unnormalised partial outputs times 1 / unscale
   // decode fused with the write (n_new > 0, n_new = T: the new rows are the
   // query rows' own keys): decode_kernel takes the key at the last position
   // of the sequence owning query row t from row t of new_k/new_v [n_new, Hkv,

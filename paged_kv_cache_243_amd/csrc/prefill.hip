@@ -1045,28 +1045,35 @@ __device__ __forceinline__ void prefill_item(const AttnParams& p, PrefillLds<ESZ
   float out_scale = 1.0f;
   if constexpr (ESZ == 1) out_scale = p.v_scale[h];
   if constexpr (PREFIX) {
-    // partial of (chunk, sequence, query head): m_ref in log2 units, the row
-    // sum of the rounded P and the unnormalised O, as the merge expects them
+    // partial of (chunk, sequence, query head) as the merge expects it: m_ref
+    // in log2 units, the row sum of the rounded P, and the unnormalised O in
+    // fp16 times a power of two that puts the row's largest magnitude in
+    // [2^14, 2^15), with that power's inverse
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float l = sum_pair(l_run[nb]);
+      // (every lane takes part: the row's two lane groups exchange their maxima)
+      float mx = 0.f;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(acc[d][nb][i]));
+      mx = fmaxf(mx, xor_shuffle(mx, 32));
+      const int k = min(max(__builtin_amdgcn_frexp_expf(mx * fabsf(out_scale)), -100), 128);
+      const float sc = out_scale * __builtin_amdgcn_ldexpf(1.f, 15 - k);
       if (!row_live[nb]) continue;
       const int r = wave * 32 * NB + nb * 32 + qcol;
       const int64_t slot = ((int64_t)chunk * p.B + b + r / G) * p.Hq + h * G + r % G;
-      float* orow = p.ws_pre_o + slot * D;
+      _Float16* orow = p.ws_pre_o + slot * D;
 #pragma unroll
       for (int d = 0; d < NDB; ++d)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          f32x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = acc[d][nb][4 * i4 + e] * out_scale;
-          *(f32x4*)(orow + d * 32 + 8 * i4 + 4 * qgrp) = o;
+          const f32x16& a = acc[d][nb];
+          *(u32x2*)(orow + d * 32 + 8 * i4 + 4 * qgrp) = u32x2{pack_f16x2(a[4 * i4] * sc, a[4 * i4 + 1] * sc),
+                                                               pack_f16x2(a[4 * i4 + 2] * sc, a[4 * i4 + 3] * sc)};
         }
-      if (qgrp == 0) {
-        p.ws_pre_ml[2 * slot] = m_ref[nb];
-        p.ws_pre_ml[2 * slot + 1] = l;
-      }
+      if (qgrp == 0) *(f32x4*)(p.ws_pre_ml + 4 * slot) = f32x4{m_ref[nb], l, __builtin_amdgcn_ldexpf(1.f, k - 15), 0.f};
     }
     return;
   }
@@ -1303,13 +1310,13 @@ size_t prefix_plan(AttnParams& p, int64_t prefix_len, int n_cu, bool tight) {
   p.prefix_chunks = (int)((prefix_len + len - 1) / len);
   const int64_t max_chunks = std::max<int64_t>(1, std::min<int64_t>(kMaxPrefixChunks, n_tiles));
   const size_t slots = (size_t)(tight ? p.prefix_chunks : max_chunks) * p.B * p.Hq;
-  return (slots * 2 * sizeof(float) + 255) / 256 * 256 + slots * p.D * sizeof(float);
+  return (slots * 4 * sizeof(float) + 255) / 256 * 256 + slots * p.D * sizeof(_Float16);
 }
 
 void prefix_workspace_carve(AttnParams& p, void* region) {
   const size_t slots = (size_t)p.prefix_chunks * p.B * p.Hq;
   p.ws_pre_ml = (float*)region;
-  p.ws_pre_o = (float*)((char*)region + (slots * 2 * sizeof(float) + 255) / 256 * 256);
+  p.ws_pre_o = (_Float16*)((char*)region + (slots * 4 * sizeof(float) + 255) / 256 * 256);
 }
 
 hipError_t launch_shared_prefix_decode(const AttnParams& p, hipStream_t stream) {

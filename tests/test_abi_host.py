@@ -342,7 +342,7 @@ def test_shared_prefix_argument_errors(pages, max_q, status):
 
 def test_shared_prefix_workspace_size():
     """decode workspace plus the prefix partials: chunks x B x Hq slots of
-    (m, l) and D floats, sized (without a device) for the most chunks a plan
+    4 floats (m, l, unscale, unused) and D fp16 values, sized (without a device) for the most chunks a plan
     can choose: at most 8, and at most one per 32 prefix positions, so 2 for
     a 4-page prefix and 8 for a 128-page one."""
     lib = pkv.load()
@@ -354,12 +354,12 @@ def test_shared_prefix_workspace_size():
     o.shared_prefix_pages = 4
     with_prefix = lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt), ctypes.byref(o))
     slots = 2 * 64 * 32
-    assert with_prefix - base == (slots * 8 + 255) // 256 * 256 + slots * 128 * 4
+    assert with_prefix - base == (slots * 16 + 255) // 256 * 256 + slots * 128 * 2
     # a 128-page prefix: min(8 cap, 64 units) = 8 chunks
     o.shared_prefix_pages = 128
     big = lib.paged_attention_workspace_size(ctypes.byref(q), ctypes.byref(kp), ctypes.byref(bt), ctypes.byref(o))
     slots = 8 * 64 * 32
-    assert big - base == (slots * 8 + 255) // 256 * 256 + slots * 128 * 4
+    assert big - base == (slots * 16 + 255) // 256 * 256 + slots * 128 * 2
 
 
 @pytest.mark.parametrize("case,status", [
