@@ -306,3 +306,41 @@ def test_logits_growing_along_the_sequence(gpu, cid):
     out = gpu_attend(gpu, w, kp, vp)
     ref = H.oracle_attend(w, okp, ovp)
     assert_close(out, ref, w.kv_dtype, f"growing logits config {cid}")
+
+
+@pytest.mark.parametrize("k", [-100, 100])
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+@pytest.mark.parametrize("prefix", [False, True])
+def test_partials_keep_extreme_value_magnitudes(gpu, k, kv, prefix):
+    """Value rows scaled by 2^k (bf16 pools: the rows themselves; fp8 pools:
+    v_scale), with many split-K partials per sequence, with and without a
+    shared prefix (whose items write partials of their own).  A partial's row
+    is stored in fp16 after a power-of-two scaling, so magnitudes far outside
+    fp16's range must come back exactly scaled: the output divided by 2^k
+    meets the usual bound against the oracle's, also divided by 2^k (both
+    scalings are exact)."""
+    note(f"values x 2^{k}, {kv}, shared prefix {prefix}")
+    if prefix:
+        cfg = dataclasses.replace(W.SMALL[4], kv_dtype=kv)
+    else:
+        cfg = dataclasses.replace(W.SMALL[2], batch=12, old_min=200, old_max=3000, num_pages=4096, kv_dtype=kv,
+                                  split_tokens=64)
+    w = W.generate(cfg, DEV, seed=37)
+    kp, vp = gpu_write(gpu, w)
+    okp, ovp = H.oracle_write(w)
+    if kv == "bf16":
+        v = torch.from_numpy(ovp.view(np.int16).copy()).view(torch.bfloat16).float() * 2.0 ** k
+        vb = v.to(torch.bfloat16)
+        read = W.valid_rows_mask(w).cpu()  # (the other rows hold poison)
+        assert torch.equal(vb.float().flatten(0, 1)[read], v.flatten(0, 1)[read]), "the scaling must be exact in bf16"
+        ovp = vb.view(torch.int16).numpy().view(ovp.dtype).reshape(ovp.shape).copy()
+        vp = vb.to(DEV)
+    else:
+        w = dataclasses.replace(w, v_scale=w.v_scale * 2.0 ** k)
+    out = torch.empty_like(w.q)
+    gpu.paged_attention(w.q, kp, vp, w.block_table, w.seq_lens, w.query_start_loc, w.scale, out,
+                        k_scale=w.k_scale, v_scale=w.v_scale, max_query_len=w.max_query_len,
+                        split_tokens=w.split_tokens, shared_prefix_pages=w.cfg.shared_prefix_tokens // 16)
+    torch.cuda.synchronize()
+    ref = H.oracle_attend(w, okp, ovp)
+    assert_close(as_f64(out) * 2.0 ** -k, ref * 2.0 ** -k, kv, f"values x 2^{k} {kv} prefix {prefix}")
