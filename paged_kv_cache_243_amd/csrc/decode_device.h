@@ -321,25 +321,25 @@ struct Partition {
 // the `rounds` = grid_parts / (nblocks * R) consecutive parts from
 // (w * R + gi) * rounds on, as one stream; it walks the segments of its range:
 // the pieces of a sequence that lie in one part.  Wave k of a group handles
-// KV heads k, k + (waves per group), ... of every segment.  A segment that
-// covers a whole sequence writes the normalised output; otherwise it writes a
-// partial to slot (b + part): its (max, sum) in fp32 and its unnormalised
-// output row in fp16, scaled by a power of two that puts the row's largest
-// magnitude in [2^14, 2^15) (the third fp32 beside max and sum undoes it).
-// fp16 halves the bytes of an fp32 row, which cost the stream about twice
-// as much HBM time, and keeps 11 significant bits (bf16 would keep 8 and
-// double the error of the merged output).  merge_kernel combines the
-// partials.  Slots
-// are unique because the ranges are ordered: a later sequence only meets later
-// parts.  After the scan the groups share no barrier, so a group whose range
-// is empty leaves.
+// KV heads k, k + (waves per group), ... of every segment.  After the scan the
+// groups share no barrier, so a group whose range is empty leaves.
+//
+// A segment that covers a whole sequence writes the normalised output;
+// otherwise it writes a partial to slot (b + part), which merge_kernel
+// combines.  Slots are unique because the ranges are ordered: a later
+// sequence only meets later parts.  A partial is its (max, sum) in fp32 and
+// its unnormalised output row in fp16, scaled by a power of two that puts
+// the row's largest magnitude in [2^14, 2^15), with the inverse of that power
+// as a third fp32.  Partial rows cost the stream far more HBM time than their
+// bytes; fp16 halves the bytes of fp32 and keeps 11 significant bits (bf16
+// keeps 8, which measurably raises the merged output's error).
 //
 // Each wave processes its work as one stream of units: a run is one KV head of
 // one segment, runs follow segment by segment (heads inside a segment), and
 // the loads of the next unit are issued while the current one is computed
 // even when the next unit opens a new run.  Page ids are fetched two units
-// ahead.  Lengths come from the
-// scan's LDS tables, so opening a run needs no dependent global load.
+// ahead.  Lengths come from the scan's LDS tables, so opening a run needs no
+// dependent global load.
 
 // A position in a wave's stream: unit j of run (sequence b, head slot hk) of
 // the segment of b that lies in part w, units [j0, j1) of b.  b < 0 past the
@@ -621,14 +621,15 @@ __device__ __forceinline__ void decode_body(const AttnParams p, DecodeLds<D>& ld
   float logit_scale, out_scale;
   run_scales(head_of(c0), logit_scale, out_scale);
   // fp8 pools: the first partial that ends before the stream does is held in
-  // registers and stored with the last one.  Partial stores made while the
-  // loads stream slow the stream far more than their bytes would; that shows
-  // on long fp8 sequences split into several parts per group (bf16 has
-  // neither the registers nor a measured gain).
+  // registers (its fp16 row, max, sum and inverse scale) and stored with the
+  // last one.  Partial stores made while the loads stream slow the stream far
+  // more than their bytes would; that shows on long fp8 sequences split into
+  // several parts per group.  The bf16 kernel has little register room, and
+  // holding a partial there measured no gain on the bf16 decode workload.
   constexpr bool kHold = ESZ == 1;
   u32x2 hacc[kHold ? NJ : 1];
   float hm = 0.f, hl = 0.f, hu = 0.f;
-  int64_t hslot = -1;  // the held partial's slot for the group's first query head, or -1
+  int64_t hslot = -1;  // the held partial's slot for the wave's first query head, or -1
 
   while (true) {
     // the unit after c1 (page ids fetched below, loads issued while c1 is computed)
