@@ -31,6 +31,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -58,12 +59,24 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+_TOKEN_RE = re.compile(rb'//[^\n]*|/\*.*?\*/|"(?:\\.|[^"\\\n])*"|\'(?:\\.|[^\'\\\n])*\'', re.S)
+
+
+def _code_only(src: bytes) -> bytes:
+    """C++ source without its comments, whitespace runs collapsed: what the
+    compiler sees (string and character literals are kept as written)."""
+    text = _TOKEN_RE.sub(lambda m: m.group(0) if m.group(0)[:1] in b"\"'" else b" ", src)
+    return re.sub(rb"\s+", b" ", text).strip()
+
+
 def kernel_source_hash() -> str:
+    """Hash of the library's sources as code (comments and layout ignored), so
+    that counters taken on one build stay attached to it through comment edits."""
     h = hashlib.sha256()
     for name in sorted(os.listdir(os.path.join(ROOT, "paged_kv_cache_243_amd", "csrc"))):
         with open(os.path.join(ROOT, "paged_kv_cache_243_amd", "csrc", name), "rb") as f:
             h.update(name.encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()))
     return h.hexdigest()[:16]
 
 
