@@ -264,7 +264,7 @@ int paged_kv_write_attention(const pkv_tensor* k, const pkv_tensor* v, const pkv
  * that needs more than PKV_NOALLOC_SCRATCH_BYTES returns PKV_ERR_SCRATCH
  * before anything is enqueued (128 MiB holds every workload of the design
  * notes, the largest being the key-split prefill of 8 sequences x 512 tokens
- * on 8704-position contexts with 1 or 2 KV heads, about 77 MB).  Nothing in
+ * on 8704-position contexts with 1, 2 or 4 KV heads, about 40 MB).  Nothing in
  * the region needs to start at zero: every kernel writes what a later kernel
  * of the same call reads.  All calls on one GPU share its region, so calls
  * that may overlap on one GPU (different streams without ordering between

@@ -35,6 +35,19 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// elements lane * PER .. + PER - 1 of an fp16 row, widened
+template <int PER>
+__device__ __forceinline__ void load_f16_elems(const _Float16* row, const int lane, float (&o)[PER]) {
+  if constexpr (PER == 2) {
+    const f16x2 v = ((const f16x2*)row)[lane];
+    o[0] = (float)v[0];
+    o[1] = (float)v[1];
+  } else {
+    static_assert(PER == 1, "head_dim 64 or 128");
+    o[0] = (float)row[lane];
+  }
+}
+
 // Four OCP E4M3FN codes in one dword -> two dwords of packed bf16 (exact: every
 // E4M3FN value is representable in bf16).  Uses gfx950's scaled conversion with
 // a unit scale.

@@ -110,19 +110,6 @@ static int merge_rows_per_wave(int64_t B, int Hq, int nw) {
   return nw == 1 && B * Hq > kMergeOneRoundRows && Hq % 2 == 0 ? 2 : 1;
 }
 
-// elements lane * PER .. + PER - 1 of an fp16 row, widened
-template <int PER>
-__device__ __forceinline__ void load_f16_elems(const _Float16* row, const int lane, float (&o)[PER]) {
-  if constexpr (PER == 2) {
-    const f16x2 v = ((const f16x2*)row)[lane];
-    o[0] = (float)v[0];
-    o[1] = (float)v[1];
-  } else {
-    static_assert(PER == 1, "head_dim 64 or 128");
-    o[0] = (float)row[lane];
-  }
-}
-
 // RPW rows per wave (consecutive query heads; only with one wave per head),
 // CHUNK decode partials per load round, and the prefix chunks' partials held
 // for at most PMAX chunks (1 when there is at most one).  Each row's

@@ -65,8 +65,8 @@ struct AttnParams {
   // prefill_split_merge_kernel combines
   int split_keys;
   int split_max_chunks;    // chunks an item may have (1 without the split)
-  float* ws_split_ml;      // [plan_tiles_cap, Hkv, split_max_chunks, 256 rows, 2]
-  float* ws_split_o;       // [plan_tiles_cap, Hkv, split_max_chunks, 256 rows, D]
+  float* ws_split_ml;      // [plan_tiles_cap, Hkv, split_max_chunks, 256 rows, 4] (max, sum, unscale, unused)
+  _Float16* ws_split_o;    // [plan_tiles_cap, Hkv, split_max_chunks, 256 rows, D] unnormalised rows / unscale
   // shared-prefix decode: the first prefix_len positions of every sequence
   // are the same pages; their attention runs as MFMA items of (prefix_tiles
   // groups of sequences) x (prefix_chunks chunks of prefix_chunk_len keys)

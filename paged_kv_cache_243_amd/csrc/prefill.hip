@@ -116,7 +116,7 @@ static size_t split_rows(const AttnParams& p) {
 
 size_t prefill_workspace_bytes(const AttnParams& p) {
   const size_t rows = split_rows(p);
-  return plan_bytes(p) + (rows ? align256(rows * 2 * sizeof(float)) + rows * p.D * sizeof(float) : 0);
+  return plan_bytes(p) + (rows ? align256(rows * 4 * sizeof(float)) + rows * p.D * sizeof(_Float16) : 0);
 }
 
 void prefill_workspace_carve(AttnParams& p, void* workspace) {
@@ -124,7 +124,7 @@ void prefill_workspace_carve(AttnParams& p, void* workspace) {
   p.ws_plan = (int32_t*)w;
   const size_t rows = split_rows(p);
   p.ws_split_ml = rows ? (float*)(w + plan_bytes(p)) : nullptr;
-  p.ws_split_o = rows ? (float*)(w + plan_bytes(p) + align256(rows * 2 * sizeof(float))) : nullptr;
+  p.ws_split_o = rows ? (_Float16*)(w + plan_bytes(p) + align256(rows * 4 * sizeof(float))) : nullptr;
 }
 
 // chunks of an item whose rows see kv keys (1 without the key split); kv <
@@ -1081,26 +1081,33 @@ __device__ __forceinline__ void prefill_item(const AttnParams& p, PrefillLds<ESZ
     // one chunk of a split item: its partial per row, combined by
     // prefill_split_merge_kernel (plans past the bound write nothing)
     if (gtile >= p.plan_tiles_cap) return;
+    // (m_ref, l, inverse scale) and the unnormalised row in fp16 times a power
+    // of two that puts its largest magnitude in [2^14, 2^15), as for the
+    // shared prefix's partials
     const int64_t item_slot = ((int64_t)gtile * p.Hkv + h) * p.split_max_chunks + chunk;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const float l = sum_pair(l_run[nb]);
+      float mx = 0.f;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(acc[d][nb][i]));
+      mx = fmaxf(mx, xor_shuffle(mx, 32));
+      const int k = min(max(__builtin_amdgcn_frexp_expf(mx * fabsf(out_scale)), -100), 128);
+      const float sc = out_scale * __builtin_amdgcn_ldexpf(1.f, 15 - k);
       const int r = wave * 32 * NB + nb * 32 + qcol;
       const int64_t slot = item_slot * kPrefillRows + r;
-      float* orow = p.ws_split_o + slot * D;
+      _Float16* orow = p.ws_split_o + slot * D;
 #pragma unroll
       for (int d = 0; d < NDB; ++d)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
-          f32x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = acc[d][nb][4 * i4 + e] * out_scale;
-          *(f32x4*)(orow + d * 32 + 8 * i4 + 4 * qgrp) = o;
+          const f32x16& a = acc[d][nb];
+          *(u32x2*)(orow + d * 32 + 8 * i4 + 4 * qgrp) = u32x2{pack_f16x2(a[4 * i4] * sc, a[4 * i4 + 1] * sc),
+                                                               pack_f16x2(a[4 * i4 + 2] * sc, a[4 * i4 + 3] * sc)};
         }
-      if (qgrp == 0) {
-        p.ws_split_ml[2 * slot] = m_ref[nb];
-        p.ws_split_ml[2 * slot + 1] = l;
-      }
+      if (qgrp == 0) *(f32x4*)(p.ws_split_ml + 4 * slot) = f32x4{m_ref[nb], l, __builtin_amdgcn_ldexpf(1.f, k - 15), 0.f};
     }
     return;
   }
@@ -1170,7 +1177,9 @@ void shared_prefix_decode_kernel(AttnParams p) {
 // Key-split prefill: combine the chunks' partials of every row of a split
 // (sequence, query tile, KV head) with a log-sum-exp merge,
 //   M = max_c m_c,  out = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c,
-// one wave per row (4 per workgroup), the lanes over the head dimension.
+// one wave per row (4 per workgroup), lane i over elements i * PER .. + PER - 1
+// of the head dimension.  O_c is stored in fp16 divided by a power of two, u_c
+// (its partial's third value), and enters as u_c times the stored row.
 // Chunk 0 starts at key 0, which every row sees, so M is finite; a chunk that
 // lies wholly past a row's position left m = -1e30 and l = 0 there (weight 0).
 template <int D>
@@ -1191,21 +1200,20 @@ __global__ __launch_bounds__(256) void prefill_split_merge_kernel(AttnParams p) 
   const int64_t tok = tok0 + r / G;
   if (r >= tpt * G || tok >= tok_end) return;
   const int64_t base = ((int64_t)g * p.Hkv + h) * p.split_max_chunks;
-  const f32x2* ml = (const f32x2*)p.ws_split_ml;
+  const f32x4* ml = (const f32x4*)p.ws_split_ml;
   // chunks in groups of 8, every load of a group issued before any is used
   constexpr int CH = 8;
   float M = -INFINITY, l = 0.f, o[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) o[i] = 0.f;
   for (int c0 = 0; c0 < nch; c0 += CH) {
-    f32x2 x[CH];
+    f32x4 x[CH];
     float oc[CH][PER];
 #pragma unroll
     for (int k = 0; k < CH; ++k) {
       const int64_t slot = (base + min(c0 + k, nch - 1)) * kPrefillRows + r;
       x[k] = ml[slot];
-#pragma unroll
-      for (int i = 0; i < PER; ++i) oc[k][i] = p.ws_split_o[slot * D + lane + 64 * i];
+      load_f16_elems<PER>(p.ws_split_o + slot * D, lane, oc[k]);
     }
     float Mc = M;
 #pragma unroll
@@ -1221,15 +1229,18 @@ __global__ __launch_bounds__(256) void prefill_split_merge_kernel(AttnParams p) 
     for (int k = 0; k < CH; ++k) {
       const float f = __builtin_amdgcn_exp2f(x[k][0] - Mc);
       l += f * x[k][1];
+      const float g = f * x[k][2];
 #pragma unroll
-      for (int i = 0; i < PER; ++i) o[i] += f * oc[k][i];
+      for (int i = 0; i < PER; ++i) o[i] += g * oc[k][i];
     }
     M = Mc;
   }
   const float inv = 1.0f / l;
   __bf16* orow = (__bf16*)p.out + ((q0 + tok) * p.Hq + h * G + r % G) * D;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) orow[lane + 64 * i] = (__bf16)(o[i] * inv);
+  if constexpr (PER == 2)
+    ((uint32_t*)orow)[lane] = pack_bf16x2(o[0] * inv, o[1] * inv);
+  else
+    orow[lane] = (__bf16)(o[0] * inv);
 }
 
 // Shared-prefix decode, prefix part: one item per (group of prefill_tokens_per_tile

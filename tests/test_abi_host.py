@@ -285,8 +285,8 @@ def test_prefill_key_split_workspace():
     """One 512-token chunk of one sequence on one KV head (G = 4), 8704-key
     rows: 9 tiles at most, far fewer workgroups than the 256 CUs, so the keys
     are cut into chunks of max(ceil(8704 / ceil(512 / 9)), 512) = 512 keys, 17
-    per item; the workspace adds (m, l) and D floats per row for every (tile,
-    head, chunk) beside the work list."""
+    per item; the workspace adds 4 floats (m, l, unscale, unused) and D fp16
+    values per row for every (tile, head, chunk) beside the work list."""
     lib = pkv.load()
     q, kp = T([512, 4, 128], B.PKV_BF16), T([65536, 16, 1, 128], B.PKV_BF16)
     bt = T([1, 544], B.PKV_I64)
@@ -295,13 +295,13 @@ def test_prefill_key_split_workspace():
     align = lambda v: (v + 255) // 256 * 256
     tiles, chunks = 512 // 64 + 1, 17
     rows = tiles * 1 * chunks * 256
-    assert n == align((2 + 2 * tiles * chunks + tiles) * 4) + align(rows * 2 * 4) + rows * 128 * 4
+    assert n == align((2 + 2 * tiles * chunks + tiles) * 4) + align(rows * 4 * 4) + rows * 128 * 2
     # 8 KV heads: 72 workgroups, still short of the CUs -> chunks of
     # max(ceil(8704 / ceil(512 / 72)), 512) = 1088 keys, 8 per item
     kp8, q8 = T([65536, 16, 8, 128], B.PKV_BF16), T([512, 32, 128], B.PKV_BF16)
     n8 = lib.paged_attention_workspace_size(ctypes.byref(q8), ctypes.byref(kp8), ctypes.byref(bt), ctypes.byref(o))
     rows8 = tiles * 8 * 8 * 256
-    assert n8 == align((2 + 2 * tiles * 8 + tiles) * 4) + align(rows8 * 2 * 4) + rows8 * 128 * 4
+    assert n8 == align((2 + 2 * tiles * 8 + tiles) * 4) + align(rows8 * 4 * 4) + rows8 * 128 * 2
 
 
 def test_prefill_grid_limit():
