@@ -344,3 +344,24 @@ def test_partials_keep_extreme_value_magnitudes(gpu, k, kv, prefix):
     torch.cuda.synchronize()
     ref = H.oracle_attend(w, okp, ovp)
     assert_close(as_f64(out) * 2.0 ** -k, ref * 2.0 ** -k, kv, f"values x 2^{k} {kv} prefix {prefix}")
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8_e4m3fn"])
+def test_decode_groups_running_several_parts(gpu, kv):
+    """64 sequences of 16 to 6,000 positions with 256-position partitions:
+    768 parts, so each of the 256 workgroups runs 3 consecutive parts as one
+    stream (about 8 units each).  Its stream then holds pieces of sequences in
+    several parts, parts that end inside a sequence and, for two of the
+    sequences, a whole sequence inside one part.  With fp8 pools
+    the first partial that ends before the stream does is kept in registers
+    and stored with the last one.  Every output row against the oracle.  (Its
+    largest error, about 3.9e-3 and 0.07 of the output rms, is the bf16
+    rounding of a short sequence's output, the same with fp32 partials and
+    without the split; the long sequences' outputs keep the rms small.)"""
+    note(f"several parts per group, {kv}")
+    cfg = dataclasses.replace(W.SMALL[5], batch=64, hq=64, hkv=8, kv_dtype=kv, old_min=15, old_max=6000,
+                              num_pages=32768, split_tokens=256)
+    w = W.generate(cfg, DEV, seed=43)
+    kp, vp, out = gpu_step(gpu, w)
+    _, _, ref = H.oracle_step(w)
+    assert_close(out, ref, kv, f"several parts per group {kv}")
