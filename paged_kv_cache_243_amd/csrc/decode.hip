@@ -67,7 +67,8 @@ __global__ __launch_bounds__(512) void decode_kernel(AttnParams p) {
 
 // Log-sum-exp merge of the partials of a sequence whose units span several
 // parts (and, with a shared prefix, of the prefix chunks' partials):
-//   M = max_w m_w,  out = sum_w 2^(m_w - M) O_w / sum_w 2^(m_w - M) l_w.
+//   M = max_w m_w,  out = sum_w 2^(m_w - M) u_w R_w / sum_w 2^(m_w - M) l_w,
+// where partial w's unnormalised row O_w is stored as R_w = O_w / u_w in fp16.
 // A workgroup serves nh query heads of one sequence (threadIdx.y), with nw
 // waves per head (1 .. kMergeWaves, by the partials a sequence has; nw * nh
 // <= kMergeWaves).  Wave k of a head takes the chunks k, k + nw, ... of
