@@ -84,12 +84,14 @@ constexpr int kMergeWaves = 16;
 constexpr int kMergeGroupWaves = 4;
 
 // merge waves per head for a grid of `parts` parts over B sequences: one per
-// 8 partials a sequence holds on average, at most kMergeWaves (the 8-way head
-// shard of the long fp8 decode, 129 partials per row: 16 waves took its step
-// from 81 to 78 us against 4)
+// 8 partials a sequence holds on average, at most 4 up to 8 such chunks and at
+// most kMergeWaves beyond (the 8-way head shard of the long fp8 decode, 129
+// partials per row: 16 waves took its step from 81 to 78 us against 4; the
+// long fp8 decode itself, 33 per row, measured no better with 5 than with 4)
 static int merge_waves(int parts, int64_t B) {
   const int64_t per_seq = parts / std::max<int64_t>(B, 1) + 1;
-  return (int)std::min<int64_t>(kMergeWaves, (per_seq + 7) / 8);
+  const int64_t chunks = (per_seq + 7) / 8;
+  return (int)std::min<int64_t>(chunks > 8 ? kMergeWaves : kMergeGroupWaves, chunks);
 }
 
 // partials a merge wave loads together: as many as a sequence holds on
