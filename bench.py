@@ -311,14 +311,14 @@ def traffic_from_profile(kernel: str):
 
 
 def fp8_prefill_config(W):
-    """The chunked-prefill workload (config 3) with fp8 E4M3FN pools."""
+    """The chunked-prefill workload (8 x 512 new tokens on up to 8192 old) with fp8 E4M3FN pools."""
     import dataclasses
     c = W.CONFIGS[3]
     return dataclasses.replace(c, name=c.name + "-fp8", kv_dtype="fp8_e4m3fn")
 
 
 def tp_shard(W, cid: int, tp: int):
-    """Config `cid` with the heads one GPU holds under a `tp`-way head split."""
+    """Workload `cid` of the workloads module with the heads one GPU holds under a `tp`-way head split."""
     return W.head_shard(W.CONFIGS[cid], tp)
 
 
@@ -658,7 +658,7 @@ def main(argv=None) -> int:
     # ---- headline: decode workload, write + attention per step, as the one
     # call paged_kv_write_attention (one kernel pass writes and attends, then
     # the merge); the two separate calls are timed beside it
-    log("generating decode workload (config 2)")
+    log("generating the bf16 decode workload (64 sequences of 512-4096 positions)")
     w2 = W.generate(2, dev)
     r2 = Runner(pkv, w2, torch, fused=True)
     r2s = Runner(pkv, w2, torch)
@@ -744,7 +744,7 @@ def main(argv=None) -> int:
     if not args.no_extra:
         extra = {}
         # chunked prefill
-        log("generating prefill workload (config 3)")
+        log("generating the chunked-prefill workload (8 x 512 new tokens)")
         w3 = W.generate(3, dev)
         r3 = Runner(pkv, w3, torch)
         t3, c3, kt3 = time_workload(r3, torch, max(5, args.steps // 2), args.warmup, flush, "prefill bf16")
@@ -816,7 +816,7 @@ def main(argv=None) -> int:
         del r3f, w3f
         torch.cuda.empty_cache()
         # shared-prefix decode
-        log("generating shared-prefix decode workload (config 4)")
+        log("generating the shared-prefix decode workload (256 sequences on a 2048-position prefix)")
         w4 = W.generate(4, dev)
         pages4 = w4.cfg.shared_prefix_tokens // w4.cfg.page_size
         r4 = Runner(pkv, w4, torch, shared_prefix_pages=pages4)
@@ -843,7 +843,7 @@ def main(argv=None) -> int:
         del r4, w4
         torch.cuda.empty_cache()
         # long-context fp8 decode
-        log("generating long-context fp8 decode workload (config 5)")
+        log("generating the long-context fp8 decode workload (16 sequences of 32k-128k positions)")
         w5 = W.generate(5, dev)
         r5 = Runner(pkv, w5, torch, fused=True)
         t5, _, kt5 = time_workload(r5, torch, args.steps, args.warmup, flush, "fp8 long decode")
@@ -880,14 +880,14 @@ def main(argv=None) -> int:
         # the two decode workloads at their 8-way tensor-parallel shard: one KV
         # head (and its query heads) per GPU, all sequences and positions
         shards = {}
-        for cid in (2, 5):
-            log(f"generating the 8-way shard of config {cid}")
+        for cid, key in ((2, "decode_bf16"), (5, "long_decode_fp8")):
+            log(f"generating the 8-way head shard of the {key} workload")
             ws = W.generate(tp_shard(W, cid, 8), dev)
             rs = Runner(pkv, ws, torch)
-            ts, cs, kts = time_workload(rs, torch, args.steps, args.warmup, flush, f"config {cid}, 8-way shard")
+            ts, cs, kts = time_workload(rs, torch, args.steps, args.warmup, flush, f"{key}, 8-way head shard")
             ks = statistics.fmean(kts.kernel)
             kbs = decode_kernel_bytes(ws)
-            shards[f"config{cid}"] = {
+            shards[key] = {
                 "q_heads": ws.cfg.hq, "kv_heads": ws.cfg.hkv, "kv_dtype": ws.cfg.kv_dtype,
                 "algorithmic_bytes_per_launch": kbs,
                 "launch_ms_mean": round(ks, 5),
@@ -898,8 +898,8 @@ def main(argv=None) -> int:
             del rs, ws
             torch.cuda.empty_cache()
         extra["tp8_shard_decode"] = {
-            "workload": "the decode workload (config 2) and the long-context fp8 decode (config 5) with the "
-                        "query and KV heads of one GPU of an 8-way head split (1 KV head); not the headline",
+            "workload": "the bf16 decode workload and the long-context fp8 decode with the query and KV "
+                        "heads of one GPU of an 8-way head split (1 KV head); not the headline",
             "kernel": "decode_kernel (one-wave parts, 8 per workgroup)",
             **shards,
         }
